@@ -1,0 +1,228 @@
+"""Integer model of the paged block manager.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+What the pages fix:
+
+* Taming the Tail, "How the Architecture Works": each sequence has a block
+  table mapping its logical blocks (contiguous from the model's point of view)
+  to physical blocks anywhere in the pool; when the current block is full a
+  new one is taken from the free block pool.
+* vLLM PagedAttention (tinycto), "1. Underlying Mechanism": blocks of B=16
+  tokens; the token that no longer fits (token 17) takes a new block on the
+  fly; a forked child shares the parent's blocks (zero copy) and copy-on-write
+  gives it private copies only where it writes.
+* KV-cache chapter, "PagedAttention: borrowing virtual memory": a reference
+  count per physical block; a block goes back to the free pool only when its
+  count reaches zero; a sequence about to write into a shared block first gets
+  a private copy of it (copy-on-write).  Answer A6: tearing down one of two
+  tables that share a block leaves the block live with count 1.
+* Taming the Tail, "The Kernel Engineering" snippet: a token's physical address
+  is the physical block times the block size plus its offset in the block.
+
+Where the pages leave the policy open, this model fixes it (the same policy is
+the specification of the C++ block manager, which must match it bit for bit):
+
+* the free pool is a FIFO queue: blocks are taken from the front and freed
+  blocks are appended at the back, a freed sequence's blocks in logical order;
+* in a batched append the sequences are served in batch order; a sequence
+  copies its last block iff that block's count is above one at its turn (so
+  of k sharers writing in one step, the first k-1 copy and the last writes in
+  place); a copy duplicates the whole block;
+* a batch may name a sequence only once;
+* every call is all-or-nothing: on any error nothing changes.
+"""
+
+from __future__ import annotations
+
+import copy
+from collections import deque
+
+
+class BlockManagerError(Exception):
+    status = -1
+
+
+class InvalidArg(BlockManagerError):
+    status = -1
+
+
+class OutOfBlocks(BlockManagerError):
+    status = -2
+
+
+class UnknownSeq(BlockManagerError):
+    status = -3
+
+
+class SeqExists(BlockManagerError):
+    status = -4
+
+
+class _Seq:
+    __slots__ = ("blocks", "n")
+
+    def __init__(self):
+        self.blocks: list[int] = []
+        self.n = 0
+
+
+class BlockManagerModel:
+    """Free pool + per-block reference counts + per-sequence block tables."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise InvalidArg("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise InvalidArg("free_order must be a permutation of the block ids")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+        self.seqs: dict[int, _Seq] = {}
+        self.forks = 0
+        self.cow_copies = 0
+
+    # -- internal helpers -------------------------------------------------
+    def _take(self) -> int:
+        if not self.free:
+            raise OutOfBlocks("free pool is empty")
+        b = self.free.popleft()
+        assert self.ref[b] == 0
+        self.ref[b] = 1
+        return b
+
+    def _release(self, b: int) -> None:
+        self.ref[b] -= 1
+        assert self.ref[b] >= 0
+        if self.ref[b] == 0:
+            self.free.append(b)
+
+    def _write_one(self, seq: _Seq, pairs: list) -> int:
+        """Give the next position of ``seq`` a slot; returns the slot."""
+        B = self.block_size
+        pos = seq.n
+        if pos % B == 0:
+            seq.blocks.append(self._take())
+        else:
+            last = seq.blocks[-1]
+            if self.ref[last] > 1:
+                fresh = self._take()
+                pairs.append((last, fresh))
+                self.ref[last] -= 1
+                seq.blocks[-1] = fresh
+                self.cow_copies += 1
+        seq.n = pos + 1
+        return seq.blocks[pos // B] * B + pos % B
+
+    def _transaction(self, fn):
+        """Run ``fn`` on the live state; restore everything if it raises."""
+        saved = (copy.deepcopy(self.seqs), list(self.ref), deque(self.free),
+                 self.forks, self.cow_copies)
+        try:
+            return fn()
+        except BlockManagerError:
+            self.seqs, self.ref, self.free, self.forks, self.cow_copies = saved
+            raise
+
+    # -- API ----------------------------------------------------------------
+    def add_seq(self, seq_id: int, n_tokens: int) -> list[int]:
+        """New sequence holding ``n_tokens`` tokens (a prefill); returns their slots."""
+        if seq_id in self.seqs:
+            raise SeqExists(seq_id)
+        if n_tokens < 0:
+            raise InvalidArg("n_tokens < 0")
+
+        def run():
+            seq = _Seq()
+            self.seqs[seq_id] = seq
+            pairs: list = []
+            return [self._write_one(seq, pairs) for _ in range(n_tokens)]
+
+        return self._transaction(run)
+
+    def append_slots(self, seq_ids, tokens_each: int):
+        """Append ``tokens_each`` tokens to every listed sequence, in batch order.
+
+        Returns (slots, copy_pairs): slots in batch order (sequence-major) and
+        the (src, dst) block copies copy-on-write requires, in the order made.
+        """
+        ids = [int(s) for s in seq_ids]
+        if tokens_each < 0:
+            raise InvalidArg("tokens_each < 0")
+        if len(set(ids)) != len(ids):
+            raise InvalidArg("a batch may name a sequence only once")
+        for s in ids:
+            if s not in self.seqs:
+                raise UnknownSeq(s)
+
+        def run():
+            slots: list[int] = []
+            pairs: list = []
+            for s in ids:
+                seq = self.seqs[s]
+                for _ in range(tokens_each):
+                    slots.append(self._write_one(seq, pairs))
+            return slots, pairs
+
+        return self._transaction(run)
+
+    def fork(self, parent: int, child: int) -> None:
+        """Child shares every block of the parent (no copy); counts go up by one."""
+        if parent not in self.seqs:
+            raise UnknownSeq(parent)
+        if child in self.seqs:
+            raise SeqExists(child)
+        src = self.seqs[parent]
+        seq = _Seq()
+        seq.blocks = list(src.blocks)
+        seq.n = src.n
+        for b in seq.blocks:
+            self.ref[b] += 1
+        self.seqs[child] = seq
+        self.forks += 1
+
+    def free_seq(self, seq_id: int) -> None:
+        """Drop a sequence; blocks whose count reaches zero rejoin the pool."""
+        if seq_id not in self.seqs:
+            raise UnknownSeq(seq_id)
+        seq = self.seqs.pop(seq_id)
+        for b in seq.blocks:
+            self._release(b)
+
+    def block_tables(self, seq_ids, max_blocks: int):
+        """Per-sequence rows of physical block ids, padded with -1, and lengths."""
+        rows, lens = [], []
+        for s in seq_ids:
+            if s not in self.seqs:
+                raise UnknownSeq(s)
+            seq = self.seqs[s]
+            if len(seq.blocks) > max_blocks:
+                raise InvalidArg("sequence needs more than max_blocks blocks")
+            rows.append(seq.blocks + [-1] * (max_blocks - len(seq.blocks)))
+            lens.append(seq.n)
+        return rows, lens
+
+    def refcount(self, block: int) -> int:
+        if not 0 <= block < self.num_blocks:
+            raise InvalidArg("block id out of range")
+        return self.ref[block]
+
+    def stats(self) -> dict:
+        B = self.block_size
+        used = sum(1 for r in self.ref if r > 0)
+        logical_blocks = sum(len(s.blocks) for s in self.seqs.values())
+        tokens = sum(s.n for s in self.seqs.values())
+        return {
+            "num_blocks": self.num_blocks,
+            "free_blocks": len(self.free),
+            "used_blocks": used,
+            "shared_blocks": sum(1 for r in self.ref if r > 1),
+            "num_seqs": len(self.seqs),
+            "logical_blocks": logical_blocks,
+            "live_tokens": tokens,
+            "tail_waste_slots": logical_blocks * B - tokens,
+            "forks": self.forks,
+            "cow_copies": self.cow_copies,
+        }

@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV-cache hot path on one MI355X.
+
+Workload: the Llama-3-70B-shaped decode layer -- batch 256, 64 query / 8 kv heads,
+head_dim 128, bf16, block size 16, log-normal context lengths (median 1,024, clipped to
+[16, 8,192]) in a pool fragmented by 10,000 steps of alloc/free churn.  Synthetic, seeded
+values (N(0,1) rounded to bf16).
+
+One step = the whole hot path for one batch:
+  host  : pa_bm_append_slots (one token per sequence, copy-on-write decisions) and
+          pa_bm_block_tables into pinned staging buffers;
+  copy  : async host->device upload of slots, tables and lengths;
+  device: pa_copy_blocks (if any pairs) -> pa_cache_write -> pa_decode (split-K + merge).
+
+Prints one JSON line.  ``value`` is the step's algorithmic HBM traffic divided by the step
+time (GB/s); tokens/s is the batch size over the step time.  ``roofline`` reports the decode
+call alone (split-K kernel + merge), timed with HIP events on the stream it runs on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(lens, w, T, with_write=True):
+    """Bytes the decode step must move (SURVEY-style accounting, exact token counts):
+    K and V of every context token, q and out, table entries in use and lengths, and the
+    cache write of the T new tokens (read + write)."""
+    elt = 2 if w.dtype == "bf16" else 4
+    B = w.block_size
+    lens = np.asarray(lens, np.int64)
+    S = len(lens)
+    kv = int(lens.sum()) * w.hkv * w.head_dim * 2 * elt
+    qo = 2 * S * w.hq * w.head_dim * elt
+    meta = 4 * int(((lens + B - 1) // B).sum()) + 4 * S
+    write = T * w.hkv * w.head_dim * 2 * elt * 2 if with_write else 0
+    return kv + qo + meta, write
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = auto)")
+    ap.add_argument("--cpu-seqs", type=int, default=256,
+                    help="sequences of the batch the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--seed", type=int, default=3)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the decode path needs no "
+                          "collective; run with --gpus 1"}), flush=True)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_378_amd import _lib
+    from paged_kv_cache_378_amd import workloads as wl
+    from paged_kv_cache_378_amd.runner import PagedState
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w = wl.llama70b(seed=args.seed)
+    t_setup = time.perf_counter()
+    st = PagedState(w, dev, poison=True)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    S, B = w.num_seqs, w.block_size
+    total = args.warmup + args.steps
+    max_ctx = st.max_ctx + total
+    max_blocks = (max_ctx + B - 1) // B
+    ws = st.workspace_for(max_ctx, args.partition) if hasattr(st, "workspace_for") else None
+    if ws is None:
+        nbytes = _lib.pa_decode_workspace_size(S, w.hq, w.head_dim, max_ctx, args.partition)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    out = st.new_out()
+    ids = np.asarray(w.step_ids, np.int64)
+
+    # double-buffered pinned staging: the host prepares step i+1 while step i's upload runs
+    pin = [dict(tables=torch.empty((S, max_blocks), dtype=torch.int32).pin_memory(),
+                lens=torch.empty(S, dtype=torch.int32).pin_memory(),
+                slots=torch.empty(S, dtype=torch.int32).pin_memory()) for _ in range(2)]
+    done = [None, None]
+    tables_d = torch.empty((S, max_blocks), dtype=torch.int32, device=dev)
+    lens_d = torch.empty(S, dtype=torch.int32, device=dev)
+    slots_d = torch.empty(S, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    host_s = []
+    dec_events = []
+    step_lens = []
+
+    def step(i, timed):
+        buf = pin[i % 2]
+        if done[i % 2] is not None:
+            done[i % 2].synchronize()
+        h0 = time.perf_counter()
+        slots, pairs = st.bm.append_slots(ids, 1)
+        st.bm.block_tables(ids, max_blocks, buf["tables"].numpy(), buf["lens"].numpy())
+        buf["slots"].numpy()[:] = slots
+        host_s.append(time.perf_counter() - h0)
+        tables_d.copy_(buf["tables"], non_blocking=True)
+        lens_d.copy_(buf["lens"], non_blocking=True)
+        slots_d.copy_(buf["slots"], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        done[i % 2] = ev
+        if len(pairs):
+            _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).to(dev, non_blocking=False))
+        _lib.pa_cache_write(st.vals["k_step"], st.vals["v_step"], st.k_cache, st.v_cache, slots_d)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        _lib.pa_decode(out, st.vals["q"], st.k_cache, st.v_cache, tables_d, lens_d, max_ctx,
+                       w.scale, args.partition, ws)
+        if timed:
+            e1.record(stream)
+            dec_events.append((e0, e1))
+            step_lens.append(buf["lens"].numpy().copy())
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    host_s.clear()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if not torch.isfinite(out.float()).all():
+        print(json.dumps({"error": "non-finite decode output"}), flush=True)
+        return 1
+
+    ms_step = 1e3 * elapsed / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in dec_events]
+    dec_avg_ms = float(np.mean(dec_ms))
+    dec_bytes, write_bytes = zip(*[algorithmic_bytes(l, w, S) for l in step_lens])
+    dec_bytes_avg = float(np.mean(dec_bytes))
+    step_bytes_avg = dec_bytes_avg + float(np.mean(write_bytes))
+    achieved = dec_bytes_avg / (dec_avg_ms * 1e-3) / 1e9
+    value = step_bytes_avg / (ms_step * 1e-3) / 1e9
+    tokens = int(np.mean([l.sum() for l in step_lens]))
+
+    cpu = None
+    if args.cpu_seqs > 0:
+        cpu = cpu_baseline(w, st, args.cpu_seqs)
+
+    line = {
+        "metric": "paged decode attention: HBM GB/s (% of peak) + decode tokens/s at batch 256",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-70b-shaped decode layer, batch 256, 64/8 heads, D=128, "
+                               "B=16, log-normal ctx (median 1024, [16, 8192]), churned pool",
+                   "global_batch": S, "seq_len": "log-normal, mean %d" % (tokens // S),
+                   "context_tokens": tokens, "partition_tokens": args.partition or "auto",
+                   "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "host_block_manager_us": round(1e6 * float(np.median(host_s)), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_decode (split-K decode + partition merge)",
+                     "avg_ms": round(dec_avg_ms, 4), "algorithmic_bytes": int(dec_bytes_avg)},
+        "cpu_baseline": cpu,
+        "setup_s": round(t_setup, 1),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(w, st, n_seqs):
+    """The fp64 oracle on the first n_seqs sequences of the same step, one thread."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as att
+    from paged_kv_cache_378_amd import workloads as wl
+
+    n_seqs = min(n_seqs, w.num_seqs)
+    q = st.vals["q"]
+    busy = 0.0
+    tokens = 0
+    with threadpool_limits(limits=1):
+        torch_threads = torch.get_num_threads()
+        torch.set_num_threads(1)
+        try:
+            for i in range(n_seqs):
+                sid = w.step_ids[i]
+                ks, vs = wl.logical_kv(w, sid, st.vals)
+                K = torch.cat(ks).to("cpu", torch.float64).numpy()
+                V = torch.cat(vs).to("cpu", torch.float64).numpy()
+                qi = q[i].to("cpu", torch.float64).numpy()
+                t0 = time.perf_counter()
+                att.dense_decode(qi, K, V, w.scale)
+                busy += time.perf_counter() - t0
+                tokens += K.shape[0]
+        finally:
+            torch.set_num_threads(torch_threads)
+    return {"value": round(n_seqs / busy, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_seqs} of {w.num_seqs} sequences of one decode step "
+                      f"({tokens} context tokens, all 64 heads), numpy fp64, 1 thread; "
+                      f"{busy:.2f} s of oracle time (data movement excluded)",
+            "oracle_s": round(busy, 2)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

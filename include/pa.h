@@ -1,0 +1,256 @@
+/*
+ * pa.h -- C ABI of the paged KV-cache library (libpa.so) for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the hot path of PagedAttention as described on three pages:
+ *   [TT]  "Taming the Tail: How PagedAttention Solves the KV-Cache Fragmentation Crisis in
+ *         Multi-Tenant LLM Serving" (architects-blueprint blog);
+ *   [VP]  "vLLM PagedAttention: Eliminating KV Cache Memory Fragmentation & 4x Throughput"
+ *         (tinycto.tv);
+ *   [KC]  the grade-12 KV-cache chapter of aicomputerinstitute.com.
+ *
+ * Two halves sit behind this header:
+ *   - a host block manager (free pool, per-block reference counts, fork with copy-on-write,
+ *     block tables and slot mappings), pure C++, no GPU needed;
+ *   - HIP kernels for gfx950 that operate on a physical pool of fixed-size blocks.
+ *
+ * Conventions for every function:
+ *   - The return value is a pa_status; PA_OK is 0, errors are negative.  After an error,
+ *     pa_last_error() returns a message (thread-local, valid until the next call on that
+ *     thread).  No C++ exception crosses this boundary.
+ *   - Block-manager calls are all-or-nothing: when they return an error nothing changed.
+ *   - Device calls take device pointers the CALLER owns and a hipStream_t passed as void*
+ *     (NULL = the null stream).  They only enqueue work: no allocation, no synchronisation.
+ *     Every argument visible on the host (sizes, dtype, alignment) is checked before any
+ *     launch; contents of device memory cannot be checked there (use pa_validate_tables on a
+ *     host copy).  Kernels never read or write outside the buffers described by the sizes
+ *     passed in: a slot, block id or context length out of range is skipped or clamped and the
+ *     affected outputs are set to NaN, never dereferenced.
+ *   - A handle (pa_bm) is not thread-safe: one scheduler thread per handle.
+ *
+ * Pool layout (the pages fix only the address rule "physical block * block size + offset",
+ * [TT] "Under the Hood: The CUDA Kernel Engineering"; the rest is this library's choice):
+ *   k_cache: [num_blocks, Hkv, B, D]  -- key of token at offset o of block p, kv-head h is
+ *                                        the contiguous row k_cache[p][h][o][0..D)
+ *   v_cache: [num_blocks, Hkv, D, B]  -- its value is the column v_cache[p][h][0..D)[o]
+ *                                        (values are stored transposed inside each block)
+ *   slot = p * B + o.   Block tables: int32 [S, max_blocks], row s lists the physical blocks of
+ *   sequence s in logical order, padded with -1.  All arrays are C-contiguous.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,   /* bad size, pointer, id or precondition                     */
+  PA_ERR_OUT_OF_BLOCKS = -2, /* the free pool cannot satisfy the request (state unchanged) */
+  PA_ERR_UNKNOWN_SEQ = -3,   /* a sequence id that the manager does not hold               */
+  PA_ERR_SEQ_EXISTS = -4,    /* a sequence id that is already in use                       */
+  PA_ERR_UNSUPPORTED = -5,   /* dtype / head_dim / block size / group combination not built */
+  PA_ERR_WORKSPACE = -6,     /* workspace missing or smaller than the size query returned  */
+  PA_ERR_HIP = -7            /* the HIP runtime reported an error at launch                */
+};
+
+enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
+
+/* Message of the last error on this thread ("" if none).  Never NULL. */
+const char* pa_last_error(void);
+
+/* Version of this ABI (bumped on any incompatible change). */
+int32_t pa_abi_version(void);
+
+/* ======================================================================================
+ * Host block manager.
+ *
+ * [TT] "How the Architecture Works": logical blocks of a sequence map through its block table
+ * to physical blocks anywhere in the pool; a new block is taken from the free block pool when
+ * the current one is full.  [VP] "1. Underlying Mechanism": B=16 (or 32) tokens per block;
+ * token 17 takes a new block; a forked child shares the parent's blocks and copy-on-write
+ * gives it private copies.  [KC] "PagedAttention: borrowing virtual memory": one reference
+ * count per physical block; a block rejoins the pool only at count zero; a sequence about to
+ * write into a shared block first receives a private copy.
+ *
+ * Fixed policy (the pages leave it open; this is part of the contract, so block tables, slot
+ * mappings and copy lists are reproducible bit for bit):
+ *   - the free pool is FIFO: allocation takes the front, a freed block is appended at the
+ *     back; a freed sequence releases its blocks in logical order;
+ *   - appends to a batch are served in batch order; a sequence copies its last block iff the
+ *     block is partly filled and its count is above one at that sequence's turn (of k sharers
+ *     appending in one call, the first k-1 copy, the last writes in place); the copy covers the
+ *     whole block (all kv-heads, all slots, K and V);
+ *   - a batch names each sequence at most once.
+ * ====================================================================================== */
+
+typedef struct pa_bm pa_bm;
+
+typedef struct {
+  int32_t num_blocks;       /* pool size                                                  */
+  int32_t block_size;       /* B                                                          */
+  int32_t free_blocks;      /* blocks with count 0                                        */
+  int32_t used_blocks;      /* blocks with count >= 1                                     */
+  int32_t shared_blocks;    /* blocks with count >= 2                                     */
+  int32_t num_seqs;         /* live sequences                                             */
+  int64_t logical_blocks;   /* sum over sequences of table entries                        */
+  int64_t live_tokens;      /* sum over sequences of their token counts                   */
+  int64_t tail_waste_slots; /* logical_blocks * B - live_tokens (unused slots in last blocks) */
+  int64_t forks;            /* pa_bm_fork calls so far                                    */
+  int64_t cow_copies;       /* block copies issued by copy-on-write so far                */
+  double usage;             /* used_blocks / num_blocks: the pool saturation to monitor,
+                               [TT] "Summing it Up", item 3                                */
+} pa_bm_stats_t;
+
+/* Create a manager over physical blocks [0, num_blocks) of block_size tokens each.
+ * init_free_order: NULL (ids in increasing order) or a host array of num_blocks ints that is a
+ * permutation of [0, num_blocks), giving the initial FIFO order.  *out receives the handle. */
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* init_free_order,
+                       pa_bm** out);
+
+/* Destroy a handle (NULL is accepted).  Device memory is not touched. */
+pa_status pa_bm_destroy(pa_bm* bm);
+
+/* New sequence holding n_tokens >= 0 tokens (a prefill): takes ceil(n/B) blocks.
+ * slots_out: NULL or a host array of n_tokens ints receiving the slot of positions 0..n-1. */
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id, int32_t n_tokens, int32_t* slots_out);
+
+/* Append tokens_each >= 0 tokens to each of n_seqs distinct sequences, in batch order
+ * (tokens_each = 1 is one decode step; larger values append a chunk).
+ * slots_out:      host array of n_seqs * tokens_each ints (sequence-major) receiving slots.
+ * copy_pairs_out: host array of pairs_cap * 2 ints receiving the copy-on-write pairs
+ *                 (src_block, dst_block) in the order made; may be NULL if pairs_cap == 0.
+ * n_copies_out:   receives the number of pairs written.
+ * The pairs must be applied (pa_copy_blocks) before the new tokens are written
+ * (pa_cache_write), on the same stream.  Errors: PA_ERR_OUT_OF_BLOCKS if the pool cannot
+ * hold the new blocks and copies; PA_ERR_INVALID_ARG if more than pairs_cap copies are
+ * needed or an id repeats; PA_ERR_UNKNOWN_SEQ.  On error nothing changes. */
+pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
+                             int32_t tokens_each, int32_t* slots_out, int32_t* copy_pairs_out,
+                             int32_t pairs_cap, int32_t* n_copies_out);
+
+/* Zero-copy fork ([VP] "Zero-Copy Forking & Parallel Sampling"): child receives the parent's
+ * table and length; every block's count goes up by one.  No device work. */
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id);
+
+/* Drop a sequence; each of its blocks' counts goes down by one and blocks reaching zero are
+ * appended to the free pool in logical order ([KC] answer A6). */
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
+
+/* Block tables and context lengths of n sequences.
+ * tables_out: host [n, max_blocks] ints, row i = physical blocks of seq_ids[i], padded -1.
+ * ctx_lens_out: host [n] ints (NULL allowed).  PA_ERR_INVALID_ARG if a sequence holds more
+ * than max_blocks blocks. */
+pa_status pa_bm_block_tables(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                             int32_t* tables_out, int32_t* ctx_lens_out);
+
+/* Token count of one sequence. */
+pa_status pa_bm_seq_len(pa_bm* bm, int64_t seq_id, int32_t* n_out);
+
+/* Reference count of one physical block. */
+pa_status pa_bm_refcount(pa_bm* bm, int32_t block, int32_t* out);
+
+/* The free pool, front first: writes min(cap, free) ids to out and the full count to *n_out. */
+pa_status pa_bm_free_list(pa_bm* bm, int32_t* out, int32_t cap, int32_t* n_out);
+
+/* Pool statistics ([TT] "Summing it Up": monitor the physical block pool saturation). */
+pa_status pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out);
+
+/* ---- host utilities ---------------------------------------------------------------- */
+
+typedef struct {
+  int64_t total_actual_tokens; /* sum of lengths                                   */
+  int64_t paged_slots;         /* B * sum ceil(len / B)                            */
+  int64_t naive_slots;         /* max_seq_len * n                                  */
+  double paged_fragmentation_pct;  /* 100 (paged - actual) / paged   (unrounded) */
+  double naive_fragmentation_pct;  /* 100 (naive - actual) / naive   (unrounded) */
+  double memory_reduction_factor;  /* naive / paged                  (unrounded) */
+} pa_accounting_t;
+
+/* Slot accounting of [KC] "Worked Example 1" for n request lengths (host arrays). */
+pa_status pa_accounting(const int32_t* lens, int32_t n, int32_t block_size, int32_t max_seq_len,
+                        pa_accounting_t* out);
+
+/* Host check of a block table before upload: every entry a sequence uses (the first
+ * ceil(ctx_len/B)) lies in [0, num_blocks), 1 <= ctx_len <= max_blocks * B.  PA_OK or
+ * PA_ERR_INVALID_ARG naming the first bad row. */
+pa_status pa_validate_tables(const int32_t* tables, const int32_t* ctx_lens, int32_t S,
+                             int32_t max_blocks, int32_t block_size, int32_t num_blocks);
+
+/* ======================================================================================
+ * Device operations (HIP, gfx950).  Supported: dtype F32 or BF16; head_dim D in {64, 128};
+ * block size B in {16, 32}; Hq a multiple of Hkv.  Tensors are C-contiguous; every pointer
+ * must be 16-byte aligned.
+ * ====================================================================================== */
+
+/* Cache write (the "store only the new token's K/V" step: [TT] "The Hidden Tax"; [VP]
+ * "writing only new token deltas").  For t in [0, T): if slot_mapping[t] is in
+ * [0, num_blocks * B) the key key[t] ([Hkv, D]) goes to k_cache[slot / B][h][slot % B][:] and
+ * value[t] to v_cache[slot / B][h][:][slot % B]; other slots (negative: padding) are skipped.
+ * Bit copy, no arithmetic.  Slots within one call must be distinct.
+ * key, value: device [T, Hkv, D] of dtype;  slot_mapping: device int32 [T]. */
+pa_status pa_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
+                         int32_t B, int32_t num_blocks, int32_t dtype, void* stream);
+
+/* Copy-on-write block copies ([KC] "PagedAttention: borrowing virtual memory"): for each of
+ * the P pairs (src, dst) in device int32 [P, 2], physical block dst of both pools becomes a
+ * bit copy of block src.  Pairs as produced by pa_bm_append_slots: distinct dst, no dst is
+ * also a src; ids outside [0, num_blocks) are skipped.  Enqueue before pa_cache_write. */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t P,
+                         int32_t num_blocks, int32_t Hkv, int32_t D, int32_t B, int32_t dtype,
+                         void* stream);
+
+/* Workspace bytes pa_decode needs for S sequences of at most max_ctx_len tokens.
+ * partition_tokens: the split-K partition length pa_decode will be called with (0 = the
+ * library's choice; the size returned then covers any choice it makes). */
+pa_status pa_decode_workspace_size(int32_t S, int32_t Hq, int32_t D, int32_t max_ctx_len,
+                                   int32_t partition_tokens, size_t* bytes);
+
+/* Paged decode attention: one query token per sequence and head over the sequence's cached
+ * K/V, reached through its block table ([TT] "Under the Hood: The CUDA Kernel Engineering":
+ * key/value addresses come from the block table, access stays coalesced, the unaligned last
+ * block is handled; [KC] "Common misconception": the same scores and softmax as dense
+ * attention).
+ *
+ *   out[s, h, :] = sum_j softmax_j(scale * q[s,h,:] . K_s[j, h / (Hq/Hkv), :]) V_s[j, ...]
+ *   over the ctx_lens[s] tokens of sequence s (including the one written this step).
+ *
+ * q, out: device [S, Hq, D] of dtype (out is rounded to nearest-even for BF16).
+ * block_tables: device int32 [S, max_blocks]; ctx_lens: device int32 [S], each in
+ * [1, max_blocks * B] and <= max_ctx_len.  Positions >= ctx_len of a sequence never influence
+ * its output (NaN or Inf there is harmless).  Computation: fp32 accumulation; split-K over
+ * partitions of partition_tokens tokens (0 = library's choice, else a multiple of 32 in
+ * [32, 8192]) followed by a merge.  workspace: device buffer of at least
+ * pa_decode_workspace_size(S, Hq, D, max_ctx_len, partition_tokens) bytes (may be NULL if
+ * that size is 0).  Deterministic: results depend on logical positions only, not on which
+ * physical blocks hold them. */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* ctx_lens, int32_t S, int32_t Hq,
+                    int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks, int32_t max_blocks,
+                    int32_t max_ctx_len, float scale, int32_t dtype, int32_t partition_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Chunked-query paged attention (prefill of the tokens past a cached prefix, [KC]
+ * "RadixAttention": only the tokens past the divergence need a prefill pass).  Each of the S
+ * sequences has ctx_lens[s] tokens in the pool INCLUDING its C new ones (already written by
+ * pa_cache_write); query row i (0 <= i < C) sits at position ctx_lens[s] - C + i and attends
+ * to positions 0 .. ctx_lens[s] - C + i (causal inside the chunk).
+ * q, out: device [S, C, Hq, D] (BF16).  ctx_lens[s] in [C, max_blocks * B].  fp32
+ * accumulation on the matrix cores.  No workspace. */
+pa_status pa_chunk_attend(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* ctx_lens, int32_t S,
+                          int32_t C, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                          int32_t num_blocks, int32_t max_blocks, float scale, int32_t dtype,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,371 @@
+"""ctypes binding of libpa.so (include/pa.h).  Argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+computation of its own: it reads sizes, dtypes and device pointers off torch
+tensors (or numpy arrays for host buffers), calls the library and raises
+``PaError`` on a non-zero status.  Device work is enqueued on the given stream
+(default: torch's current stream) and is asynchronous, like the C calls.
+
+The library is required: importing this module fails loudly if libpa.so has not
+been built (there is no fallback of any kind).
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -m paged_kv_cache_378_amd.build "
+        "or __graft_entry__.build())")
+
+_lib = C.CDLL(LIB_PATH)
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_OUT_OF_BLOCKS = -2
+PA_ERR_UNKNOWN_SEQ = -3
+PA_ERR_SEQ_EXISTS = -4
+PA_ERR_UNSUPPORTED = -5
+PA_ERR_WORKSPACE = -6
+PA_ERR_HIP = -7
+PA_DTYPE_F32 = 0
+PA_DTYPE_BF16 = 1
+
+_i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+_pi32 = C.POINTER(C.c_int32)
+_pi64 = C.POINTER(C.c_int64)
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class OutOfBlocks(PaError):
+    pass
+
+
+class UnknownSeq(PaError):
+    pass
+
+
+class SeqExists(PaError):
+    pass
+
+
+_ERRORS = {PA_ERR_OUT_OF_BLOCKS: OutOfBlocks, PA_ERR_UNKNOWN_SEQ: UnknownSeq,
+           PA_ERR_SEQ_EXISTS: SeqExists}
+
+
+class pa_bm_stats_t(C.Structure):
+    _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("free_blocks", _i32),
+                ("used_blocks", _i32), ("shared_blocks", _i32), ("num_seqs", _i32),
+                ("logical_blocks", _i64), ("live_tokens", _i64), ("tail_waste_slots", _i64),
+                ("forks", _i64), ("cow_copies", _i64), ("usage", C.c_double)]
+
+
+class pa_accounting_t(C.Structure):
+    _fields_ = [("total_actual_tokens", _i64), ("paged_slots", _i64), ("naive_slots", _i64),
+                ("paged_fragmentation_pct", C.c_double), ("naive_fragmentation_pct", C.c_double),
+                ("memory_reduction_factor", C.c_double)]
+
+
+_SIGS = {
+    "pa_last_error": ([], C.c_char_p),
+    "pa_abi_version": ([], _i32),
+    "pa_bm_create": ([_i32, _i32, _pi32, C.POINTER(_vp)], _i32),
+    "pa_bm_destroy": ([_vp], _i32),
+    "pa_bm_add_seq": ([_vp, _i64, _i32, _pi32], _i32),
+    "pa_bm_append_slots": ([_vp, _pi64, _i32, _i32, _pi32, _pi32, _i32, _pi32], _i32),
+    "pa_bm_fork": ([_vp, _i64, _i64], _i32),
+    "pa_bm_free_seq": ([_vp, _i64], _i32),
+    "pa_bm_block_tables": ([_vp, _pi64, _i32, _i32, _pi32, _pi32], _i32),
+    "pa_bm_seq_len": ([_vp, _i64, _pi32], _i32),
+    "pa_bm_refcount": ([_vp, _i32, _pi32], _i32),
+    "pa_bm_free_list": ([_vp, _pi32, _i32, _pi32], _i32),
+    "pa_bm_stats": ([_vp, C.POINTER(pa_bm_stats_t)], _i32),
+    "pa_accounting": ([_pi32, _i32, _i32, _i32, C.POINTER(pa_accounting_t)], _i32),
+    "pa_validate_tables": ([_pi32, _pi32, _i32, _i32, _i32, _i32], _i32),
+    "pa_cache_write": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
+    "pa_copy_blocks": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
+    "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
+    "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                   _f32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "pa_chunk_attend": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                         _i32, _f32, _i32, _vp], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        msg = _lib.pa_last_error().decode()
+        raise _ERRORS.get(status, PaError)(status, msg)
+
+
+def _i32_host(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr32(a: np.ndarray):
+    return a.ctypes.data_as(_pi32)
+
+
+def pa_abi_version() -> int:
+    return _lib.pa_abi_version()
+
+
+# -- block manager -------------------------------------------------------------------
+
+def pa_bm_create(num_blocks: int, block_size: int, init_free_order=None):
+    h = _vp()
+    order = None if init_free_order is None else _i32_host(init_free_order)
+    _check(_lib.pa_bm_create(num_blocks, block_size, None if order is None else _ptr32(order),
+                             C.byref(h)))
+    return h
+
+
+def pa_bm_destroy(h) -> None:
+    _check(_lib.pa_bm_destroy(h))
+
+
+def pa_bm_add_seq(h, seq_id: int, n_tokens: int) -> np.ndarray:
+    slots = np.empty(max(n_tokens, 0), np.int32)
+    _check(_lib.pa_bm_add_seq(h, seq_id, n_tokens, _ptr32(slots)))
+    return slots
+
+
+def pa_bm_append_slots(h, seq_ids, tokens_each: int, pairs_cap: int | None = None):
+    ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+    slots = np.empty(len(ids) * tokens_each, np.int32)
+    cap = len(ids) if pairs_cap is None else pairs_cap
+    pairs = np.empty((max(cap, 1), 2), np.int32)
+    n = _i32()
+    _check(_lib.pa_bm_append_slots(h, ids.ctypes.data_as(_pi64), len(ids), tokens_each,
+                                   _ptr32(slots), _ptr32(pairs), cap, C.byref(n)))
+    return slots, pairs[: n.value].copy()
+
+
+def pa_bm_fork(h, parent: int, child: int) -> None:
+    _check(_lib.pa_bm_fork(h, parent, child))
+
+
+def pa_bm_free_seq(h, seq_id: int) -> None:
+    _check(_lib.pa_bm_free_seq(h, seq_id))
+
+
+def pa_bm_block_tables(h, seq_ids, max_blocks: int, tables_out=None, ctx_lens_out=None):
+    ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+    tables = np.empty((len(ids), max_blocks), np.int32) if tables_out is None else tables_out
+    lens = np.empty(len(ids), np.int32) if ctx_lens_out is None else ctx_lens_out
+    assert tables.dtype == np.int32 and tables.flags.c_contiguous and tables.shape == (len(ids), max_blocks)
+    assert lens.dtype == np.int32 and lens.flags.c_contiguous and lens.shape == (len(ids),)
+    _check(_lib.pa_bm_block_tables(h, ids.ctypes.data_as(_pi64), len(ids), max_blocks,
+                                   _ptr32(tables), _ptr32(lens)))
+    return tables, lens
+
+
+def pa_bm_seq_len(h, seq_id: int) -> int:
+    n = _i32()
+    _check(_lib.pa_bm_seq_len(h, seq_id, C.byref(n)))
+    return n.value
+
+
+def pa_bm_refcount(h, block: int) -> int:
+    n = _i32()
+    _check(_lib.pa_bm_refcount(h, block, C.byref(n)))
+    return n.value
+
+
+def pa_bm_free_list(h) -> np.ndarray:
+    n = _i32()
+    _check(_lib.pa_bm_free_list(h, None, 0, C.byref(n)))
+    out = np.empty(n.value, np.int32)
+    _check(_lib.pa_bm_free_list(h, _ptr32(out), n.value, C.byref(n)))
+    return out
+
+
+def pa_bm_stats(h) -> dict:
+    st = pa_bm_stats_t()
+    _check(_lib.pa_bm_stats(h, C.byref(st)))
+    return {name: getattr(st, name) for name, _ in pa_bm_stats_t._fields_}
+
+
+def pa_accounting(lens, block_size: int, max_seq_len: int) -> dict:
+    a = _i32_host(lens)
+    r = pa_accounting_t()
+    _check(_lib.pa_accounting(_ptr32(a), len(a), block_size, max_seq_len, C.byref(r)))
+    return {name: getattr(r, name) for name, _ in pa_accounting_t._fields_}
+
+
+def pa_validate_tables(tables, ctx_lens, block_size: int, num_blocks: int) -> None:
+    t = _i32_host(tables)
+    l = _i32_host(ctx_lens)
+    _check(_lib.pa_validate_tables(_ptr32(t), _ptr32(l), t.shape[0], t.shape[1], block_size,
+                                   num_blocks))
+
+
+class BlockManager:
+    """Owning wrapper of a pa_bm handle; each method calls the C entry point it names."""
+
+    def __init__(self, num_blocks: int, block_size: int, init_free_order=None):
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.h = pa_bm_create(num_blocks, block_size, init_free_order)
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h is not None and h.value:
+            _lib.pa_bm_destroy(h)
+            self.h = None
+
+    def add_seq(self, seq_id, n_tokens):
+        return pa_bm_add_seq(self.h, seq_id, n_tokens)
+
+    def append_slots(self, seq_ids, tokens_each, pairs_cap=None):
+        return pa_bm_append_slots(self.h, seq_ids, tokens_each, pairs_cap)
+
+    def fork(self, parent, child):
+        pa_bm_fork(self.h, parent, child)
+
+    def free_seq(self, seq_id):
+        pa_bm_free_seq(self.h, seq_id)
+
+    def block_tables(self, seq_ids, max_blocks, tables_out=None, ctx_lens_out=None):
+        return pa_bm_block_tables(self.h, seq_ids, max_blocks, tables_out, ctx_lens_out)
+
+    def seq_len(self, seq_id):
+        return pa_bm_seq_len(self.h, seq_id)
+
+    def refcount(self, block):
+        return pa_bm_refcount(self.h, block)
+
+    def free_list(self):
+        return pa_bm_free_list(self.h)
+
+    def stats(self):
+        return pa_bm_stats(self.h)
+
+
+# -- device operations (torch tensors in, nothing computed here) -----------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return PA_DTYPE_BF16
+    raise PaError(PA_ERR_UNSUPPORTED, f"dtype {t.dtype} is not supported")
+
+
+def _dev(t, what: str, dtype=None):
+    if not t.is_cuda:
+        raise PaError(PA_ERR_INVALID_ARG, f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise PaError(PA_ERR_INVALID_ARG, f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise PaError(PA_ERR_INVALID_ARG, f"{what} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+
+
+def _pool_shape(k_cache, v_cache):
+    NB, Hkv, B, D = k_cache.shape
+    if tuple(v_cache.shape) != (NB, Hkv, D, B) or v_cache.dtype != k_cache.dtype:
+        raise PaError(PA_ERR_INVALID_ARG,
+                      f"v_cache must be [num_blocks, Hkv, D, B] = {(NB, Hkv, D, B)} of "
+                      f"{k_cache.dtype}, got {tuple(v_cache.shape)} {v_cache.dtype}")
+    return NB, Hkv, B, D
+
+
+def pa_cache_write(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    torch = _torch()
+    NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
+        raise PaError(PA_ERR_INVALID_ARG, "key and value must be [T, Hkv, D]")
+    if key.dtype != k_cache.dtype or value.dtype != k_cache.dtype:
+        raise PaError(PA_ERR_INVALID_ARG, "key/value dtype must match the pools")
+    if tuple(slot_mapping.shape) != (T,):
+        raise PaError(PA_ERR_INVALID_ARG, "slot_mapping must be [T]")
+    _check(_lib.pa_cache_write(_dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
+                               _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32),
+                               T, Hkv, D, B, NB, _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    torch = _torch()
+    NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
+    P = pairs.shape[0]
+    if P and tuple(pairs.shape) != (P, 2):
+        raise PaError(PA_ERR_INVALID_ARG, "pairs must be [P, 2]")
+    if P == 0:
+        return
+    _check(_lib.pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                               _dev(pairs, "pairs", torch.int32), P, NB, Hkv, D, B,
+                               _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_decode_workspace_size(S: int, Hq: int, D: int, max_ctx_len: int,
+                             partition_tokens: int = 0) -> int:
+    n = _sz()
+    _check(_lib.pa_decode_workspace_size(S, Hq, D, max_ctx_len, partition_tokens, C.byref(n)))
+    return n.value
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, max_ctx_len: int, scale: float,
+              partition_tokens: int = 0, workspace=None, stream=None) -> None:
+    torch = _torch()
+    NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
+    S, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise PaError(PA_ERR_INVALID_ARG, "q/out must be [S, Hq, D] of the pools' dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(ctx_lens.shape) != (S,):
+        raise PaError(PA_ERR_INVALID_ARG, "block_tables must be [S, max_blocks], ctx_lens [S]")
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                            workspace.numel() * workspace.element_size())
+    _check(_lib.pa_decode(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                          _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32),
+                          _dev(ctx_lens, "ctx_lens", torch.int32), S, Hq, Hkv, D, B, NB,
+                          block_tables.shape[1], max_ctx_len, float(scale), _dtype_code(q),
+                          partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_chunk_attend(out, q, k_cache, v_cache, block_tables, ctx_lens, scale: float,
+                    stream=None) -> None:
+    torch = _torch()
+    NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
+    S, Cn, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (S, Cn, Hq, D) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise PaError(PA_ERR_INVALID_ARG, "q/out must be [S, C, Hq, D] of the pools' dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(ctx_lens.shape) != (S,):
+        raise PaError(PA_ERR_INVALID_ARG, "block_tables must be [S, max_blocks], ctx_lens [S]")
+    _check(_lib.pa_chunk_attend(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                _dev(v_cache, "v_cache"),
+                                _dev(block_tables, "block_tables", torch.int32),
+                                _dev(ctx_lens, "ctx_lens", torch.int32), S, Cn, Hq, Hkv, D, B, NB,
+                                block_tables.shape[1], float(scale), _dtype_code(q),
+                                _stream(stream)))

@@ -1,0 +1,394 @@
+// Host block manager: free pool, reference counts, fork, copy-on-write, block tables.
+//
+// Behaviour (see the policy block in pa.h):
+//  * "Taming the Tail", "How the Architecture Works": logical blocks of a sequence map through
+//    a block table to physical blocks anywhere in the pool; a full current block means a new
+//    block from the free block pool.
+//  * "vLLM PagedAttention" (tinycto), "1. Underlying Mechanism": with B = 16 the 17th token
+//    takes a new block on the fly; forked children share the parent's blocks; copy-on-write
+//    gives a writer its own copy.
+//  * KV-cache chapter, "PagedAttention: borrowing virtual memory" and answer A6: per-block
+//    reference counts; a block is free again only at count zero; a writer into a shared block
+//    first receives a private copy.
+//
+// The free pool is a ring buffer of capacity num_blocks (a block is in it at most once), so
+// allocation and release are O(1).  Every mutating call validates and sizes its work in a
+// dry run first, so a failing call changes nothing.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pa.h"
+#include "pa_status.h"
+
+namespace {
+
+struct Seq {
+  std::vector<int32_t> blocks;  // physical ids in logical order
+  int32_t n = 0;                // tokens held
+};
+
+}  // namespace
+
+struct pa_bm {
+  int32_t num_blocks = 0;
+  int32_t B = 0;
+  std::vector<int32_t> ref;   // per-block reference count
+  std::vector<int32_t> ring;  // FIFO free pool
+  int32_t head = 0;           // index of the front of the pool in `ring`
+  int32_t nfree = 0;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t forks = 0;
+  int64_t cow_copies = 0;
+
+  int32_t take() {  // caller guarantees nfree > 0
+    int32_t b = ring[head];
+    head = (head + 1 == num_blocks) ? 0 : head + 1;
+    --nfree;
+    ref[b] = 1;
+    return b;
+  }
+  void release(int32_t b) {
+    if (--ref[b] == 0) {
+      int32_t tail = head + nfree;
+      if (tail >= num_blocks) tail -= num_blocks;
+      ring[tail] = b;
+      ++nfree;
+    }
+  }
+  // New blocks a sequence of n tokens needs to grow by k tokens (block boundaries crossed).
+  int64_t boundary_blocks(int32_t n, int32_t k) const {
+    if (k <= 0) return 0;
+    // positions n .. n+k-1 that are multiples of B
+    int64_t first = (static_cast<int64_t>(n) + B - 1) / B;             // multiples >= n
+    int64_t last = (static_cast<int64_t>(n) + k - 1) / B;              // multiples <= n+k-1
+    return last - first + 1;
+  }
+};
+
+using pa::fail;
+using pa::ok;
+
+extern "C" {
+
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* init_free_order,
+                       pa_bm** out) {
+  if (!out) return fail(PA_ERR_INVALID_ARG, "pa_bm_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_create: num_blocks (%d) and block_size (%d) must be > 0",
+                num_blocks, block_size);
+  pa_bm* bm = new (std::nothrow) pa_bm();
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_create: out of host memory");
+  try {
+    bm->num_blocks = num_blocks;
+    bm->B = block_size;
+    bm->ref.assign(num_blocks, 0);
+    bm->ring.resize(num_blocks);
+    if (init_free_order) {
+      std::vector<char> seen(num_blocks, 0);
+      for (int32_t i = 0; i < num_blocks; ++i) {
+        int32_t b = init_free_order[i];
+        if (b < 0 || b >= num_blocks || seen[b]) {
+          delete bm;
+          return fail(PA_ERR_INVALID_ARG,
+                      "pa_bm_create: init_free_order is not a permutation (entry %d = %d)", i, b);
+        }
+        seen[b] = 1;
+        bm->ring[i] = b;
+      }
+    } else {
+      for (int32_t i = 0; i < num_blocks; ++i) bm->ring[i] = i;
+    }
+    bm->head = 0;
+    bm->nfree = num_blocks;
+  } catch (...) {
+    delete bm;
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_create: out of host memory");
+  }
+  *out = bm;
+  return ok();
+}
+
+pa_status pa_bm_destroy(pa_bm* bm) {
+  delete bm;
+  return ok();
+}
+
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id, int32_t n_tokens, int32_t* slots_out) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: NULL handle");
+  if (n_tokens < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: n_tokens %d < 0", n_tokens);
+  if (bm->seqs.count(seq_id))
+    return fail(PA_ERR_SEQ_EXISTS, "pa_bm_add_seq: sequence %lld exists", (long long)seq_id);
+  const int64_t need = bm->boundary_blocks(0, n_tokens);
+  if (need > bm->nfree)
+    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_add_seq: needs %lld blocks, %d free",
+                (long long)need, bm->nfree);
+  try {
+    Seq s;
+    s.blocks.reserve(need);
+    for (int64_t i = 0; i < need; ++i) s.blocks.push_back(bm->take());
+    s.n = n_tokens;
+    if (slots_out) {
+      const int32_t B = bm->B;
+      for (int32_t j = 0; j < n_tokens; ++j) slots_out[j] = s.blocks[j / B] * B + j % B;
+    }
+    bm->seqs.emplace(seq_id, std::move(s));
+  } catch (...) {
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: out of host memory");
+  }
+  return ok();
+}
+
+pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
+                             int32_t tokens_each, int32_t* slots_out, int32_t* copy_pairs_out,
+                             int32_t pairs_cap, int32_t* n_copies_out) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: NULL handle");
+  if (n_seqs < 0 || tokens_each < 0 || pairs_cap < 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: negative count");
+  if (n_seqs > 0 && !seq_ids) return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: seq_ids NULL");
+  if (n_seqs > 0 && tokens_each > 0 && !slots_out)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: slots_out NULL");
+  if (pairs_cap > 0 && !copy_pairs_out)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: copy_pairs_out NULL");
+  if (n_copies_out) *n_copies_out = 0;
+  const int32_t B = bm->B;
+
+  // Dry run: resolve ids, reject repeats, count blocks and copies in batch order.
+  std::vector<Seq*> batch(n_seqs);
+  std::vector<char> cow(n_seqs, 0);
+  int64_t need = 0, copies = 0;
+  try {
+    std::unordered_set<int64_t> seen;
+    seen.reserve(static_cast<size_t>(n_seqs) * 2);
+    std::unordered_map<int32_t, int32_t> dec;  // block -> copies already made from it
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      auto it = bm->seqs.find(seq_ids[i]);
+      if (it == bm->seqs.end())
+        return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_append_slots: unknown sequence %lld",
+                    (long long)seq_ids[i]);
+      if (!seen.insert(seq_ids[i]).second)
+        return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: sequence %lld repeats in the batch",
+                    (long long)seq_ids[i]);
+      Seq* s = &it->second;
+      batch[i] = s;
+      if (tokens_each == 0) continue;
+      if (s->n % B != 0) {
+        const int32_t last = s->blocks.back();
+        int32_t& d = dec[last];
+        if (bm->ref[last] - d > 1) {
+          cow[i] = 1;
+          ++d;
+          ++copies;
+          ++need;
+        }
+      }
+      if (static_cast<int64_t>(s->n) + tokens_each > INT32_MAX)
+        return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: sequence length overflows int32");
+      const int64_t grow = bm->boundary_blocks(s->n, tokens_each);
+      need += grow;
+      // Capacity now, so the commit below cannot throw half-way.
+      s->blocks.reserve(s->blocks.size() + static_cast<size_t>(grow));
+    }
+  } catch (...) {
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: out of host memory");
+  }
+  if (copies > pairs_cap)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: %lld copy pairs needed, capacity %d",
+                (long long)copies, pairs_cap);
+  if (need > bm->nfree)
+    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append_slots: needs %lld blocks, %d free",
+                (long long)need, bm->nfree);
+
+  // Commit.
+  try {
+    int32_t np = 0;
+    int64_t o = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      Seq* s = batch[i];
+      if (tokens_each == 0) continue;
+      if (cow[i]) {
+        const int32_t last = s->blocks.back();
+        const int32_t fresh = bm->take();
+        --bm->ref[last];  // stays >= 1: the dry run saw a count above one
+        s->blocks.back() = fresh;
+        copy_pairs_out[2 * np] = last;
+        copy_pairs_out[2 * np + 1] = fresh;
+        ++np;
+        ++bm->cow_copies;
+      }
+      for (int32_t t = 0; t < tokens_each; ++t) {
+        const int32_t pos = s->n;
+        if (pos % B == 0) s->blocks.push_back(bm->take());
+        slots_out[o++] = s->blocks[pos / B] * B + pos % B;
+        s->n = pos + 1;
+      }
+    }
+    if (n_copies_out) *n_copies_out = np;
+  } catch (...) {
+    // Unreachable: the dry run reserved every vector the commit grows.
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: out of host memory during commit");
+  }
+  return ok();
+}
+
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_fork: NULL handle");
+  auto it = bm->seqs.find(parent_id);
+  if (it == bm->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_fork: unknown parent %lld", (long long)parent_id);
+  if (bm->seqs.count(child_id))
+    return fail(PA_ERR_SEQ_EXISTS, "pa_bm_fork: child %lld exists", (long long)child_id);
+  try {
+    Seq child = it->second;  // copy of table and length
+    for (int32_t b : child.blocks) ++bm->ref[b];
+    bm->seqs.emplace(child_id, std::move(child));
+  } catch (...) {
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_fork: out of host memory");
+  }
+  ++bm->forks;
+  return ok();
+}
+
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_free_seq: NULL handle");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_free_seq: unknown sequence %lld", (long long)seq_id);
+  for (int32_t b : it->second.blocks) bm->release(b);
+  bm->seqs.erase(it);
+  return ok();
+}
+
+pa_status pa_bm_block_tables(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                             int32_t* tables_out, int32_t* ctx_lens_out) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_block_tables: NULL handle");
+  if (n < 0 || max_blocks < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_block_tables: negative size");
+  if (n > 0 && (!seq_ids || (max_blocks > 0 && !tables_out)))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_block_tables: NULL array");
+  std::vector<const Seq*> rows(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_block_tables: unknown sequence %lld",
+                  (long long)seq_ids[i]);
+    if (static_cast<int64_t>(it->second.blocks.size()) > max_blocks)
+      return fail(PA_ERR_INVALID_ARG, "pa_bm_block_tables: sequence %lld holds %zu blocks > %d",
+                  (long long)seq_ids[i], it->second.blocks.size(), max_blocks);
+    rows[i] = &it->second;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t* row = tables_out + static_cast<size_t>(i) * max_blocks;
+    const size_t k = rows[i]->blocks.size();
+    if (k) std::memcpy(row, rows[i]->blocks.data(), k * sizeof(int32_t));
+    std::fill(row + k, row + max_blocks, -1);
+    if (ctx_lens_out) ctx_lens_out[i] = rows[i]->n;
+  }
+  return ok();
+}
+
+pa_status pa_bm_seq_len(pa_bm* bm, int64_t seq_id, int32_t* n_out) {
+  if (!bm || !n_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_seq_len: NULL argument");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_seq_len: unknown sequence %lld", (long long)seq_id);
+  *n_out = it->second.n;
+  return ok();
+}
+
+pa_status pa_bm_refcount(pa_bm* bm, int32_t block, int32_t* out) {
+  if (!bm || !out) return fail(PA_ERR_INVALID_ARG, "pa_bm_refcount: NULL argument");
+  if (block < 0 || block >= bm->num_blocks)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_refcount: block %d outside [0, %d)", block,
+                bm->num_blocks);
+  *out = bm->ref[block];
+  return ok();
+}
+
+pa_status pa_bm_free_list(pa_bm* bm, int32_t* out, int32_t cap, int32_t* n_out) {
+  if (!bm || !n_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_free_list: NULL argument");
+  if (cap < 0 || (cap > 0 && !out)) return fail(PA_ERR_INVALID_ARG, "pa_bm_free_list: bad capacity");
+  const int32_t k = std::min(cap, bm->nfree);
+  for (int32_t i = 0; i < k; ++i) {
+    int32_t idx = bm->head + i;
+    if (idx >= bm->num_blocks) idx -= bm->num_blocks;
+    out[i] = bm->ring[idx];
+  }
+  *n_out = bm->nfree;
+  return ok();
+}
+
+pa_status pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out) {
+  if (!bm || !out) return fail(PA_ERR_INVALID_ARG, "pa_bm_stats: NULL argument");
+  pa_bm_stats_t st{};
+  st.num_blocks = bm->num_blocks;
+  st.block_size = bm->B;
+  st.free_blocks = bm->nfree;
+  for (int32_t r : bm->ref) {
+    if (r >= 1) ++st.used_blocks;
+    if (r >= 2) ++st.shared_blocks;
+  }
+  st.num_seqs = static_cast<int32_t>(bm->seqs.size());
+  for (const auto& kv : bm->seqs) {
+    st.logical_blocks += static_cast<int64_t>(kv.second.blocks.size());
+    st.live_tokens += kv.second.n;
+  }
+  st.tail_waste_slots = st.logical_blocks * bm->B - st.live_tokens;
+  st.forks = bm->forks;
+  st.cow_copies = bm->cow_copies;
+  st.usage = static_cast<double>(st.used_blocks) / bm->num_blocks;
+  *out = st;
+  return ok();
+}
+
+pa_status pa_accounting(const int32_t* lens, int32_t n, int32_t block_size, int32_t max_seq_len,
+                        pa_accounting_t* out) {
+  if (!out || (n > 0 && !lens)) return fail(PA_ERR_INVALID_ARG, "pa_accounting: NULL argument");
+  if (n <= 0 || block_size <= 0 || max_seq_len <= 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_accounting: n, block_size and max_seq_len must be > 0");
+  int64_t actual = 0, blocks = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (lens[i] < 0) return fail(PA_ERR_INVALID_ARG, "pa_accounting: length %d < 0", lens[i]);
+    actual += lens[i];
+    blocks += (static_cast<int64_t>(lens[i]) + block_size - 1) / block_size;
+  }
+  pa_accounting_t r{};
+  r.total_actual_tokens = actual;
+  r.paged_slots = blocks * block_size;
+  r.naive_slots = static_cast<int64_t>(max_seq_len) * n;
+  if (r.paged_slots == 0) return fail(PA_ERR_INVALID_ARG, "pa_accounting: all lengths are zero");
+  r.paged_fragmentation_pct =
+      100.0 * static_cast<double>(r.paged_slots - actual) / static_cast<double>(r.paged_slots);
+  r.naive_fragmentation_pct =
+      100.0 * static_cast<double>(r.naive_slots - actual) / static_cast<double>(r.naive_slots);
+  r.memory_reduction_factor = static_cast<double>(r.naive_slots) / static_cast<double>(r.paged_slots);
+  *out = r;
+  return ok();
+}
+
+pa_status pa_validate_tables(const int32_t* tables, const int32_t* ctx_lens, int32_t S,
+                             int32_t max_blocks, int32_t block_size, int32_t num_blocks) {
+  if (S < 0 || max_blocks <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_validate_tables: bad sizes");
+  if (S > 0 && (!tables || !ctx_lens)) return fail(PA_ERR_INVALID_ARG, "pa_validate_tables: NULL");
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t n = ctx_lens[s];
+    if (n < 1 || n > static_cast<int64_t>(max_blocks) * block_size)
+      return fail(PA_ERR_INVALID_ARG, "pa_validate_tables: row %d: ctx_len %lld outside [1, %lld]",
+                  s, (long long)n, (long long)max_blocks * block_size);
+    const int64_t used = (n + block_size - 1) / block_size;
+    const int32_t* row = tables + static_cast<size_t>(s) * max_blocks;
+    for (int64_t j = 0; j < used; ++j)
+      if (row[j] < 0 || row[j] >= num_blocks)
+        return fail(PA_ERR_INVALID_ARG, "pa_validate_tables: row %d entry %lld = %d outside [0, %d)",
+                    s, (long long)j, row[j], num_blocks);
+  }
+  return ok();
+}
+
+}  // extern "C"

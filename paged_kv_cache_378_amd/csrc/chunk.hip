@@ -1,13 +1,337 @@
-// Chunked-query paged attention (MFMA).  Placeholder until the kernel lands.
+// Chunked-query paged attention on the gfx950 matrix cores.
+//
+// What is computed: the prefill of the tokens past a cached prefix (KV-cache chapter,
+// "RadixAttention": only the tokens after the point of divergence need a prefill pass, over
+// the K/V blocks already in the pool).  Sequence s holds n = ctx_lens[s] tokens including its
+// C new ones; query row i sits at position n - C + i and attends to positions 0 .. n - C + i
+// (causal inside the chunk), with the same scores and softmax as dense attention (KV-cache
+// chapter, "Common misconception").  The K/V of every position are reached through the block
+// table ("Taming the Tail", "Under the Hood: The CUDA Kernel Engineering").
+//
+// Decomposition (CDNA4-specific):
+//   * a workgroup = (sequence, kv-head, block of TQ chunk tokens); its rows are the
+//     (token, query head) pairs of that kv-head's group, so every K/V tile loaded is used by
+//     all g heads (GQA) -- 256 rows per workgroup, 64 per wave, in 4 column tiles of 16;
+//   * K/V tiles of 32 keys are staged in LDS (double-buffered: the next tile's global loads
+//     are in flight while the current one is multiplied); rows are padded by 16 bytes so the
+//     16-lane operand reads hit distinct banks;
+//   * S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 32 keys x 16 rows per tile pair) puts keys on the
+//     MFMA rows so a query row's scores sit in one lane column: the row max needs only two
+//     cross-lane steps; O^T = V^T P^T contracts over the 32 keys with P taken straight from
+//     the score registers (V is stored transposed per block in the pool);
+//   * online softmax in the log2 domain, fp32 accumulation, P rounded to bf16 for the MFMA
+//     and the row sum accumulated from the same rounded values.
+
+#include <cmath>
+
 #include "device_common.h"
+
+namespace pa {
+
+namespace chunk {
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 64;
+constexpr int kNC = kRowsPerWave / 16;  // 16-row column tiles per wave
+constexpr int kRows = kWaves * kRowsPerWave;
+constexpr int kKT = 32;                 // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Args {
+  uint16_t* out;
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  int S, C, Hq, Hkv, G, TQ, max_blocks, num_blocks;
+  float scale_log2;
+};
+
+template <int D>
+struct Smem {
+  static constexpr int KROW = D * 2 + 16;      // bytes per key row of the K tile (padded)
+  static constexpr int VROW = kKT * 2 + 16;    // bytes per dim row of the V^T tile (padded)
+  static constexpr int KBYTES = kKT * KROW;
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int STAGE = KBYTES + VBYTES;
+};
+
+template <int D, int B>
+__global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
+  constexpr int NST = D / 32;  // QK k-steps
+  constexpr int NNT = D / 16;  // PV dim tiles
+  using SM = Smem<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SM::STAGE];
+
+  const int qb = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = wave_id();
+  const int r16 = lane & 15, gp = lane >> 4;
+  const int G = a.G, C = a.C;
+
+  const int n_raw = a.ctx_lens[s];
+  const int cap = a.max_blocks * B;
+  const bool bad = n_raw < C || n_raw > cap || C < 1;
+  const int n = bad ? min(max(n_raw, 0), cap) : n_raw;
+  const int base = n - C;               // position of chunk row 0 (may be < 0 if bad)
+  const int i0 = qb * a.TQ;             // first chunk token of this workgroup
+  const int i1 = min(C, i0 + a.TQ);
+  // keys this workgroup needs: 0 .. base + i1 - 1
+  const int kend = bad ? 0 : base + i1;
+  const int ntiles = (kend + kKT - 1) / kKT;
+
+  // ---- query operand: row rho = 64 w + 16 c + r16 -> (token i0 + rho / G, head rho % G)
+  int row_tok[kNC];   // chunk token of this lane's row in column tile c (-1: padding)
+  int row_head[kNC];
+  bf16x8 qop[kNC][NST];
+#pragma unroll
+  for (int c = 0; c < kNC; ++c) {
+    const int rho = kRowsPerWave * w + 16 * c + r16;
+    const int tok = i0 + rho / G;
+    const bool valid = rho < a.TQ * G && tok < i1;
+    row_tok[c] = valid ? tok : -1;
+    row_head[c] = rho % G;
+    const uint16_t* qp = a.q + ((static_cast<size_t>(s) * C + (valid ? tok : 0)) * a.Hq +
+                                kvh * G + (valid ? row_head[c] : 0)) * D;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (4 * st + gp));
+      if (!valid) u = make_uint4(0, 0, 0, 0);
+      qop[c][st] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  // ---- cooperative tile loads: 256 threads x 16 B per pass
+  // K tile: 32 keys x D dims (row-major)  -> KTILE_VECS 16-byte pieces
+  // V tile: D dims x 32 keys (transposed) -> VTILE_VECS 16-byte pieces
+  constexpr int KV_PER_ROW = D * 2 / 16;           // 16-byte pieces per key row
+  constexpr int KTILE_VECS = kKT * KV_PER_ROW;
+  constexpr int VP_PER_ROW = kKT * 2 / 16;         // 16-byte pieces per dim row (4)
+  constexpr int VTILE_VECS = D * VP_PER_ROW;
+  constexpr int PASSES_K = KTILE_VECS / (kWaves * kWave);
+  constexpr int PASSES_V = VTILE_VECS / (kWaves * kWave);
+  static_assert(KTILE_VECS % (kWaves * kWave) == 0 && VTILE_VECS % (kWaves * kWave) == 0, "");
+  const size_t head_stride = static_cast<size_t>(B) * D;
+  const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
+
+  uint4 pk[PASSES_K], pv[PASSES_V];
+  int bad_entry = 0;
+  auto gload = [&](int t) {
+    const int k0 = t * kKT;
+#pragma unroll
+    for (int p = 0; p < PASSES_K; ++p) {
+      const int e = tid + p * kWaves * kWave;
+      const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
+      const int j = min(k0 + key, kend - 1);   // clamp: never past the last needed key
+      int blk = trow[j / B];
+      if (blk < 0 || blk >= a.num_blocks) { bad_entry = 1; blk = 0; }
+      pk[p] = *reinterpret_cast<const uint4*>(
+          a.kc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(j % B) * D + piece * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES_V; ++p) {
+      const int e = tid + p * kWaves * kWave;
+      const int dim = e / VP_PER_ROW, piece = e % VP_PER_ROW;   // piece = 8 keys
+      const int j = min(k0 + 8 * piece, (kend - 1) & ~7);
+      int blk = trow[j / B];
+      if (blk < 0 || blk >= a.num_blocks) { bad_entry = 1; blk = 0; }
+      pv[p] = *reinterpret_cast<const uint4*>(
+          a.vc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(dim) * B + (j % B));
+      // Keys at or past kend carry weight 0, but their slots may hold anything (even NaN,
+      // and 0 * NaN = NaN inside the MFMA): zero them.
+      const int nvalid = kend - (k0 + 8 * piece);
+      if (nvalid < 8) {
+        uint16_t e8[8];
+        __builtin_memcpy(e8, &pv[p], 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= nvalid) e8[e] = 0;
+        __builtin_memcpy(&pv[p], e8, 16);
+      }
+    }
+  };
+  auto lstore = [&](int stage) {
+    unsigned char* kb = smem + stage * SM::STAGE;
+    unsigned char* vb = kb + SM::KBYTES;
+#pragma unroll
+    for (int p = 0; p < PASSES_K; ++p) {
+      const int e = tid + p * kWaves * kWave;
+      const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
+      *reinterpret_cast<uint4*>(kb + key * SM::KROW + piece * 16) = pk[p];
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES_V; ++p) {
+      const int e = tid + p * kWaves * kWave;
+      const int dim = e / VP_PER_ROW, piece = e % VP_PER_ROW;
+      *reinterpret_cast<uint4*>(vb + dim * SM::VROW + piece * 16) = pv[p];
+    }
+  };
+
+  float m_run[kNC], l_run[kNC];
+  f32x4 o[kNC][NNT];
+#pragma unroll
+  for (int c = 0; c < kNC; ++c) {
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NNT; ++i) o[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int stage = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+    const unsigned char* kb = smem + stage * SM::STAGE;
+    const unsigned char* vb = kb + SM::KBYTES;
+    const int k0 = t * kKT;
+
+    // S^T = K Q^T : row r16 of key group m is key 8*(r16/4) + 4*m + r16%4 of the tile
+    f32x4 sacc[2][kNC];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int key = 8 * (r16 >> 2) + 4 * m + (r16 & 3);
+      bf16x8 kop[NST];
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+        kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + key * SM::KROW + (4 * st + gp) * 16));
+#pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        sacc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+          sacc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], qop[c][st], sacc[m][c], 0, 0, 0);
+      }
+    }
+
+    // online softmax per column tile; lane (gp, r16) owns keys k0 + 8 gp + j of row r16
+    bf16x8 pop[kNC];
+    float alpha[kNC];
+#pragma unroll
+    for (int c = 0; c < kNC; ++c) {
+      const int limit = row_tok[c] < 0 ? -1 : base + row_tok[c];  // last visible position
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = sacc[j >> 2][c][j & 3] * a.scale_log2;
+        x[j] = (k0 + 8 * gp + j <= limit) ? v : -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[c], mx);
+      // rows that have seen nothing yet (m_new = -inf) keep zero weights
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      alpha[c] = exp2f(m_run[c] - m_use);
+      m_run[c] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const __bf16 pb = static_cast<__bf16>(exp2f(x[j] - m_use));
+        pop[c][j] = pb;
+        psum += static_cast<float>(pb);
+      }
+      l_run[c] = l_run[c] * alpha[c] + psum;
+    }
+
+    // O^T += V^T P^T over the 32 keys (V of keys past kend was zeroed when staged).
+#pragma unroll
+    for (int ni = 0; ni < NNT; ++ni) {
+      const bf16x8 vop = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(vb + (16 * ni + r16) * SM::VROW + gp * 16));
+#pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        o[c][ni] *= alpha[c];
+        o[c][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[c], o[c][ni], 0, 0, 0);
+      }
+    }
+
+    if (t + 1 < ntiles) lstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  // bad table entries anywhere in the workgroup poison its outputs
+  const int any_bad = __syncthreads_or(bad_entry);
+
+  // ---- normalise and store: lane holds row r16 of tile c, dims 16 ni + 4 gp + i
+#pragma unroll
+  for (int c = 0; c < kNC; ++c) {
+    float l = l_run[c];
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (row_tok[c] < 0) continue;
+    const float inv = (bad || any_bad) ? NAN : 1.f / l;
+    uint16_t* op = a.out + ((static_cast<size_t>(s) * C + row_tok[c]) * a.Hq + kvh * G + row_head[c]) * D;
+#pragma unroll
+    for (int ni = 0; ni < NNT; ++ni) {
+      uint2 pk2;
+      pk2.x = static_cast<uint32_t>(f32_to_bf16(o[c][ni][0] * inv)) |
+              (static_cast<uint32_t>(f32_to_bf16(o[c][ni][1] * inv)) << 16);
+      pk2.y = static_cast<uint32_t>(f32_to_bf16(o[c][ni][2] * inv)) |
+              (static_cast<uint32_t>(f32_to_bf16(o[c][ni][3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(op + 16 * ni + 4 * gp) = pk2;
+    }
+  }
+}
+
+}  // namespace chunk
+}  // namespace pa
+
+using namespace pa;
 
 extern "C" pa_status pa_chunk_attend(void* out, const void* q, const void* k_cache,
                                      const void* v_cache, const int32_t* block_tables,
                                      const int32_t* ctx_lens, int32_t S, int32_t C, int32_t Hq,
                                      int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
                                      int32_t max_blocks, float scale, int32_t dtype, void* stream) {
-  (void)out; (void)q; (void)k_cache; (void)v_cache; (void)block_tables; (void)ctx_lens; (void)S;
-  (void)C; (void)Hq; (void)Hkv; (void)D; (void)B; (void)num_blocks; (void)max_blocks;
-  (void)scale; (void)dtype; (void)stream;
-  return pa::fail(PA_ERR_UNSUPPORTED, "pa_chunk_attend: not built yet");
+  if (dtype != PA_DTYPE_BF16) return fail(PA_ERR_UNSUPPORTED, "pa_chunk_attend: only bf16 is built");
+  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "pa_chunk_attend: head_dim %d not in {64, 128}", D);
+  if (B != 16 && B != 32) return fail(PA_ERR_UNSUPPORTED, "pa_chunk_attend: block size %d not in {16, 32}", B);
+  if (S < 0 || C < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv)
+    return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: S %d, C %d, Hq %d, Hkv %d", S, C, Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G > chunk::kRows) return fail(PA_ERR_UNSUPPORTED, "pa_chunk_attend: group of %d heads > %d", G, chunk::kRows);
+  if (S > 65535 || Hkv > 65535) return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: S and Hkv must be <= 65535");
+  if (num_blocks <= 0 || max_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: num_blocks %d, max_blocks %d", num_blocks, max_blocks);
+  if (static_cast<int64_t>(C) > static_cast<int64_t>(max_blocks) * B)
+    return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: chunk longer than a table row can hold");
+  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: scale is NaN");
+  if (S == 0 || C == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens)
+    return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: NULL pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: q, out and the pools must be 16-byte aligned");
+  chunk::Args a{};
+  a.out = static_cast<uint16_t*>(out);
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(k_cache);
+  a.vc = static_cast<const uint16_t*>(v_cache);
+  a.tables = block_tables;
+  a.ctx_lens = ctx_lens;
+  a.S = S;
+  a.C = C;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.TQ = chunk::kRows / G;
+  a.max_blocks = max_blocks;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * chunk::kLog2e;
+  const dim3 grid((C + a.TQ - 1) / a.TQ, Hkv, S);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (D == 64) {
+    if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<64, 16>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((chunk::chunk_kernel<64, 32>), grid, dim3(256), 0, st, a);
+  } else {
+    if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<128, 16>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((chunk::chunk_kernel<128, 32>), grid, dim3(256), 0, st, a);
+  }
+  return launch_status("pa_chunk_attend");
 }

@@ -29,7 +29,7 @@
 //     8 consecutive tokens of one dim are contiguous too.  No LDS round trip for K/V.
 //   * one query head per kv-head (g in {1, 2}) or fp32: a VALU kernel; LPT lanes share one
 //     token's dot product (reduced with cross-lane shuffles), the round max uses shuffles, and
-//     the PV update broadcasts each token's weight with v_readlane.
+//     the PV update broadcasts the round's weights through a per-wave LDS slot.
 //
 // Tiles beyond the context are never formed; lanes whose token lies past ctx_len load a
 // clamped in-range address and their score is set to -inf and their V elements to zero, so
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kNW * kWave) void decode_mfma_kernel(DecodeArgs a) 
   const int b0 = t0 / B;
   const int nb = (t1 + B - 1) / B - b0;
 
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = wave_id();
   const int r16 = lane & 15, gp = lane >> 4;
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
   const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
@@ -288,6 +288,12 @@ __global__ __launch_bounds__(kNW * kWave) void decode_mfma_kernel(DecodeArgs a) 
 
 // ---------------------------------------------------------------------------------------
 // VALU kernel: T in {float, bf16 bits}, G in {1, 2, 4, 8}; LPT lanes per token.
+//
+// A round covers TPR = 64 / LPT consecutive tokens (inside one block).  Lane (tk, pp) holds
+// a 1/LPT slice of token tk's key row; the dot products are finished with xor-shuffles over
+// the LPT lanes, the round max with xor-shuffles over the tokens.  For P.V each lane owns
+// D / 64 dims and reads their V^T rows (TPR contiguous tokens); the TPR weights of the round
+// are broadcast through a per-wave LDS slot.
 // ---------------------------------------------------------------------------------------
 template <typename T, int D, int B, int G, int LPT>
 __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) {
@@ -296,15 +302,16 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
   constexpr int CPL = D / LPT / VEC;    // 16-byte chunks of a key row per lane
   constexpr int DPL = CPL * VEC;        // dims per lane in QK
   constexpr int DV = D / kWave;         // dims per lane in PV
-  constexpr int VPR = TPR * sizeof(T) / 16 > 0 ? TPR * sizeof(T) / 16 : 1;  // 16B loads per V row
+  constexpr int VPR = TPR * sizeof(T) / 16;  // 16-byte loads per V^T row piece
   static_assert(CPL >= 1, "head_dim too small for LPT");
   static_assert(B % TPR == 0, "a round must stay inside one block");
-  static_assert(TPR * sizeof(T) >= 16, "V rows are read in 16-byte pieces");
+  static_assert(VPR >= 1 && TPR % 4 == 0, "V rows are read in 16-byte pieces");
 
   __shared__ int s_tbl[kMaxPT / B];
   __shared__ int s_bad;
   __shared__ float s_ml[kNW][G][2];
   __shared__ float s_o[kNW][G][D];
+  __shared__ __attribute__((aligned(16))) float s_p[kNW][G][TPR];  // weights of the round
 
   const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
   bool bad_len;
@@ -316,7 +323,7 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
   const int b0 = t0 / B;
   const int nb = (t1 + B - 1) / B - b0;
 
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = wave_id();
   const int tk = lane / LPT, pp = lane % LPT;
   const T* kc = static_cast<const T*>(a.kc);
   const T* vc = static_cast<const T*>(a.vc);
@@ -348,32 +355,29 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
     for (int e = 0; e < DV; ++e) acc[h][e] = 0.f;
   }
 
-  struct Round {
-    uint4 k[CPL];
-    uint4 v[DV][VPR];
-  };
   const size_t head_stride = static_cast<size_t>(B) * D;
   const int nrounds = n > 0 ? (t1 - t0 + TPR - 1) / TPR : 0;
 
-  auto load = [&](Round& rd, int r) {
+  for (int r = w; r < nrounds; r += kNW) {
     const int tt = t0 + TPR * r;
+    // ---- loads: this lane's key slice (clamped to a live token) and its V^T rows
     const int tok = min(tt + tk, t1 - 1);
-    const int p = s_tbl[tok / B - b0];
-    const T* kp = kc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride +
+    const T* kp = kc + (static_cast<size_t>(s_tbl[tok / B - b0]) * a.Hkv + kvh) * head_stride +
                   static_cast<size_t>(tok % B) * D;
+    uint4 kr[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) rd.k[i] = *reinterpret_cast<const uint4*>(kp + (pp + LPT * i) * VEC);
-    const int pr = s_tbl[tt / B - b0];  // the whole round lies in one block
-    const T* vp = vc + (static_cast<size_t>(pr) * a.Hkv + kvh) * head_stride + (tt % B);
+    for (int i = 0; i < CPL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + (pp + LPT * i) * VEC);
+    const T* vp = vc + (static_cast<size_t>(s_tbl[tt / B - b0]) * a.Hkv + kvh) * head_stride + (tt % B);
+    T vv[DV][TPR];
 #pragma unroll
     for (int e = 0; e < DV; ++e)
 #pragma unroll
-      for (int c = 0; c < VPR; ++c)
-        rd.v[e][c] = *reinterpret_cast<const uint4*>(vp + static_cast<size_t>(lane + kWave * e) * B + c * (16 / sizeof(T)));
-  };
+      for (int c = 0; c < VPR; ++c) {
+        const uint4 u = *reinterpret_cast<const uint4*>(vp + static_cast<size_t>(lane + kWave * e) * B + c * VEC);
+        __builtin_memcpy(&vv[e][c * VEC], &u, 16);
+      }
 
-  auto compute = [&](Round& rd, int r) {
-    const int tt = t0 + TPR * r;
+    // ---- scores of the round (log2 domain); tokens past the end get -inf
     const bool valid = tt + tk < t1;
     float x[G];
 #pragma unroll
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       T e[VEC];
-      __builtin_memcpy(e, &rd.k[i], 16);
+      __builtin_memcpy(e, &kr[i], 16);
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
         const float kv = Elem<T>::to_f32(e[j]);
@@ -395,52 +399,44 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
       for (int off = 1; off < LPT; off <<= 1) x[h] += shfl_xor(x[h], off);
       if (!valid) x[h] = -INFINITY;
     }
-    // V elements of tokens past the end are zeroed (they may hold anything).
-    T vv[DV][TPR];
+    // V elements of tokens past the end may hold anything (even NaN): zero them.
+    const int nv = t1 - tt;
+    if (nv < TPR) {
 #pragma unroll
-    for (int e = 0; e < DV; ++e) {
-      __builtin_memcpy(vv[e], rd.v[e], TPR * sizeof(T));
-      const int nv = t1 - tt;
-      if (nv < TPR) {
+      for (int e = 0; e < DV; ++e)
 #pragma unroll
         for (int j = 0; j < TPR; ++j)
           if (j >= nv) vv[e][j] = T(0);
-      }
     }
+
+    // ---- online softmax update and P.V
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mx = x[h];
 #pragma unroll
       for (int off = LPT; off < kWave; off <<= 1) mx = fmaxf(mx, shfl_xor(mx, off));
-      const float m_new = fmaxf(m_run[h], mx);
+      const float m_new = fmaxf(m_run[h], mx);  // finite: the round has a live token
       const float alpha = exp2f(m_run[h] - m_new);
       m_run[h] = m_new;
       const float p = exp2f(x[h] - m_new);
       l_run[h] = l_run[h] * alpha + (pp == 0 ? p : 0.f);
+      if (pp == 0) s_p[w][h][tk] = p;
 #pragma unroll
       for (int e = 0; e < DV; ++e) acc[h][e] *= alpha;
-#pragma unroll
-      for (int j = 0; j < TPR; ++j) {
-        const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j * LPT));
-#pragma unroll
-        for (int e = 0; e < DV; ++e) acc[h][e] = fmaf(pj, Elem<T>::to_f32(vv[e][j]), acc[h][e]);
-      }
     }
-  };
-
-  int r = w;
-  if (r < nrounds) {
-    Round ra, rb;
-    load(ra, r);
-    for (;;) {
-      if (r + kNW >= nrounds) { compute(ra, r); break; }
-      load(rb, r + kNW);
-      compute(ra, r);
-      r += kNW;
-      if (r + kNW >= nrounds) { compute(rb, r); break; }
-      load(ra, r + kNW);
-      compute(rb, r);
-      r += kNW;
+    // The wave reads back what it just wrote (LDS ops of one wave complete in order).
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int j4 = 0; j4 < TPR / 4; ++j4) {
+        const float4 p4 = *reinterpret_cast<const float4*>(&s_p[w][h][4 * j4]);
+        const float pj[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < DV; ++e)
+            acc[h][e] = fmaf(pj[q], Elem<T>::to_f32(vv[e][4 * j4 + q]), acc[h][e]);
+      }
     }
   }
 
@@ -505,18 +501,19 @@ static size_t workspace_bytes(int S, int Hq, int D, int Pmax) {
 
 typedef void (*KernelFn)(DecodeArgs);
 
+// Lanes per token: enough that the per-lane q slice stays small.
 template <int D, int B>
 static KernelFn pick_valu(int32_t dtype, int G) {
   if (dtype == PA_DTYPE_F32) {
     switch (G) {
-      case 1: return decode_valu_kernel<float, D, B, 1, 4>;
+      case 1: return decode_valu_kernel<float, D, B, 1, (D == 64 ? 4 : 8)>;
       case 2: return decode_valu_kernel<float, D, B, 2, (D == 64 ? 4 : 8)>;
       case 4: return decode_valu_kernel<float, D, B, 4, (D == 64 ? 8 : 16)>;
       case 8: return decode_valu_kernel<float, D, B, 8, 16>;
     }
   } else {
     switch (G) {
-      case 1: return decode_valu_kernel<uint16_t, D, B, 1, 4>;
+      case 1: return decode_valu_kernel<uint16_t, D, B, 1, (D == 64 ? 4 : 8)>;
       case 2: return decode_valu_kernel<uint16_t, D, B, 2, (D == 64 ? 4 : 8)>;
     }
   }

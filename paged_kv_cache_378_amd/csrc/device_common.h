@@ -40,6 +40,13 @@ template <> struct Elem<uint16_t> {  // bf16 carried as raw bits
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// Index of this wave in its workgroup, as a wave-uniform (scalar) value.  Without the
+// readfirstlane the compiler treats threadIdx.x / 64 as divergent, so every loop bounded by
+// it becomes exec-masked vector control flow instead of a scalar loop.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+}
+
 // Error check after a launch.
 inline pa_status launch_status(const char* what) {
   hipError_t e = hipGetLastError();

@@ -90,7 +90,7 @@ class PagedState:
             _lib.pa_copy_blocks(self.k_cache, self.v_cache, pairs_d)
         _lib.pa_cache_write(self.vals["k_step"], self.vals["v_step"], self.k_cache, self.v_cache,
                             slots_d)
-        if w.step_tokens == 1:
+        if not w.chunk:
             _lib.pa_decode(out, self.vals["q"], self.k_cache, self.v_cache, tables_d, lens_d,
                            max_ctx or self.max_ctx, w.scale, partition_tokens, workspace)
         else:
@@ -111,6 +111,6 @@ class PagedState:
         host = self.host_step()
         dev = self.upload(*host)
         out = self.new_out()
-        ws = self.workspace(partition_tokens) if self.w.step_tokens == 1 else None
+        ws = None if self.w.chunk else self.workspace(partition_tokens)
         self.device_step(*dev, out, ws, partition_tokens)
         return out, host

@@ -52,6 +52,7 @@ class Workload:
     rows: dict                  # value tensor name -> number of rows
     segments: dict              # seq id -> [(tensor name, first row, count), ...]
     meta: dict = field(default_factory=dict)
+    chunk: bool = False         # the step is a chunked query (q is [S, C, Hq, D])
 
     @property
     def num_seqs(self) -> int:
@@ -84,7 +85,7 @@ def value_tensor(w: Workload, name: str, device="cpu"):
     gen = torch.Generator(device=device)
     gen.manual_seed(w.seed * 1000 + _TENSOR_IDS[name])
     if name == "q":
-        shape = (w.num_seqs, w.step_tokens, w.hq, w.head_dim) if w.step_tokens > 1 else \
+        shape = (w.num_seqs, w.step_tokens, w.hq, w.head_dim) if w.chunk else \
                 (w.num_seqs, w.hq, w.head_dim)
     else:
         shape = (w.rows[name[2:]], w.hkv, w.head_dim)
@@ -287,7 +288,7 @@ def chunked(seed: int = 5, S: int = 8, cached: int = 4096, C: int = 512, B: int 
                     head_dim=D, block_size=B, num_blocks=num_blocks, scale=1 / math.sqrt(D),
                     seed=seed, free_order=rng.permutation(num_blocks).astype(np.int32),
                     script=script, step_ids=list(range(S)), step_tokens=C,
-                    rows={"prefill": S * cached, "step": S * C}, segments=segs)
+                    rows={"prefill": S * cached, "step": S * C}, segments=segs, chunk=True)
 
 
 def logical_kv(w: Workload, sid, tensors: dict):

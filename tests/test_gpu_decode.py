@@ -43,6 +43,12 @@ def small_cases():
         "shared_prefix_b32": wl.shared_prefix(B=32, n_seqs=12, prefix=96, n_families=4,
                                               suffix_range=(1, 70)),
         "long_b32": wl.long_context(S=2, n=5000),
+        # many rounds per wave in the VALU kernel (a broken register schedule once showed
+        # up only here, in the first 64 output dims)
+        "fp32_g1_d128_multiround": wl.custom_decode("fp32_g1_mr", 29, [1, 15, 16, 17, 300, 1500],
+                                                    8, 8, 128, 16, "f32"),
+        "bf16_g2_d128_multiround": wl.custom_decode("bf16_g2_mr", 30, [1, 15, 16, 17, 300, 1500],
+                                                    8, 4, 128, 16, "bf16"),
     }
 
 

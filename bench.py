@@ -58,6 +58,13 @@ def main() -> int:
     ap.add_argument("--cpu-seqs", type=int, default=256,
                     help="sequences of the batch the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--pool", choices=["churned", "contiguous"], default="churned",
+                    help="churned: blocks scattered by 10,000 alloc/free steps (the workload); "
+                         "contiguous: identity free order and no churn, so each sequence's blocks "
+                         "are physically consecutive (the contiguous-cache comparison)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before the timed steps, run one device-to-device copy of this many MiB "
+                         "(a plain copy of known size that calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -73,7 +80,11 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    w = wl.llama70b(seed=args.seed)
+    if args.pool == "churned":
+        w = wl.llama70b(seed=args.seed)
+    else:
+        w = wl.llama70b(seed=args.seed, churn_steps=0)
+        w.free_order = np.arange(w.num_blocks, dtype=np.int32)
     t_setup = time.perf_counter()
     st = PagedState(w, dev, poison=True)
     torch.cuda.synchronize()
@@ -83,54 +94,63 @@ def main() -> int:
     total = args.warmup + args.steps
     max_ctx = st.max_ctx + total
     max_blocks = (max_ctx + B - 1) // B
-    ws = st.workspace_for(max_ctx, args.partition) if hasattr(st, "workspace_for") else None
-    if ws is None:
-        nbytes = _lib.pa_decode_workspace_size(S, w.hq, w.head_dim, max_ctx, args.partition)
-        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    nbytes = _lib.pa_decode_workspace_size(S, w.hq, w.head_dim, max_ctx, args.partition)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     out = st.new_out()
     ids = np.asarray(w.step_ids, np.int64)
 
-    # double-buffered pinned staging: the host prepares step i+1 while step i's upload runs
-    pin = [dict(tables=torch.empty((S, max_blocks), dtype=torch.int32).pin_memory(),
-                lens=torch.empty(S, dtype=torch.int32).pin_memory(),
-                slots=torch.empty(S, dtype=torch.int32).pin_memory()) for _ in range(2)]
-    done = [None, None]
-    tables_d = torch.empty((S, max_blocks), dtype=torch.int32, device=dev)
-    lens_d = torch.empty(S, dtype=torch.int32, device=dev)
-    slots_d = torch.empty(S, dtype=torch.int32, device=dev)
+    # A ring of pinned staging buffers, each [slots | lens | tables] in one int32 array, so a
+    # step needs one host->device copy and the host waits only on an event recorded RING steps
+    # earlier (long complete), never on the step just enqueued.
+    RING = 4
+    n_meta = 2 * S + S * max_blocks
+    pin = [torch.empty(n_meta, dtype=torch.int32).pin_memory() for _ in range(RING)]
+    done = [torch.cuda.Event() for _ in range(RING)]
+    used = [False] * RING
+    meta_d = torch.empty(n_meta, dtype=torch.int32, device=dev)
+    slots_d, lens_d = meta_d[:S], meta_d[S:2 * S]
+    tables_d = meta_d[2 * S:].view(S, max_blocks)
     stream = torch.cuda.current_stream()
+    ev_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
 
     host_s = []
     dec_events = []
     step_lens = []
 
     def step(i, timed):
-        buf = pin[i % 2]
-        if done[i % 2] is not None:
-            done[i % 2].synchronize()
+        r = i % RING
+        if used[r]:
+            done[r].synchronize()
+        buf = pin[r].numpy()
         h0 = time.perf_counter()
         slots, pairs = st.bm.append_slots(ids, 1)
-        st.bm.block_tables(ids, max_blocks, buf["tables"].numpy(), buf["lens"].numpy())
-        buf["slots"].numpy()[:] = slots
+        st.bm.block_tables(ids, max_blocks, buf[2 * S:].reshape(S, max_blocks), buf[S:2 * S])
+        buf[:S] = slots
         host_s.append(time.perf_counter() - h0)
-        tables_d.copy_(buf["tables"], non_blocking=True)
-        lens_d.copy_(buf["lens"], non_blocking=True)
-        slots_d.copy_(buf["slots"], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        done[i % 2] = ev
+        meta_d.copy_(pin[r], non_blocking=True)
+        done[r].record(stream)
+        used[r] = True
         if len(pairs):
             _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).to(dev, non_blocking=False))
         _lib.pa_cache_write(st.vals["k_step"], st.vals["v_step"], st.k_cache, st.v_cache, slots_d)
         if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = ev_pool[len(dec_events)]
             e0.record(stream)
         _lib.pa_decode(out, st.vals["q"], st.k_cache, st.v_cache, tables_d, lens_d, max_ctx,
                        w.scale, args.partition, ws)
         if timed:
             e1.record(stream)
             dec_events.append((e0, e1))
-            step_lens.append(buf["lens"].numpy().copy())
+            step_lens.append(buf[S:2 * S].copy())
+
+    if args.calib_copy_mib > 0:
+        src_buf = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
 
     for i in range(args.warmup):
         step(i, False)
@@ -173,7 +193,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "llama3-70b-shaped decode layer, batch 256, 64/8 heads, D=128, "
-                               "B=16, log-normal ctx (median 1024, [16, 8192]), churned pool",
+                               "B=16, log-normal ctx (median 1024, [16, 8192]), %s pool" % args.pool,
                    "global_batch": S, "seq_len": "log-normal, mean %d" % (tokens // S),
                    "context_tokens": tokens, "partition_tokens": args.partition or "auto",
                    "parallelism": "none (1 GPU)"},

@@ -12,11 +12,17 @@
 // unaligned last block is handled).
 //
 // Work decomposition (chosen for CDNA4, not taken from the pages):
-//   * one workgroup per (sequence, kv-head, partition of PT tokens); NW = 4 waves split the
-//     partition's 32-token tiles round-robin and each keeps its own online-softmax state
+//   * a work item is one partition of PT tokens of one (sequence, kv-head); NW = 4 waves split
+//     the partition's 32-token tiles round-robin and each keeps its own online-softmax state
 //     (running max m, running sum l, unnormalised output o), scores in the log2 domain;
-//   * the partition's block-table slice is staged in LDS once, so tile loads never wait on a
-//     dependent table load;
+//   * a one-workgroup planning kernel turns the context lengths into a work list, longest
+//     first: every full partition, then the partial last partitions by decreasing length.
+//     The decode kernel is persistent (about as many workgroups as the chip holds at once)
+//     and pulls items from that list through an atomic cursor, prefetching the next index
+//     while it works on the current one.  No workgroup is launched for a partition that does
+//     not exist, and the short items fill the tail of the schedule;
+//   * the partition's block-table slice is staged in LDS once (loaded together with the
+//     context length), so tile loads never wait on a dependent table load;
 //   * the four wave states are merged through LDS; a single-partition sequence writes its
 //     final output directly, otherwise the partition writes (m, l, o/l) and a merge kernel
 //     combines the partitions (the FlashAttention-style tiling the KV-cache chapter mentions
@@ -36,6 +42,9 @@
 // values past the end (even NaN) cannot reach the output.
 
 #include <cmath>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "device_common.h"
 
@@ -44,6 +53,8 @@ namespace pa {
 constexpr int kNW = 4;            // waves per workgroup
 constexpr int kMaxPT = 8192;      // largest partition (tokens)
 constexpr int kMinAutoPT = 256;   // smallest partition the automatic choice uses
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxBuckets = kMaxPT / 32 + 1;  // partial partitions bucketed by 32-token tiles
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
@@ -55,6 +66,8 @@ struct DecodeArgs {
   const int32_t* ctx_lens;
   float* part_o;    // [S, Hq, Pmax, D]  partition outputs (normalised)
   float2* part_ml;  // [S, Hq, Pmax]     (max in log2 units, sum)
+  int2* items;      // work list: (sequence, part * Hkv + kv-head), longest first
+  int* queue;       // [0] number of items, [1] next unclaimed item
   int S, Hq, Hkv, G, max_blocks, num_blocks, PT, Pmax;
   int len_cap;      // min(max_blocks * B, max_ctx_len): longest context the call may see
   float scale_log2;
@@ -99,60 +112,109 @@ __device__ void finish_partition(const DecodeArgs& a, int s, int kvh, int part, 
   }
 }
 
-// Stage the partition's slice of the block table in LDS.  Entries outside the pool are
-// replaced by block 0 (so every load stays inside the pool) and flag the partition as bad.
-__device__ __forceinline__ void stage_table(const DecodeArgs& a, int s, int b0, int nb,
-                                            int* s_tbl, int* s_bad) {
+// Start of a work item: read the context length and stage the partition's slice of the
+// block table in LDS.  The table loads do not depend on the length (the slice is cut at
+// max_blocks), so both are in flight together.  Entries the partition uses that lie outside
+// the pool are replaced by block 0 (every load stays inside the pool) and flag the item as
+// bad; entries past the context end are ignored.
+struct ItemRange {
+  int n, nparts, t0, t1, b0;
+  bool bad;
+};
+
+template <int B>
+__device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, int s, int part, int* s_tbl,
+                                                int* s_bad) {
+  constexpr int kPer = (kMaxPT / B + kNW * kWave - 1) / (kNW * kWave);
+  const int raw_n = a.ctx_lens[s];
+  const int b0 = part * (a.PT / B);
+  const int nb_max = min(a.PT / B, a.max_blocks - b0);
+  const int32_t* row = a.tables + static_cast<size_t>(s) * a.max_blocks + b0;
+  int ent[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kNW * kWave;
+    ent[r] = i < nb_max ? row[i] : 0;
+  }
+  ItemRange it;
+  bool bad_len;
+  it.n = eff_len(raw_n, a.len_cap, bad_len);
+  it.nparts = it.n > 0 ? (it.n + a.PT - 1) / a.PT : 1;
+  it.t0 = part * a.PT;
+  it.t1 = min(it.n, it.t0 + a.PT);
+  it.b0 = b0;
+  const int nb = it.t1 > it.t0 ? (it.t1 + B - 1) / B - b0 : 0;
   if (threadIdx.x == 0) *s_bad = 0;
   __syncthreads();
-  const int32_t* row = a.tables + static_cast<size_t>(s) * a.max_blocks + b0;
-  for (int i = threadIdx.x; i < nb; i += kNW * kWave) {
-    int p = row[i];
-    if (p < 0 || p >= a.num_blocks) {
-      *s_bad = 1;
-      p = 0;
+  bool bad_ent = false;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = threadIdx.x + r * kNW * kWave;
+    if (i < nb) {
+      int p = ent[r];
+      if (p < 0 || p >= a.num_blocks) {
+        bad_ent = true;
+        p = 0;
+      }
+      s_tbl[i] = p;
     }
-    s_tbl[i] = p;
   }
+  if (bad_ent) *s_bad = 1;
   __syncthreads();
+  it.bad = bad_len || *s_bad;
+  return it;
+}
+
+// Persistent work loop: workgroup g starts with item g, then takes items from the shared
+// cursor (which the planning kernel set to the grid size).  The next index is claimed while
+// the current item runs, so the atomic's latency is hidden.  Every workgroup leaves once the
+// cursor passes the item count.
+template <typename Body>
+__device__ __forceinline__ void for_each_item(const DecodeArgs& a, int* s_next, Body&& body) {
+  const int count = a.queue[0];
+  int i = blockIdx.x;
+  while (i < count) {
+    int nxt = 0;
+    if (threadIdx.x == 0) nxt = atomicAdd(&a.queue[1], 1);
+    const int2 it = a.items[i];
+    body(it.x, it.y % a.Hkv, it.y / a.Hkv);
+    if (threadIdx.x == 0) *s_next = nxt;
+    __syncthreads();
+    i = __builtin_amdgcn_readfirstlane(*s_next);
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------------------
 // MFMA kernel: bf16, 1 <= G <= 16 query heads per kv-head, D in {64, 128}, B in {16, 32}.
+//
+// A wave walks its partition in tiles of 32 tokens (tiles w, w + NW, ...).  Per tile a lane
+// holds 2 x D/32 16-byte pieces of K and D/16 pieces of V^T in registers.  The loads are
+// staggered so that one tile's worth of registers is enough for a full tile in flight: the
+// next tile's K is issued as soon as QK^T has consumed the current K, and the next tile's V
+// as soon as PV has consumed the current V.  That keeps the register budget at three waves
+// per SIMD (12 waves, ~190 KB of K/V in flight per CU).
 // ---------------------------------------------------------------------------------------
-template <int D, int B>
-struct MfmaTile {
-  static constexpr int NST = D / 32;  // k-steps of QK^T (8 dims per lane per step)
-  static constexpr int NNT = D / 16;  // 16-dim output tiles of PV
-  bf16x8 k[2][NST];                   // two 16-token row groups
-  bf16x8 v[NNT];                      // V^T rows (dims) x 8 tokens
+constexpr int kMfmaWaves = 3;  // waves per SIMD the register budget is cut for
+
+template <int D>
+struct MfmaK {
+  bf16x8 k[2][D / 32];  // two 16-token row groups x D/32 k-steps
+};
+template <int D>
+struct MfmaV {
+  bf16x8 v[D / 16];     // V^T rows (16 dims per tile) x 8 tokens of this lane group
 };
 
 template <int D, int B>
-__global__ __launch_bounds__(kNW * kWave) void decode_mfma_kernel(DecodeArgs a) {
-  using Tile = MfmaTile<D, B>;
-  constexpr int NST = Tile::NST, NNT = Tile::NNT;
-  __shared__ int s_tbl[kMaxPT / B];
-  __shared__ int s_bad;
-  __shared__ float s_ml[kNW][16][2];
-  __shared__ float s_o[kNW][16][D];
-
-  const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-  bool bad_len;
-  const int n = eff_len(a.ctx_lens[s], a.len_cap, bad_len);
-  const int nparts = n > 0 ? (n + a.PT - 1) / a.PT : 1;
-  const int t0 = part * a.PT;
-  if (part >= nparts) return;
-  const int t1 = min(n, t0 + a.PT);
-  const int b0 = t0 / B;
-  const int nb = (t1 + B - 1) / B - b0;
-
+__device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, int part,
+                                          int* s_tbl, int* s_bad, float (*s_ml)[16][2],
+                                          float (*s_o)[16][D]) {
+  constexpr int NST = D / 32, NNT = D / 16;
   const int lane = threadIdx.x & (kWave - 1), w = wave_id();
   const int r16 = lane & 15, gp = lane >> 4;
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
   const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
-
-  stage_table(a, s, b0, nb > 0 ? nb : 0, s_tbl, &s_bad);
 
   // Q^T operand: column = head r16 (zero for padded heads), k = 8 dims per step.
   bf16x8 qop[NST];
@@ -168,49 +230,57 @@ __global__ __launch_bounds__(kNW * kWave) void decode_mfma_kernel(DecodeArgs a) 
     }
   }
 
+  const ItemRange rg = begin_item<B>(a, s, part, s_tbl, s_bad);
+  const int t0 = rg.t0, t1 = rg.t1, b0 = rg.b0;
+
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[NNT];
 #pragma unroll
   for (int i = 0; i < NNT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ntiles = n > 0 ? (t1 - t0 + 31) / 32 : 0;
+  const int ntiles = t1 > t0 ? (t1 - t0 + 31) / 32 : 0;
   const size_t head_stride = static_cast<size_t>(B) * D;  // elements per (block, kv-head)
 
-  // Issue the global loads of tile `tile` into `tl`.
-  auto load = [&](Tile& tl, int tile) {
+  // K rows: row r16 of row group m holds token 8*(r16/4) + 4*m + r16%4 of the tile, so that
+  // after QK^T lane group gp owns tokens 8*gp .. 8*gp+7 (the PV operand layout).
+  auto load_k = [&](MfmaK<D>& kt, int tile) {
     const int tt = t0 + 32 * tile;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      // row r16 of row group m holds token 8*(r16/4) + 4*m + r16%4 of the tile, so that after
-      // QK^T lane group gp owns tokens 8*gp .. 8*gp+7 (the PV operand layout).
-      int tok = tt + 8 * (r16 >> 2) + 4 * m + (r16 & 3);
-      tok = min(tok, t1 - 1);
+      const int tok = min(tt + 8 * (r16 >> 2) + 4 * m + (r16 & 3), t1 - 1);
       const int p = s_tbl[tok / B - b0];
       const uint16_t* kp = kc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride +
                            static_cast<size_t>(tok % B) * D;
 #pragma unroll
       for (int st = 0; st < NST; ++st)
-        tl.k[m][st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kp + 8 * (4 * st + gp)));
+        kt.k[m][st] = ld_kv16(kp + 8 * (4 * st + gp));
     }
-    int tv = tt + 8 * gp;
-    tv = min(tv, (t1 - 1) & ~7);
+  };
+  // V^T rows: lane (gp, r16) reads dim 16*ni + r16 at tokens 8*gp .. 8*gp+7 of the tile
+  // (16 contiguous bytes of the transposed block).
+  auto load_v = [&](MfmaV<D>& vt, int tile) {
+    const int tv = min(t0 + 32 * tile + 8 * gp, (t1 - 1) & ~7);
     const int p = s_tbl[tv / B - b0];
     const uint16_t* vp = vc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride + (tv % B);
 #pragma unroll
     for (int ni = 0; ni < NNT; ++ni)
-      tl.v[ni] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vp + (16 * ni + r16) * B));
+      vt.v[ni] = ld_kv16(vp + (16 * ni + r16) * B);
   };
 
-  auto compute = [&](Tile& tl, int tile) {
+  // One tile: QK^T on kt, refill kt with tile `pf`, softmax, PV on vt, refill vt with `pf`.
+  auto step = [&](MfmaK<D>& kt, MfmaV<D>& vt, int tile, int pf) {
     const int tt = t0 + 32 * tile;
+    const bool more = pf < ntiles;
     f32x4 sacc[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < NST; ++st)
-        sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl.k[m][st], qop[st], sacc[m], 0, 0, 0);
+        sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt.k[m][st], qop[st], sacc[m], 0, 0, 0);
     }
+    if (more) load_k(kt, pf);
+
     // lane (gp, r16): scores of head r16 for tokens tt + 8*gp + j, j = 4*m + i
     const int valid = t1 - (tt + 8 * gp);  // tokens of this lane's group that exist
     float x[8];
@@ -236,39 +306,33 @@ __global__ __launch_bounds__(kNW * kWave) void decode_mfma_kernel(DecodeArgs a) 
       psum += static_cast<float>(pb);
     }
     l_run = l_run * alpha + psum;
-    if (valid < 8) {  // tail: zero the V elements of tokens past the end
+    if (valid < 8) {  // tail: zero the V elements of tokens past the end (0 * NaN = NaN)
 #pragma unroll
       for (int ni = 0; ni < NNT; ++ni) {
         uint16_t vv[8];
-        __builtin_memcpy(vv, &tl.v[ni], 16);
+        __builtin_memcpy(vv, &vt.v[ni], 16);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (j >= valid) vv[j] = 0;
-        __builtin_memcpy(&tl.v[ni], vv, 16);
+        __builtin_memcpy(&vt.v[ni], vv, 16);
       }
     }
 #pragma unroll
     for (int ni = 0; ni < NNT; ++ni) {
       o[ni] *= alpha;
-      o[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl.v[ni], pop, o[ni], 0, 0, 0);
+      o[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt.v[ni], pop, o[ni], 0, 0, 0);
     }
+    if (more) load_v(vt, pf);
   };
 
-  // Two register sets: the next tile's loads are in flight while the current one computes.
-  int tile = w;
-  if (tile < ntiles) {
-    Tile ta, tb;
-    load(ta, tile);
-    for (;;) {
-      if (tile + kNW >= ntiles) { compute(ta, tile); break; }
-      load(tb, tile + kNW);
-      compute(ta, tile);
-      tile += kNW;
-      if (tile + kNW >= ntiles) { compute(tb, tile); break; }
-      load(ta, tile + kNW);
-      compute(tb, tile);
-      tile += kNW;
-    }
+  // The wave's tiles are w, w + NW, ...  (A second register set, two tiles in flight at two
+  // waves per SIMD, measured no faster than one set at three waves per SIMD.)
+  if (w < ntiles) {
+    MfmaK<D> kt;
+    MfmaV<D> vt;
+    load_k(kt, w);
+    load_v(vt, w);
+    for (int tile = w; tile < ntiles; tile += kNW) step(kt, vt, tile, tile + kNW);
   }
 
   // Wave state -> LDS.  l_run is per lane (its 8 tokens); sum the four lane groups.
@@ -283,7 +347,19 @@ __global__ __launch_bounds__(kNW * kWave) void decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_o[w][r16][16 * ni + 4 * gp + i] = o[ni][i];
   __syncthreads();
-  finish_partition<uint16_t, D, 16>(a, s, kvh, part, nparts, bad_len || s_bad, s_ml, s_o);
+  finish_partition<uint16_t, D, 16>(a, s, kvh, part, rg.nparts, rg.bad, s_ml, s_o);
+}
+
+template <int D, int B>
+__global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(kMfmaWaves, kMfmaWaves)))
+void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ int s_tbl[kMaxPT / B];
+  __shared__ int s_bad, s_next;
+  __shared__ float s_ml[kNW][16][2];
+  __shared__ float s_o[kNW][16][D];
+  for_each_item(a, &s_next, [&](int s, int kvh, int part) {
+    mfma_item<D, B>(a, s, kvh, part, s_tbl, &s_bad, s_ml, s_o);
+  });
 }
 
 // ---------------------------------------------------------------------------------------
@@ -295,40 +371,24 @@ __global__ __launch_bounds__(kNW * kWave) void decode_mfma_kernel(DecodeArgs a) 
 // D / 64 dims and reads their V^T rows (TPR contiguous tokens); the TPR weights of the round
 // are broadcast through a per-wave LDS slot.
 // ---------------------------------------------------------------------------------------
-template <typename T, int D, int B, int G, int LPT>
-__global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) {
+template <typename T, int D, int B, int G, int LPT, int TPR>
+__device__ __forceinline__ void valu_item(const DecodeArgs& a, int s, int kvh, int part,
+                                          int* s_tbl, int* s_bad, float (*s_ml)[G][2],
+                                          float (*s_o)[G][D], float (*s_p)[G][TPR]) {
   constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte load
-  constexpr int TPR = kWave / LPT;      // tokens per round
   constexpr int CPL = D / LPT / VEC;    // 16-byte chunks of a key row per lane
   constexpr int DPL = CPL * VEC;        // dims per lane in QK
   constexpr int DV = D / kWave;         // dims per lane in PV
   constexpr int VPR = TPR * sizeof(T) / 16;  // 16-byte loads per V^T row piece
+  static_assert(TPR == kWave / LPT, "tokens per round");
   static_assert(CPL >= 1, "head_dim too small for LPT");
   static_assert(B % TPR == 0, "a round must stay inside one block");
   static_assert(VPR >= 1 && TPR % 4 == 0, "V rows are read in 16-byte pieces");
-
-  __shared__ int s_tbl[kMaxPT / B];
-  __shared__ int s_bad;
-  __shared__ float s_ml[kNW][G][2];
-  __shared__ float s_o[kNW][G][D];
-  __shared__ __attribute__((aligned(16))) float s_p[kNW][G][TPR];  // weights of the round
-
-  const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-  bool bad_len;
-  const int n = eff_len(a.ctx_lens[s], a.len_cap, bad_len);
-  const int nparts = n > 0 ? (n + a.PT - 1) / a.PT : 1;
-  const int t0 = part * a.PT;
-  if (part >= nparts) return;
-  const int t1 = min(n, t0 + a.PT);
-  const int b0 = t0 / B;
-  const int nb = (t1 + B - 1) / B - b0;
 
   const int lane = threadIdx.x & (kWave - 1), w = wave_id();
   const int tk = lane / LPT, pp = lane % LPT;
   const T* kc = static_cast<const T*>(a.kc);
   const T* vc = static_cast<const T*>(a.vc);
-
-  stage_table(a, s, b0, nb > 0 ? nb : 0, s_tbl, &s_bad);
 
   // q slice of this lane, pre-scaled into the log2 domain.
   float qr[G][DPL];
@@ -346,6 +406,9 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
       }
   }
 
+  const ItemRange rg = begin_item<B>(a, s, part, s_tbl, s_bad);
+  const int t0 = rg.t0, t1 = rg.t1, b0 = rg.b0;
+
   float m_run[G], l_run[G], acc[G][DV];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -356,7 +419,7 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
   }
 
   const size_t head_stride = static_cast<size_t>(B) * D;
-  const int nrounds = n > 0 ? (t1 - t0 + TPR - 1) / TPR : 0;
+  const int nrounds = t1 > t0 ? (t1 - t0 + TPR - 1) / TPR : 0;
 
   for (int r = w; r < nrounds; r += kNW) {
     const int tt = t0 + TPR * r;
@@ -453,50 +516,178 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
     for (int e = 0; e < DV; ++e) s_o[w][h][lane + kWave * e] = acc[h][e];
   }
   __syncthreads();
-  finish_partition<T, D, G>(a, s, kvh, part, nparts, bad_len || s_bad, s_ml, s_o);
+  finish_partition<T, D, G>(a, s, kvh, part, rg.nparts, rg.bad, s_ml, s_o);
+}
+
+template <typename T, int D, int B, int G, int LPT>
+__global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) {
+  constexpr int TPR = kWave / LPT;      // tokens per round
+  __shared__ int s_tbl[kMaxPT / B];
+  __shared__ int s_bad, s_next;
+  __shared__ float s_ml[kNW][G][2];
+  __shared__ float s_o[kNW][G][D];
+  __shared__ __attribute__((aligned(16))) float s_p[kNW][G][TPR];  // weights of the round
+  for_each_item(a, &s_next, [&](int s, int kvh, int part) {
+    valu_item<T, D, B, G, LPT, TPR>(a, s, kvh, part, s_tbl, &s_bad, s_ml, s_o, s_p);
+  });
 }
 
 // ---------------------------------------------------------------------------------------
 // Partition merge: m = max_p m_p; out = sum_p o_p l_p 2^(m_p - m) / sum_p l_p 2^(m_p - m).
-// One workgroup per (head, sequence); sequences with one partition were finished already.
+// One workgroup per (kv-head, sequence) covers the G x D outputs of that head group, four
+// consecutive dims per thread (16-byte partial loads); sequences with one partition were
+// finished by the decode kernel already.
 // ---------------------------------------------------------------------------------------
-template <typename T, int D, int B>
-__global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
-  const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+constexpr int kMergeThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+  const int kvh = blockIdx.x, s = blockIdx.y;
   bool bad;
   const int n = eff_len(a.ctx_lens[s], a.len_cap, bad);
   const int nparts = n > 0 ? (n + a.PT - 1) / a.PT : 1;
   if (nparts <= 1) return;
-  const size_t row = (static_cast<size_t>(s) * a.Hq + hq) * a.Pmax;
-  const float2* ml = a.part_ml + row;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[p].x);
-  float L = 0.f, O = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float2 e = ml[p];
-    const float wgt = e.y * exp2f(e.x - M);
-    L += wgt;
-    O = fmaf(wgt, a.part_o[(row + p) * D + d], O);
+  constexpr int C4 = D / 4;  // float4 chunks per head
+  for (int c = threadIdx.x; c < a.G * C4; c += kMergeThreads) {
+    const int h = c / C4, d4 = c - h * C4;
+    const int hq = kvh * a.G + h;
+    const size_t row = (static_cast<size_t>(s) * a.Hq + hq) * a.Pmax;
+    const float2* ml = a.part_ml + row;
+    const float4* po = reinterpret_cast<const float4*>(a.part_o + row * D) + d4;
+    float M = -INFINITY;
+    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[p].x);
+    float L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int p = 0; p < nparts; ++p) {
+      const float2 e = ml[p];
+      const float wgt = e.y * exp2f(e.x - M);
+      const float4 v = po[static_cast<size_t>(p) * C4];
+      L += wgt;
+      O.x = fmaf(wgt, v.x, O.x);
+      O.y = fmaf(wgt, v.y, O.y);
+      O.z = fmaf(wgt, v.z, O.z);
+      O.w = fmaf(wgt, v.w, O.w);
+    }
+    const float inv = bad ? NAN : 1.f / L;
+    T* op = static_cast<T*>(a.out) + (static_cast<size_t>(s) * a.Hq + hq) * D + 4 * d4;
+    op[0] = Elem<T>::from_f32(O.x * inv);
+    op[1] = Elem<T>::from_f32(O.y * inv);
+    op[2] = Elem<T>::from_f32(O.z * inv);
+    op[3] = Elem<T>::from_f32(O.w * inv);
   }
-  const float r = bad ? NAN : O / L;
-  static_cast<T*>(a.out)[(static_cast<size_t>(s) * a.Hq + hq) * D + d] = Elem<T>::from_f32(r);
+}
+
+// ---------------------------------------------------------------------------------------
+// Planning: the work list, longest items first.  One workgroup reads every context length,
+// counts the full partitions and buckets the partial last partitions by their length in
+// 32-token tiles, then places full partitions first and the partial ones by decreasing
+// bucket (an empty or invalid context gets one item, which writes NaN).  It also sets the
+// persistent kernel's cursor to the grid size (workgroup g starts with item g).  Positions
+// inside a bucket are claimed with LDS atomics, so the order inside a bucket can change from
+// call to call; results do not depend on it (each item's output has a fixed place).
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int grid) {
+  __shared__ int s_base[kMaxBuckets];
+  __shared__ int s_full, s_fcur;
+  const int nbk = a.PT / 32;  // a partial partition has 0 .. PT-1 tokens: buckets 0 .. nbk
+  for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_base[b] = 0;
+  if (threadIdx.x == 0) {
+    s_full = 0;
+    s_fcur = 0;
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
+    bool bad;
+    const int n = eff_len(a.ctx_lens[s], a.len_cap, bad);
+    const int full = n / a.PT, rem = n - full * a.PT;
+    if (full) atomicAdd(&s_full, full);
+    if (rem > 0 || n == 0) atomicAdd(&s_base[(rem + 31) / 32], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int base = s_full * a.Hkv;
+    for (int b = nbk; b >= 0; --b) {
+      const int c = s_base[b];
+      s_base[b] = base;
+      base += c * a.Hkv;
+    }
+    a.queue[0] = base;
+    a.queue[1] = grid;
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
+    bool bad;
+    const int n = eff_len(a.ctx_lens[s], a.len_cap, bad);
+    const int full = n / a.PT, rem = n - full * a.PT;
+    if (full) {
+      const int f0 = atomicAdd(&s_fcur, full);
+      for (int p = 0; p < full; ++p)
+        for (int k = 0; k < a.Hkv; ++k) a.items[(f0 + p) * a.Hkv + k] = make_int2(s, p * a.Hkv + k);
+    }
+    if (rem > 0 || n == 0) {
+      const int pos = atomicAdd(&s_base[(rem + 31) / 32], a.Hkv);
+      for (int k = 0; k < a.Hkv; ++k) a.items[pos + k] = make_int2(s, full * a.Hkv + k);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------------------
-static int auto_partition(int S, int Hkv, int max_ctx_len) {
-  (void)S;
-  (void)Hkv;
-  (void)max_ctx_len;
-  return 512;
+// Partition length when the caller leaves it to the library: the longest of 2048 .. 256
+// tokens that still gives the persistent grid several items per workgroup (judged from the
+// longest context; shorter contexts only add items).  Longer partitions mean fewer partial
+// results to write and merge and fewer item start-ups; shorter ones balance small batches.
+static int auto_partition(int S, int Hkv, int max_ctx_len, int resident) {
+  for (int pt = 2048; pt > kMinAutoPT; pt /= 2) {
+    const int64_t items = static_cast<int64_t>(S) * Hkv * ((max_ctx_len + pt - 1) / pt);
+    if (items >= 4 * static_cast<int64_t>(resident)) return pt;
+  }
+  return kMinAutoPT;
 }
 
-static size_t workspace_bytes(int S, int Hq, int D, int Pmax) {
-  if (Pmax <= 1) return 0;
-  const size_t rows = static_cast<size_t>(S) * Hq * Pmax;
-  const size_t ml = (rows * sizeof(float2) + 255) & ~size_t(255);
-  return ml + rows * D * sizeof(float);
+// Workspace: [queue header | work list | partition (m, l) | partition outputs].  The work
+// list is sized for Hq heads (an upper bound of Hkv) so that the size query needs no Hkv.
+struct WsLayout {
+  size_t items, ml, o, total;
+};
+
+static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static WsLayout ws_layout(int S, int Hq, int D, int Pmax) {
+  WsLayout L{};
+  size_t off = 256;
+  L.items = off;
+  off += round256(static_cast<size_t>(S) * Pmax * Hq * sizeof(int2));
+  if (Pmax > 1) {
+    const size_t rows = static_cast<size_t>(S) * Hq * Pmax;
+    L.ml = off;
+    off += round256(rows * sizeof(float2));
+    L.o = off;
+    off += rows * D * sizeof(float);
+  }
+  L.total = off;
+  return L;
+}
+
+// Workgroups of kernel k that fit on the device at once (the persistent grid size).
+static int resident_grid(const void* k, int threads, size_t lds_dynamic) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(k, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, lds_dynamic) != hipSuccess)
+    return 0;
+  const int g = cus * (per_cu > 0 ? per_cu : 1);
+  cache[key] = g;
+  return g;
 }
 
 typedef void (*KernelFn)(DecodeArgs);
@@ -520,8 +711,11 @@ static KernelFn pick_valu(int32_t dtype, int G) {
   return nullptr;
 }
 
+// Picks the kernel, the partition length and the grid, lays out the workspace and launches
+// plan -> decode -> merge on `stream`.
 template <int D, int B>
-static pa_status launch(const DecodeArgs& a, int32_t dtype, hipStream_t stream) {
+static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void* workspace,
+                        size_t workspace_bytes_in, hipStream_t stream) {
   KernelFn k = nullptr;
   if (dtype == PA_DTYPE_BF16 && a.G >= 3 && a.G <= 16)
     k = decode_mfma_kernel<D, B>;
@@ -531,13 +725,32 @@ static pa_status launch(const DecodeArgs& a, int32_t dtype, hipStream_t stream) 
     return fail(PA_ERR_UNSUPPORTED,
                 "pa_decode: %d query heads per kv-head not supported for dtype %d "
                 "(bf16: 1..16, f32: 1, 2, 4, 8)", a.G, dtype);
-  hipLaunchKernelGGL(k, dim3(a.Pmax, a.Hkv, a.S), dim3(kNW * kWave), 0, stream, a);
+  const int cap = resident_grid(reinterpret_cast<const void*>(k), kNW * kWave, 0);
+  if (cap <= 0) return fail(PA_ERR_HIP, "pa_decode: cannot query the device's compute units");
+  a.PT = partition_tokens ? partition_tokens : auto_partition(a.S, a.Hkv, a.len_cap, cap);
+  a.Pmax = (a.len_cap + a.PT - 1) / a.PT;
+  if (static_cast<int64_t>(a.S) * a.Pmax * a.Hq >= (int64_t(1) << 31))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: S * partitions * Hq too large");
+  const WsLayout L = ws_layout(a.S, a.Hq, D, a.Pmax);  // fits: PT >= the size query's choice
+  char* ws = static_cast<char*>(workspace);
+  a.queue = reinterpret_cast<int*>(ws);
+  a.items = reinterpret_cast<int2*>(ws + L.items);
+  if (a.Pmax > 1) {
+    a.part_ml = reinterpret_cast<float2*>(ws + L.ml);
+    a.part_o = reinterpret_cast<float*>(ws + L.o);
+  }
+
+  const int64_t max_items = static_cast<int64_t>(a.S) * a.Pmax * a.Hkv;
+  const int grid = static_cast<int>(max_items < cap ? max_items : cap);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, grid);
+  if (pa_status st = launch_status("pa_decode (plan)")) return st;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kNW * kWave), 0, stream, a);
   if (pa_status st = launch_status("pa_decode")) return st;
   if (a.Pmax > 1) {
     if (dtype == PA_DTYPE_F32)
-      hipLaunchKernelGGL((merge_kernel<float, D, B>), dim3(a.Hq, a.S), dim3(D), 0, stream, a);
+      hipLaunchKernelGGL((merge_kernel<float, D>), dim3(a.Hkv, a.S), dim3(kMergeThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((merge_kernel<uint16_t, D, B>), dim3(a.Hq, a.S), dim3(D), 0, stream, a);
+      hipLaunchKernelGGL((merge_kernel<uint16_t, D>), dim3(a.Hkv, a.S), dim3(kMergeThreads), 0, stream, a);
     return launch_status("pa_decode (merge)");
   }
   return ok();
@@ -557,7 +770,9 @@ extern "C" pa_status pa_decode_workspace_size(int32_t S, int32_t Hq, int32_t D, 
     return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_size: partition_tokens %d", partition_tokens);
   const int pt = partition_tokens ? partition_tokens : kMinAutoPT;
   const int Pmax = max_ctx_len > 0 ? (max_ctx_len + pt - 1) / pt : 1;
-  *bytes = workspace_bytes(S, Hq, D, Pmax);
+  if (static_cast<int64_t>(S) * Pmax * Hq >= (int64_t(1) << 31))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_size: S * partitions * Hq too large");
+  *bytes = ws_layout(S, Hq, D, Pmax).total;
   return ok();
 }
 
@@ -600,22 +815,25 @@ extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, co
   a.G = Hq / Hkv;
   a.max_blocks = max_blocks;
   a.num_blocks = num_blocks;
-  a.PT = partition_tokens ? partition_tokens : auto_partition(S, Hkv, max_ctx_len);
-  a.Pmax = (max_ctx_len + a.PT - 1) / a.PT;
   a.len_cap = max_ctx_len;  // validated above: max_ctx_len <= max_blocks * B
   a.scale_log2 = scale * kLog2e;
-  const size_t need = workspace_bytes(S, Hq, D, a.Pmax);
-  if (need > 0) {
+  // The workspace must hold the layout for the shortest partition this call may pick (the
+  // size pa_decode_workspace_size reports), checked before anything touches the device.
+  {
+    const int pt_min = partition_tokens ? partition_tokens : kMinAutoPT;
+    const int pmax_min = (max_ctx_len + pt_min - 1) / pt_min;
+    if (static_cast<int64_t>(S) * pmax_min * Hq >= (int64_t(1) << 31))
+      return fail(PA_ERR_INVALID_ARG, "pa_decode: S * partitions * Hq too large");
+    const size_t need = ws_layout(S, Hq, D, pmax_min).total;
     if (!workspace || workspace_bytes_in < need)
       return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given", need,
                   workspace ? workspace_bytes_in : size_t(0));
     if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace must be 16-byte aligned");
-    const size_t rows = static_cast<size_t>(S) * Hq * a.Pmax;
-    const size_t ml = (rows * sizeof(float2) + 255) & ~size_t(255);
-    a.part_ml = static_cast<float2*>(workspace);
-    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (D == 64) return B == 16 ? launch<64, 16>(a, dtype, st) : launch<64, 32>(a, dtype, st);
-  return B == 16 ? launch<128, 16>(a, dtype, st) : launch<128, 32>(a, dtype, st);
+  const int pt = partition_tokens;
+  void* w = workspace;
+  const size_t wb = workspace_bytes_in;
+  if (D == 64) return B == 16 ? launch<64, 16>(a, dtype, pt, w, wb, st) : launch<64, 32>(a, dtype, pt, w, wb, st);
+  return B == 16 ? launch<128, 16>(a, dtype, pt, w, wb, st) : launch<128, 32>(a, dtype, pt, w, wb, st);
 }

@@ -83,8 +83,11 @@ def test_device_calls_reject_bad_arguments_before_launch(libpa):
 
 
 def test_workspace_size(libpa):
-    assert libpa.pa_decode_workspace_size(4, 4, 64, 100, 32) > 0       # 4 partitions
-    assert libpa.pa_decode_workspace_size(4, 4, 64, 100, 128) == 0      # one partition
+    one = libpa.pa_decode_workspace_size(4, 4, 64, 100, 128)            # one partition: work list
+    four = libpa.pa_decode_workspace_size(4, 4, 64, 100, 32)            # 4 partitions: + partials
+    assert 0 < one < four
+    # partials: 4 seqs x 4 heads x 4 partitions x (64 outputs + max + sum) fp32
+    assert four - one >= 4 * 4 * 4 * (64 + 2) * 4
     assert libpa.pa_decode_workspace_size(4, 4, 64, 1000, 0) > 0        # automatic choice
     with pytest.raises(libpa.PaError):
         libpa.pa_decode_workspace_size(4, 4, 64, 100, 40)

@@ -8,13 +8,16 @@ values (N(0,1) rounded to bf16).
 
 One step = the whole hot path for one batch:
   host  : pa_bm_append_slots (one token per sequence, copy-on-write decisions) and
-          pa_bm_block_tables into pinned staging buffers;
-  copy  : async host->device upload of slots, tables and lengths;
-  device: pa_copy_blocks (if any pairs) -> pa_cache_write -> pa_decode (split-K + merge).
+          pa_bm_seq_lens into a pinned staging buffer;
+  copy  : one async host->device upload of the step's slots and lengths (2 KB);
+  device: pa_copy_blocks (if any pairs) -> pa_cache_append (cache write + the block-table
+          entries the step created, on the device-resident tables) -> pa_decode (plan,
+          split-K decode, merge).
+The block tables are uploaded once before the timed steps and from then on live on the device.
 
 Prints one JSON line.  ``value`` is the step's algorithmic HBM traffic divided by the step
 time (GB/s); tokens/s is the batch size over the step time.  ``roofline`` reports the decode
-call alone (split-K kernel + merge), timed with HIP events on the stream it runs on.
+call alone (plan + split-K kernel + merge), timed with HIP events on the stream it runs on.
 """
 
 from __future__ import annotations
@@ -99,17 +102,18 @@ def main() -> int:
     out = st.new_out()
     ids = np.asarray(w.step_ids, np.int64)
 
-    # A ring of pinned staging buffers, each [slots | lens | tables] in one int32 array, so a
-    # step needs one host->device copy and the host waits only on an event recorded RING steps
+    # Block tables and lengths live on the device; each step uploads only [slots | lens] from a
+    # ring of pinned staging buffers, so the host waits only on an event recorded RING steps
     # earlier (long complete), never on the step just enqueued.
+    tables0, lens0 = st.bm.block_tables(ids, max_blocks)
+    tables_d = torch.from_numpy(tables0).to(dev)
     RING = 4
-    n_meta = 2 * S + S * max_blocks
-    pin = [torch.empty(n_meta, dtype=torch.int32).pin_memory() for _ in range(RING)]
+    pin = [torch.empty(2 * S, dtype=torch.int32).pin_memory() for _ in range(RING)]
     done = [torch.cuda.Event() for _ in range(RING)]
     used = [False] * RING
-    meta_d = torch.empty(n_meta, dtype=torch.int32, device=dev)
+    meta_d = torch.empty(2 * S, dtype=torch.int32, device=dev)
     slots_d, lens_d = meta_d[:S], meta_d[S:2 * S]
-    tables_d = meta_d[2 * S:].view(S, max_blocks)
+    lens_d.copy_(torch.from_numpy(lens0))
     stream = torch.cuda.current_stream()
     ev_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
@@ -125,15 +129,16 @@ def main() -> int:
         buf = pin[r].numpy()
         h0 = time.perf_counter()
         slots, pairs = st.bm.append_slots(ids, 1)
-        st.bm.block_tables(ids, max_blocks, buf[2 * S:].reshape(S, max_blocks), buf[S:2 * S])
         buf[:S] = slots
+        st.bm.seq_lens(ids, buf[S:])
         host_s.append(time.perf_counter() - h0)
         meta_d.copy_(pin[r], non_blocking=True)
         done[r].record(stream)
         used[r] = True
         if len(pairs):
             _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).to(dev, non_blocking=False))
-        _lib.pa_cache_write(st.vals["k_step"], st.vals["v_step"], st.k_cache, st.v_cache, slots_d)
+        _lib.pa_cache_append(st.vals["k_step"], st.vals["v_step"], st.k_cache, st.v_cache, slots_d,
+                             tables_d, lens_d)
         if timed:
             e0, e1 = ev_pool[len(dec_events)]
             e0.record(stream)
@@ -142,7 +147,7 @@ def main() -> int:
         if timed:
             e1.record(stream)
             dec_events.append((e0, e1))
-            step_lens.append(buf[S:2 * S].copy())
+            step_lens.append(buf[S:].copy())
 
     if args.calib_copy_mib > 0:
         src_buf = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -163,6 +168,10 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     if not torch.isfinite(out.float()).all():
         print(json.dumps({"error": "non-finite decode output"}), flush=True)
+        return 1
+    # the device-resident tables must still mirror the block manager's exactly
+    if not np.array_equal(tables_d.cpu().numpy(), st.bm.block_tables(ids, max_blocks)[0]):
+        print(json.dumps({"error": "device block tables diverged from the block manager"}), flush=True)
         return 1
 
     ms_step = 1e3 * elapsed / args.steps

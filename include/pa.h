@@ -152,6 +152,11 @@ pa_status pa_bm_block_tables(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32
 /* Token count of one sequence. */
 pa_status pa_bm_seq_len(pa_bm* bm, int64_t seq_id, int32_t* n_out);
 
+/* Token counts of n sequences (host array lens_out[n]); the context lengths of a step without
+ * rebuilding the block tables.  PA_ERR_UNKNOWN_SEQ names the first unknown id (lens_out may be
+ * partly written then). */
+pa_status pa_bm_seq_lens(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* lens_out);
+
 /* Reference count of one physical block. */
 pa_status pa_bm_refcount(pa_bm* bm, int32_t block, int32_t* out);
 
@@ -197,6 +202,27 @@ pa_status pa_validate_tables(const int32_t* tables, const int32_t* ctx_lens, int
 pa_status pa_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
                          const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
                          int32_t B, int32_t num_blocks, int32_t dtype, void* stream);
+
+/* The device half of one serving step in one launch: the cache write above plus the block-table
+ * entries the step created, so that block tables and context lengths can stay resident on the
+ * device from step to step and only the step's slots and new lengths cross the bus ([TT] "How
+ * the Architecture Works": a sequence's table gains an entry when its last block is full; [KC]
+ * "PagedAttention: borrowing virtual memory": a copy-on-write replaces the shared last block).
+ * The batch is S sequences, each appending tokens_each tokens (1 = decode, C = a chunk), in the
+ * order pa_bm_append_slots returns their slots.  For t in [0, S * tokens_each): row
+ * r = t / tokens_each sits at position pos = ctx_lens[r] - tokens_each + t % tokens_each
+ * (ctx_lens holds the lengths AFTER the step); its key/value go to slot_mapping[t] exactly as in
+ * pa_cache_write, and block_tables[r][pos / B] = slot_mapping[t] / B.  This is the one entry
+ * of the row a step can change: a new block at a block boundary, or the private copy that
+ * replaced a shared last block.  Tokens with a slot outside [0, num_blocks * B) or a position
+ * outside [0, max_blocks * B) are skipped (not written anywhere).
+ * key, value: device [S * tokens_each, Hkv, D]; slot_mapping: device int32 [S * tokens_each];
+ * block_tables: device int32 [S, max_blocks], updated in place; ctx_lens: device int32 [S]. */
+pa_status pa_cache_append(const void* key, const void* value, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int32_t S, int32_t tokens_each,
+                          int32_t* block_tables, int32_t max_blocks, const int32_t* ctx_lens,
+                          int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks, int32_t dtype,
+                          void* stream);
 
 /* Copy-on-write block copies ([KC] "PagedAttention: borrowing virtual memory"): for each of
  * the P pairs (src, dst) in device int32 [P, 2], physical block dst of both pools becomes a

@@ -89,12 +89,15 @@ _SIGS = {
     "pa_bm_free_seq": ([_vp, _i64], _i32),
     "pa_bm_block_tables": ([_vp, _pi64, _i32, _i32, _pi32, _pi32], _i32),
     "pa_bm_seq_len": ([_vp, _i64, _pi32], _i32),
+    "pa_bm_seq_lens": ([_vp, _pi64, _i32, _pi32], _i32),
     "pa_bm_refcount": ([_vp, _i32, _pi32], _i32),
     "pa_bm_free_list": ([_vp, _pi32, _i32, _pi32], _i32),
     "pa_bm_stats": ([_vp, C.POINTER(pa_bm_stats_t)], _i32),
     "pa_accounting": ([_pi32, _i32, _i32, _i32, C.POINTER(pa_accounting_t)], _i32),
     "pa_validate_tables": ([_pi32, _pi32, _i32, _i32, _i32, _i32], _i32),
     "pa_cache_write": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
+    "pa_cache_append": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                         _i32, _vp], _i32),
     "pa_copy_blocks": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -184,6 +187,14 @@ def pa_bm_seq_len(h, seq_id: int) -> int:
     return n.value
 
 
+def pa_bm_seq_lens(h, seq_ids, lens_out=None) -> np.ndarray:
+    ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+    lens = np.empty(len(ids), np.int32) if lens_out is None else lens_out
+    assert lens.dtype == np.int32 and lens.flags.c_contiguous and lens.shape == (len(ids),)
+    _check(_lib.pa_bm_seq_lens(h, ids.ctypes.data_as(_pi64), len(ids), _ptr32(lens)))
+    return lens
+
+
 def pa_bm_refcount(h, block: int) -> int:
     n = _i32()
     _check(_lib.pa_bm_refcount(h, block, C.byref(n)))
@@ -228,7 +239,7 @@ class BlockManager:
 
     def __del__(self):
         h = getattr(self, "h", None)
-        if h is not None and h.value:
+        if h is not None and h.value and _lib is not None:
             _lib.pa_bm_destroy(h)
             self.h = None
 
@@ -249,6 +260,9 @@ class BlockManager:
 
     def seq_len(self, seq_id):
         return pa_bm_seq_len(self.h, seq_id)
+
+    def seq_lens(self, seq_ids, lens_out=None):
+        return pa_bm_seq_lens(self.h, seq_ids, lens_out)
 
     def refcount(self, block):
         return pa_bm_refcount(self.h, block)
@@ -314,6 +328,28 @@ def pa_cache_write(key, value, k_cache, v_cache, slot_mapping, stream=None) -> N
     _check(_lib.pa_cache_write(_dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
                                _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32),
                                T, Hkv, D, B, NB, _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_cache_append(key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
+                    tokens_each: int = 1, stream=None) -> None:
+    torch = _torch()
+    NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
+    if block_tables.dim() != 2 or ctx_lens.dim() != 1 or ctx_lens.shape[0] != block_tables.shape[0]:
+        raise PaError(PA_ERR_INVALID_ARG, "block_tables must be [S, max_blocks], ctx_lens [S]")
+    S, max_blocks = block_tables.shape
+    T = S * tokens_each
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
+        raise PaError(PA_ERR_INVALID_ARG, "key and value must be [S * tokens_each, Hkv, D]")
+    if key.dtype != k_cache.dtype or value.dtype != k_cache.dtype:
+        raise PaError(PA_ERR_INVALID_ARG, "key/value dtype must match the pools")
+    if tuple(slot_mapping.shape) != (T,):
+        raise PaError(PA_ERR_INVALID_ARG, "slot_mapping must be [S * tokens_each]")
+    _check(_lib.pa_cache_append(_dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
+                                _dev(v_cache, "v_cache"),
+                                _dev(slot_mapping, "slot_mapping", torch.int32), S, tokens_each,
+                                _dev(block_tables, "block_tables", torch.int32), max_blocks,
+                                _dev(ctx_lens, "ctx_lens", torch.int32), Hkv, D, B, NB,
+                                _dtype_code(k_cache), _stream(stream)))
 
 
 def pa_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:

@@ -301,6 +301,19 @@ pa_status pa_bm_seq_len(pa_bm* bm, int64_t seq_id, int32_t* n_out) {
   return ok();
 }
 
+pa_status pa_bm_seq_lens(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* lens_out) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_seq_lens: NULL handle");
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_seq_lens: negative count");
+  if (n > 0 && (!seq_ids || !lens_out)) return fail(PA_ERR_INVALID_ARG, "pa_bm_seq_lens: NULL array");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_seq_lens: unknown sequence %lld", (long long)seq_ids[i]);
+    lens_out[i] = it->second.n;
+  }
+  return ok();
+}
+
 pa_status pa_bm_refcount(pa_bm* bm, int32_t block, int32_t* out) {
   if (!bm || !out) return fail(PA_ERR_INVALID_ARG, "pa_bm_refcount: NULL argument");
   if (block < 0 || block >= bm->num_blocks)

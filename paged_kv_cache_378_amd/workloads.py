@@ -306,8 +306,9 @@ def logical_kv(w: Workload, sid, tensors: dict):
 
 
 def custom_decode(name: str, seed: int, lens, hq: int, hkv: int, D: int, B: int, dtype: str,
-                  churn_steps: int = 0) -> Workload:
-    """Independent sequences of the given lengths (a decode step over a shuffled pool)."""
+                  churn_steps: int = 0, extra_blocks: int = 0) -> Workload:
+    """Independent sequences of the given lengths (a decode step over a shuffled pool);
+    ``extra_blocks`` enlarges the pool for appends beyond the workload's own step."""
     rng = np.random.default_rng(seed)
     law = None
     if churn_steps:
@@ -316,4 +317,4 @@ def custom_decode(name: str, seed: int, lens, hq: int, hkv: int, D: int, B: int,
         def law(r):
             return int(r.integers(lo, hi + 1))
     return _decode_workload(name, seed, lens, hq, hkv, D, B, dtype, churn_steps=churn_steps,
-                            churn_law=law, rng=rng)
+                            churn_law=law, rng=rng, extra_blocks=extra_blocks)

@@ -24,6 +24,7 @@ def same_state(lib_bm, model: BlockManagerModel, ids):
         t, l = lib_bm.block_tables(ids, maxb)
         mt, ml = model.block_tables(ids, maxb)
         assert np.array_equal(t, np.array(mt, np.int32)) and list(l) == ml
+        assert list(lib_bm.seq_lens(ids)) == ml
     st = lib_bm.stats()
     ms = model.stats()
     for k in ("free_blocks", "used_blocks", "shared_blocks", "num_seqs", "logical_blocks",
@@ -209,3 +210,12 @@ def test_host_block_manager_step_is_cheap(libpa):
         bm.block_tables(w.step_ids, 600, tables, lens)
     per_step = (time.perf_counter() - t0) / 20
     assert per_step < 5e-3, per_step
+
+
+def test_seq_lens_errors(libpa):
+    bm = libpa.BlockManager(8, 16)
+    bm.add_seq(5, 20)
+    assert list(bm.seq_lens([5])) == [20]
+    assert list(bm.seq_lens([])) == []
+    with pytest.raises(libpa.UnknownSeq):
+        bm.seq_lens([5, 6])

@@ -588,37 +588,45 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
 // call to call; results do not depend on it (each item's output has a fixed place).
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int grid) {
-  __shared__ int s_base[kMaxBuckets];
+  __shared__ int s_cnt[kMaxBuckets];   // partial partitions per bucket
+  __shared__ int s_base[kMaxBuckets];  // first item of each bucket (then a cursor)
   __shared__ int s_full, s_fcur;
   const int nbk = a.PT / 32;  // a partial partition has 0 .. PT-1 tokens: buckets 0 .. nbk
-  for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_base[b] = 0;
+  for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
   if (threadIdx.x == 0) {
     s_full = 0;
     s_fcur = 0;
   }
   __syncthreads();
+  // The common case (S <= kPlanThreads) keeps each thread's length in a register for the
+  // second pass; larger batches read the lengths again.
+  int n_own = 0;
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
     bool bad;
     const int n = eff_len(a.ctx_lens[s], a.len_cap, bad);
+    if (s == threadIdx.x) n_own = n;
     const int full = n / a.PT, rem = n - full * a.PT;
     if (full) atomicAdd(&s_full, full);
-    if (rem > 0 || n == 0) atomicAdd(&s_base[(rem + 31) / 32], 1);
+    if (rem > 0 || n == 0) atomicAdd(&s_cnt[(rem + 31) / 32], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int base = s_full * a.Hkv;
-    for (int b = nbk; b >= 0; --b) {
-      const int c = s_base[b];
-      s_base[b] = base;
-      base += c * a.Hkv;
+  // Buckets in decreasing order after the full partitions: base[b] = full + sum_{b' > b} cnt[b'].
+  for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) {
+    int above = 0;
+    for (int c = b + 1; c <= nbk; ++c) above += s_cnt[c];
+    s_base[b] = (s_full + above) * a.Hkv;
+    if (b == 0) {
+      a.queue[0] = (s_full + above + s_cnt[0]) * a.Hkv;
+      a.queue[1] = grid;
     }
-    a.queue[0] = base;
-    a.queue[1] = grid;
   }
   __syncthreads();
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
-    bool bad;
-    const int n = eff_len(a.ctx_lens[s], a.len_cap, bad);
+    int n = n_own;
+    if (s != threadIdx.x) {
+      bool bad;
+      n = eff_len(a.ctx_lens[s], a.len_cap, bad);
+    }
     const int full = n / a.PT, rem = n - full * a.PT;
     if (full) {
       const int f0 = atomicAdd(&s_fcur, full);

@@ -27,7 +27,7 @@
  *     affected outputs are set to NaN, never dereferenced.
  *   - A handle (pa_bm) is not thread-safe: one scheduler thread per handle.
  *
- * Pool layout (the pages fix only the address rule "physical block * block size + offset",
+ * Pool layout (the pages fix only the address rule: physical block times block size plus offset,
  * [TT] "Under the Hood: The CUDA Kernel Engineering"; the rest is this library's choice):
  *   k_cache: [num_blocks, Hkv, B, D]  -- key of token at offset o of block p, kv-head h is
  *                                        the contiguous row k_cache[p][h][o][0..D)
@@ -193,8 +193,8 @@ pa_status pa_validate_tables(const int32_t* tables, const int32_t* ctx_lens, int
  * must be 16-byte aligned.
  * ====================================================================================== */
 
-/* Cache write (the "store only the new token's K/V" step: [TT] "The Hidden Tax"; [VP]
- * "writing only new token deltas").  For t in [0, T): if slot_mapping[t] is in
+/* Cache write (each step stores only the new token's K/V: [TT] "The Hidden Tax"; [VP]
+ * "1. Underlying Mechanism").  For t in [0, T): if slot_mapping[t] is in
  * [0, num_blocks * B) the key key[t] ([Hkv, D]) goes to k_cache[slot / B][h][slot % B][:] and
  * value[t] to v_cache[slot / B][h][:][slot % B]; other slots (negative: padding) are skipped.
  * Bit copy, no arithmetic.  Slots within one call must be distinct.

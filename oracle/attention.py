@@ -3,11 +3,10 @@
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 The pages state that paging changes where K and V live, not what attention
-computes: "mathematically identical to standard multi-head attention"
-(vLLM PagedAttention (tinycto), FAQ), "100% exact and lossless" (same page,
-"Common Misconceptions"), and the same scores, softmax and number of
-floating-point operations as contiguous attention (KV-cache chapter, "Common
-misconception").  The oracle is therefore: rebuild each sequence's contiguous
+computes: the result equals standard multi-head attention exactly (vLLM
+PagedAttention (tinycto), FAQ and "Common Misconceptions"), with the same
+scores, softmax and floating-point operation count as contiguous attention
+(KV-cache chapter, "Common misconception").  The oracle is therefore: rebuild each sequence's contiguous
 K/V from its block table (``cache.gather_sequence``), then run textbook
 attention on it.
 

@@ -28,8 +28,8 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, key: np.ndarray,
 
     Writes only what the slot names; every other byte of the pools is left
     unchanged.  Taming the Tail, "The Hidden Tax": each step stores only the
-    new token's K/V; tinycto "1. Underlying Mechanism": only new token deltas
-    are written.
+    new token's K/V; tinycto "1. Underlying Mechanism": a step writes the new
+    token's entries and nothing else.
     """
     B = block_size
     for t, slot in enumerate(slots):

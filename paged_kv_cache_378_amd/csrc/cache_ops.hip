@@ -1,8 +1,8 @@
 // Cache write (slot scatter) and copy-on-write block copy on gfx950.
 //
 // Cache write: "Taming the Tail", "The Hidden Tax" -- each step stores only the new token's
-// K/V; "vLLM PagedAttention" (tinycto), "1. Underlying Mechanism" -- only new token deltas are
-// written.  Block copy: KV-cache chapter, "PagedAttention: borrowing virtual memory" -- a
+// K/V; "vLLM PagedAttention" (tinycto), "1. Underlying Mechanism" -- a step writes the new
+// token's entries and nothing else.  Block copy: KV-cache chapter, "PagedAttention: borrowing virtual memory" -- a
 // writer into a shared block first gets a private copy.
 //
 // Both are pure bit copies and HBM-bound.  One thread moves one 16-byte chunk of a token's

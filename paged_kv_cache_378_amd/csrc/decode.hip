@@ -1,7 +1,7 @@
 // Paged decode attention on gfx950: split-K over context partitions, then a merge.
 //
-// What is computed ("vLLM PagedAttention" (tinycto), FAQ: mathematically identical to
-// standard multi-head attention; KV-cache chapter, "Common misconception": the same scores and
+// What is computed ("vLLM PagedAttention" (tinycto), FAQ: paging leaves the result of standard
+// multi-head attention unchanged; KV-cache chapter, "Common misconception": the same scores and
 // softmax, the memory is only gathered through the block table):
 //
 //   out[s, h] = sum_j softmax_j(scale * q[s, h] . K_s[j, h / g]) V_s[j, h / g]

@@ -103,8 +103,8 @@ def test_pool_bytes_and_tables_match_oracle_bitwise(gpu, name):
 @pytest.mark.parametrize("name", ["tiny_fp32", "bf16_g8_llama_churn", "bf16_g1_d128",
                                   "shared_prefix_b32"])
 def test_physical_layout_does_not_change_a_bit(gpu, name):
-    """Paging is 'mathematically identical' to contiguous attention: two different free
-    orders (hence different physical blocks) must give bit-identical outputs."""
+    """Paging does not change the attention result (tinycto FAQ): two different free orders
+    (hence different physical blocks) must give bit-identical outputs."""
     w = CASES[name]
     _, out_a, _ = run(w, 0)
     rng = np.random.default_rng(99)

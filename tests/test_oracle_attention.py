@@ -132,8 +132,8 @@ def test_paged_equals_dense_and_ignores_poison():
 
 
 def test_layout_permutation_invariance_bitwise():
-    # Paging is "mathematically identical" to contiguous attention (tinycto
-    # FAQ): relabelling the physical blocks changes nothing, bit for bit.
+    # Paging leaves the attention result unchanged (tinycto FAQ): relabelling
+    # the physical blocks changes nothing, bit for bit.
     rng = np.random.default_rng(12)
     S, Hq, Hkv, D, B, NB = 3, 4, 2, 8, 4, 80
     k, v, tables, ctx, _ = _paged_setup(rng, S, Hq, Hkv, D, B, NB, [5, 37, 64])

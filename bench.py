@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_llama70b_b256.md")
 
 
@@ -76,21 +77,72 @@ def algorithmic_bytes(lens, w, T, with_write=True):
     return kv + qo + meta, write
 
 
+WORKLOADS = {
+    "llama70b": "llama3-70b-shaped decode layer, batch 256, 64/8 heads, D=128, B=16, log-normal "
+                "ctx (median 1024, [16, 8192])",
+    "mistral7b": "mistral-7b-shaped decode layer, batch 64, 32/8 heads, D=128, B=16, "
+                 "ctx U[128, 4096]",
+    "long32k": "long-context decode, batch 32 x 32768 tokens, 64/8 heads, D=128, B=32",
+    "shared16": "shared 1024-token prefix + copy-on-write forks, 224 sequences, 32/8 heads, "
+                "D=128, B=16",
+    "shared32": "shared 1024-token prefix + copy-on-write forks, 224 sequences, 32/8 heads, "
+                "D=128, B=32",
+    "chunk": "chunked-query prefill, 8 sequences x 512 new tokens over 4096 cached, 64/8 heads, "
+             "D=128, B=32, causal inside the chunk",
+}
+
+
+def make_workload(wl, name, pool):
+    if name == "llama70b":
+        if pool == "churned":
+            return wl.llama70b()
+        w = wl.llama70b(churn_steps=0)
+    elif name == "mistral7b":
+        w = wl.mistral()
+    elif name == "long32k":
+        w = wl.long_context()
+    elif name == "shared16":
+        w = wl.shared_prefix(B=16)
+    elif name == "shared32":
+        w = wl.shared_prefix(B=32)
+    else:
+        w = wl.chunked()
+    if pool == "contiguous":
+        w.free_order = np.arange(w.num_blocks, dtype=np.int32)
+    return w
+
+
+def unique_kv_bytes(tables, lens, w):
+    """K/V bytes of the distinct physical blocks a batch reads (each block counted once, with
+    the largest number of its slots any sequence uses)."""
+    B = w.block_size
+    used = {}
+    for row, n in zip(tables, lens):
+        for j in range((int(n) + B - 1) // B):
+            p = int(row[j])
+            used[p] = max(used.get(p, 0), min(B, int(n) - j * B))
+    elt = 2 if w.dtype == "bf16" else 4
+    return sum(used.values()) * w.hkv * w.head_dim * 2 * elt
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llama70b",
+                    help="llama70b (default, the headline batch); the others are the remaining "
+                         "configurations of the path, measured the same way")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = auto)")
     ap.add_argument("--cpu-seqs", type=int, default=256,
                     help="sequences of the batch the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum oracle time for the CPU baseline (the sample is repeated)")
-    ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--pool", choices=["churned", "contiguous"], default="churned",
-                    help="churned: blocks scattered by 10,000 alloc/free steps (the workload); "
-                         "contiguous: identity free order and no churn, so each sequence's blocks "
-                         "are physically consecutive (the contiguous-cache comparison)")
+                    help="churned: the workload's scattered pool (the llama70b pool is also "
+                         "fragmented by 10,000 alloc/free steps); contiguous: identity free order "
+                         "and no churn, so each sequence's blocks are physically consecutive (the "
+                         "contiguous-cache comparison)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the timed steps, run one device-to-device copy of this many MiB "
                          "(a plain copy of known size that calibrates the HBM byte counters)")
@@ -103,22 +155,65 @@ def main() -> int:
 
     import torch
 
-    from paged_kv_cache_378_amd import _lib
     from paged_kv_cache_378_amd import workloads as wl
     from paged_kv_cache_378_amd.runner import PagedState
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    if args.pool == "churned":
-        w = wl.llama70b(seed=args.seed)
-    else:
-        w = wl.llama70b(seed=args.seed, churn_steps=0)
-        w.free_order = np.arange(w.num_blocks, dtype=np.int32)
+    w = make_workload(wl, args.workload, args.pool)
     t_setup = time.perf_counter()
     st = PagedState(w, dev, poison=True)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
+    if args.calib_copy_mib > 0:
+        src_buf = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
+    run = run_chunk if w.chunk else run_decode
+    line = run(args, w, st, t_setup)
+    print(json.dumps(line), flush=True)
+    return 0 if "error" not in line else 1
 
+
+def timed_loop(args, step):
+    """Warm-up, then exactly args.steps timed steps between two device synchronisations, with
+    the set-up's Python objects frozen and the cyclic GC off (a collection over the workload
+    script once stalled one step for tens of milliseconds)."""
+    import torch
+    gc.collect()
+    gc.freeze()
+    gc.disable()
+    try:
+        for i in range(args.warmup):
+            step(i, False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warmup, args.warmup + args.steps):
+            step(i, True)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+    finally:
+        gc.enable()
+
+
+def base_line(args, w, ms_step):
+    return {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+            "data": "synthetic"}
+
+
+def run_decode(args, w, st, t_setup):
+    """One decode step of the whole path per iteration (host block manager, 2 KiB upload,
+    copy-on-write copies, cache write + table patch, plan + split-K decode + merge)."""
+    import torch
+
+    from paged_kv_cache_378_amd import _lib
+
+    dev = st.device
     S, B = w.num_seqs, w.block_size
     total = args.warmup + args.steps
     max_ctx = st.max_ctx + total
@@ -143,10 +238,7 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     ev_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
-
-    host_s = []
-    dec_events = []
-    step_lens = []
+    host_s, dec_events, step_lens, n_pairs = [], [], [], []
 
     def step(i, timed):
         r = i % RING
@@ -157,12 +249,14 @@ def main() -> int:
         slots, pairs = st.bm.append_slots(ids, 1)
         buf[:S] = slots
         st.bm.seq_lens(ids, buf[S:])
-        host_s.append(time.perf_counter() - h0)
+        n_pairs.append(len(pairs))
+        if timed:
+            host_s.append(time.perf_counter() - h0)
         meta_d.copy_(pin[r], non_blocking=True)
         done[r].record(stream)
         used[r] = True
         if len(pairs):
-            _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).to(dev, non_blocking=False))
+            _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).to(dev))
         _lib.pa_cache_append(st.vals["k_step"], st.vals["v_step"], st.k_cache, st.v_cache, slots_d,
                              tables_d, lens_d)
         if timed:
@@ -175,68 +269,45 @@ def main() -> int:
             dec_events.append((e0, e1))
             step_lens.append(buf[S:].copy())
 
-    if args.calib_copy_mib > 0:
-        src_buf = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
-        dst_buf = torch.empty_like(src_buf)
-        torch.cuda.synchronize()
-        dst_buf.copy_(src_buf)
-        torch.cuda.synchronize()
-        del src_buf, dst_buf
-
-    # Setup made many Python objects (the churn script); a cyclic-GC pass over them inside the
-    # timed loop stalls the host for tens of milliseconds.  Freeze them and keep the collector
-    # off while steps run, as a serving loop would.
-    gc.collect()
-    gc.freeze()
-    gc.disable()
-    for i in range(args.warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    host_s.clear()
-    t0 = time.perf_counter()
-    for i in range(args.warmup, total):
-        step(i, True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    gc.enable()
+    elapsed = timed_loop(args, step)
     if not torch.isfinite(out.float()).all():
-        print(json.dumps({"error": "non-finite decode output"}), flush=True)
-        return 1
+        return {"error": "non-finite decode output"}
     # the device-resident tables must still mirror the block manager's exactly
-    if not np.array_equal(tables_d.cpu().numpy(), st.bm.block_tables(ids, max_blocks)[0]):
-        print(json.dumps({"error": "device block tables diverged from the block manager"}), flush=True)
-        return 1
+    final_tables, final_lens = st.bm.block_tables(ids, max_blocks)
+    if not np.array_equal(tables_d.cpu().numpy(), final_tables):
+        return {"error": "device block tables diverged from the block manager"}
 
     ms_step = 1e3 * elapsed / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in dec_events]
-    dec_avg_ms = float(np.mean(dec_ms))
+    dec_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_events]))
     dec_bytes, write_bytes = zip(*[algorithmic_bytes(l, w, S) for l in step_lens])
     dec_bytes_avg = float(np.mean(dec_bytes))
     step_bytes_avg = dec_bytes_avg + float(np.mean(write_bytes))
+    tokens = int(np.mean([l.sum() for l in step_lens]))
+    shared = args.workload.startswith("shared")
+    extra = {}
+    if shared:
+        # shared prefix blocks are read once per sequence but live once in HBM: the roofline
+        # counts each physical block once; the logical (per-sequence) rate is "effective"
+        elt = 2
+        logical_kv = tokens * w.hkv * w.head_dim * 2 * elt
+        uniq = unique_kv_bytes(final_tables, final_lens, w)
+        extra = {"effective_logical_GBps": round(dec_bytes_avg / (dec_avg_ms * 1e-3) / 1e9, 1),
+                 "unique_kv_bytes": uniq, "logical_kv_bytes": logical_kv,
+                 "cow_pairs_first_step": n_pairs[0], "cow_pairs_later_steps": sum(n_pairs[1:])}
+        dec_bytes_avg = dec_bytes_avg - logical_kv + uniq
+        step_bytes_avg = step_bytes_avg - logical_kv + uniq
     achieved = dec_bytes_avg / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes_avg / (ms_step * 1e-3) / 1e9
-    tokens = int(np.mean([l.sum() for l in step_lens]))
-
+    headline = args.workload == "llama70b"
     cpu = None
-    if args.cpu_seqs > 0:
+    if args.cpu_seqs > 0 and headline:
         cpu = cpu_baseline(w, st, args.cpu_seqs, args.cpu_seconds)
-
-    line = {
-        "metric": "paged decode attention: HBM GB/s (% of peak) + decode tokens/s at batch 256",
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "llama3-70b-shaped decode layer, batch 256, 64/8 heads, D=128, "
-                               "B=16, log-normal ctx (median 1024, [16, 8192]), %s pool" % args.pool,
-                   "global_batch": S, "seq_len": "log-normal, mean %d" % (tokens // S),
+    line = {"metric": "paged decode attention: HBM GB/s (% of peak) + decode tokens/s at batch 256",
+            "value": round(value, 1), "unit": "GB/s"}
+    line.update(base_line(args, w, ms_step))
+    line.update({
+        "config": {"workload": WORKLOADS[args.workload] + ", %s pool" % args.pool,
+                   "global_batch": S, "seq_len": "mean %d" % (tokens // S),
                    "context_tokens": tokens, "partition_tokens": args.partition or "auto",
                    "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(S / (ms_step * 1e-3), 1),
@@ -244,14 +315,91 @@ def main() -> int:
         "host_block_manager_us": round(1e6 * float(np.median(host_s)), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic() if headline and args.pool == "churned" else None,
                      "kernel": "pa_decode (plan + persistent split-K decode + merge)",
                      "avg_ms": round(dec_avg_ms, 4), "algorithmic_bytes": int(dec_bytes_avg)},
         "cpu_baseline": cpu,
         "setup_s": round(t_setup, 1),
-    }
-    print(json.dumps(line), flush=True)
-    return 0
+    })
+    line.update(extra)
+    return line
+
+
+def chunk_flops(lens, C, w):
+    """Causal-exact attention flops of a chunk step: 4 D Hq per (query, visible key) pair."""
+    pairs = sum(sum(int(n) - C + i + 1 for i in range(C)) for n in lens)
+    return 4 * w.head_dim * w.hq * pairs
+
+
+def run_chunk(args, w, st, t_setup):
+    """The chunk step: the block manager appends C tokens to every sequence (once, before the
+    timing), then each timed iteration replays the step's device work on the same slots and
+    values -- cache write + table patch of the S*C new tokens, then chunked-query attention --
+    so the pool does not grow from iteration to iteration."""
+    import torch
+
+    from paged_kv_cache_378_amd import _lib
+
+    dev = st.device
+    S, B, C = w.num_seqs, w.block_size, w.step_tokens
+    ids = np.asarray(w.step_ids, np.int64)
+    max_ctx = max(w.ctx_lens())
+    max_blocks = (max_ctx + B - 1) // B
+    tables0, lens_before = st.bm.block_tables(ids, max_blocks)
+    slots, pairs = st.bm.append_slots(ids, C)
+    lens = st.bm.seq_lens(ids)
+    assert not len(pairs)
+    tables_d = torch.from_numpy(tables0).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    slots_d = torch.from_numpy(slots).to(dev)
+    out = st.new_out()
+    stream = torch.cuda.current_stream()
+    ev_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    events = []
+
+    def step(i, timed):
+        _lib.pa_cache_append(st.vals["k_step"], st.vals["v_step"], st.k_cache, st.v_cache, slots_d,
+                             tables_d, lens_d, C)
+        if timed:
+            e0, e1 = ev_pool[len(events)]
+            e0.record(stream)
+        _lib.pa_chunk_attend(out, st.vals["q"], st.k_cache, st.v_cache, tables_d, lens_d, w.scale)
+        if timed:
+            e1.record(stream)
+            events.append((e0, e1))
+
+    elapsed = timed_loop(args, step)
+    if not torch.isfinite(out.float()).all():
+        return {"error": "non-finite chunk output"}
+    if not np.array_equal(tables_d.cpu().numpy(), st.bm.block_tables(ids, max_blocks)[0]):
+        return {"error": "device block tables diverged from the block manager"}
+    ms_step = 1e3 * elapsed / args.steps
+    att_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    flops = chunk_flops(lens, C, w)
+    elt = 2
+    kv = int(np.sum(lens)) * w.hkv * w.head_dim * 2 * elt
+    qo = 2 * S * C * w.hq * w.head_dim * elt
+    write = S * C * w.hkv * w.head_dim * 2 * elt * 2
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    line = {"metric": "chunked-query paged attention: TFLOP/s (causal-exact flops)",
+            "value": round(value, 1), "unit": "TFLOP/s"}
+    line.update(base_line(args, w, ms_step))
+    line.update({
+        "config": {"workload": WORKLOADS["chunk"] + ", %s pool" % args.pool, "global_batch": S,
+                   "chunk_tokens": C, "context_tokens": int(np.sum(lens)),
+                   "parallelism": "none (1 GPU)"},
+        "prefill_tokens_per_s": round(S * C / (ms_step * 1e-3), 1),
+        "step_bytes": kv + qo + write,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "pa_chunk_attend (chunk_kernel)",
+                     "avg_ms": round(att_ms, 4), "algorithmic_flops": flops},
+        "cpu_baseline": None,
+        "setup_s": round(t_setup, 1),
+    })
+    return line
 
 
 def cpu_baseline(w, st, n_seqs, min_seconds):

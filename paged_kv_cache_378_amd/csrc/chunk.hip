@@ -11,7 +11,9 @@
 // Decomposition (CDNA4-specific):
 //   * a workgroup = (sequence, kv-head, block of TQ chunk tokens); its rows are the
 //     (token, query head) pairs of that kv-head's group, so every K/V tile loaded is used by
-//     all g heads (GQA) -- 256 rows per workgroup, 64 per wave, in 4 column tiles of 16;
+//     all g heads (GQA) -- 256 rows per workgroup, 32 per wave (8 waves), in 2 column tiles
+//     of 16 (the accumulators of 32 rows fit in VGPRs; 64 rows per wave spilled them to AGPRs
+//     and the loop moved them back and forth);
 //   * K/V tiles of 32 keys are staged in LDS (double-buffered: the next tile's global loads
 //     are in flight while the current one is multiplied); rows are padded by 16 bytes so the
 //     16-lane operand reads hit distinct banks;
@@ -22,6 +24,7 @@
 //   * online softmax in the log2 domain, fp32 accumulation, P rounded to bf16 for the MFMA
 //     and the row sum accumulated from the same rounded values.
 
+#include <climits>
 #include <cmath>
 
 #include "device_common.h"
@@ -30,11 +33,14 @@ namespace pa {
 
 namespace chunk {
 
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 64;
+constexpr int kWaves = 8;
+constexpr int kRowsPerWave = 32;
 constexpr int kNC = kRowsPerWave / 16;  // 16-row column tiles per wave
 constexpr int kRows = kWaves * kRowsPerWave;
-constexpr int kKT = 32;                 // keys per tile
+constexpr int kKT = 64;                 // keys per LDS tile (one barrier per tile)
+constexpr int kSub = 32;                // keys per compute step (two steps per tile)
+constexpr int kTblWin = 512;            // block-table entries staged in LDS at a time
+constexpr float kLazy = 8.f;            // lazy-rescale threshold (log2 units: weights < 256)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Args {
@@ -63,6 +69,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   constexpr int NNT = D / 16;  // PV dim tiles
   using SM = Smem<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SM::STAGE];
+  __shared__ int s_tbl[kTblWin];  // physical blocks of logical blocks win0 .. win0 + kTblWin - 1
 
   const int qb = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = wave_id();
@@ -113,9 +120,28 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   static_assert(KTILE_VECS % (kWaves * kWave) == 0 && VTILE_VECS % (kWaves * kWave) == 0, "");
   const size_t head_stride = static_cast<size_t>(B) * D;
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
+  const int nblk_total = (kend + B - 1) / B;  // logical blocks this workgroup reads
+
+  // The table slice is staged in LDS (a window of kTblWin entries, moved forward when the
+  // tiles pass its end), so a tile's K/V loads never wait on a dependent table load.  Entries
+  // outside the pool are replaced by block 0 and poison the workgroup's outputs.
+  int bad_entry = 0;
+  int win0 = 0;
+  auto load_window = [&](int first) {
+    const int cnt = min(kTblWin, nblk_total - first);
+    for (int i = tid; i < cnt; i += kWaves * kWave) {
+      int blk = trow[first + i];
+      if (blk < 0 || blk >= a.num_blocks) {
+        bad_entry = 1;
+        blk = 0;
+      }
+      s_tbl[i] = blk;
+    }
+  };
+  load_window(0);
+  __syncthreads();
 
   uint4 pk[PASSES_K], pv[PASSES_V];
-  int bad_entry = 0;
   auto gload = [&](int t) {
     const int k0 = t * kKT;
 #pragma unroll
@@ -123,8 +149,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       const int e = tid + p * kWaves * kWave;
       const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
       const int j = min(k0 + key, kend - 1);   // clamp: never past the last needed key
-      int blk = trow[j / B];
-      if (blk < 0 || blk >= a.num_blocks) { bad_entry = 1; blk = 0; }
+      const int blk = s_tbl[j / B - win0];
       pk[p] = *reinterpret_cast<const uint4*>(
           a.kc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(j % B) * D + piece * 8);
     }
@@ -133,8 +158,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       const int e = tid + p * kWaves * kWave;
       const int dim = e / VP_PER_ROW, piece = e % VP_PER_ROW;   // piece = 8 keys
       const int j = min(k0 + 8 * piece, (kend - 1) & ~7);
-      int blk = trow[j / B];
-      if (blk < 0 || blk >= a.num_blocks) { bad_entry = 1; blk = 0; }
+      const int blk = s_tbl[j / B - win0];
       pv[p] = *reinterpret_cast<const uint4*>(
           a.vc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(dim) * B + (j % B));
       // Keys at or past kend carry weight 0, but their slots may hold anything (even NaN,
@@ -177,6 +201,93 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     for (int i = 0; i < NNT; ++i) o[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // One 32-key step on the staged tile: keys k0 .. k0 + 31 = rows kSub*hs .. of the tile.
+  auto compute_sub = [&](const unsigned char* kb, const unsigned char* vb, int k0, int hs) {
+
+      // S^T = K Q^T : row r16 of key group m is key 8*(r16/4) + 4*m + r16%4 of the tile
+      f32x4 sacc[2][kNC];
+  #pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int key = kSub * hs + 8 * (r16 >> 2) + 4 * m + (r16 & 3);
+        bf16x8 kop[NST];
+  #pragma unroll
+        for (int st = 0; st < NST; ++st)
+          kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + key * SM::KROW + (4 * st + gp) * 16));
+  #pragma unroll
+        for (int c = 0; c < kNC; ++c) {
+          sacc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int st = 0; st < NST; ++st)
+            sacc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], qop[c][st], sacc[m][c], 0, 0, 0);
+        }
+      }
+
+      // Online softmax per column tile; lane (gp, r16) owns keys k0 + 8 gp + j of row r16.
+      // Masking is needed only on tiles that reach past the causal limit of the workgroup's first
+      // row (which also covers every key at or past kend); padding rows are never masked, their
+      // outputs are dropped.
+      const bool need_mask = k0 + kSub - 1 > base + i0;  // uniform
+      bf16x8 pop[kNC];
+      float alpha[kNC];
+      bool any_rescale = false;
+  #pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        float x[8];
+        if (need_mask) {
+          const int limit = row_tok[c] < 0 ? INT32_MAX : base + row_tok[c];  // last visible key
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float v = sacc[j >> 2][c][j & 3] * a.scale_log2;
+            x[j] = (k0 + 8 * gp + j <= limit) ? v : -INFINITY;
+          }
+        } else {
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = sacc[j >> 2][c][j & 3] * a.scale_log2;
+        }
+        float mx = x[0];
+  #pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        // Lazy rescaling: the row's reference max m_run moves only when a score exceeds it by
+        // more than kLazy (log2 units).  Weights exp2(x - m_run) then stay below 2^kLazy, and
+        // the rescale of the 32 accumulators of the row (held in AGPRs) is rare.  After the final
+        // division by l the result is the same softmax.
+        alpha[c] = 1.f;
+        if (mx > m_run[c] + kLazy) {
+          alpha[c] = exp2f(m_run[c] - mx);  // 0 on the first visible key (m_run = -inf)
+          m_run[c] = mx;
+          any_rescale = true;
+        }
+        const float m_use = m_run[c] == -INFINITY ? 0.f : m_run[c];
+        float psum = 0.f;
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const __bf16 pb = static_cast<__bf16>(exp2f(x[j] - m_use));
+          pop[c][j] = pb;
+          psum += static_cast<float>(pb);
+        }
+        l_run[c] = l_run[c] * alpha[c] + psum;
+      }
+
+      // O^T += V^T P^T over the 32 keys (V of keys past kend was zeroed when staged).
+      if (__builtin_amdgcn_ballot_w64(any_rescale)) {  // uniform: some row of the wave rescales
+  #pragma unroll
+        for (int c = 0; c < kNC; ++c)
+  #pragma unroll
+          for (int ni = 0; ni < NNT; ++ni) o[c][ni] *= alpha[c];
+      }
+  #pragma unroll
+      for (int ni = 0; ni < NNT; ++ni) {
+        const bf16x8 vop = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(vb + (16 * ni + r16) * SM::VROW + (4 * hs + gp) * 16));
+  #pragma unroll
+        for (int c = 0; c < kNC; ++c)
+          o[c][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[c], o[c][ni], 0, 0, 0);
+      }
+
+  };
+
   if (ntiles > 0) {
     gload(0);
     lstore(0);
@@ -185,73 +296,24 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
 
   for (int t = 0; t < ntiles; ++t) {
     const int stage = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+    if (t + 1 < ntiles) {
+      // keys of tile t+1: (t+1)*kKT .. min(kend, (t+2)*kKT) - 1
+      const int last_blk = (min(kend, (t + 2) * kKT) - 1) / B;
+      if (last_blk >= win0 + kTblWin) {  // uniform: move the window (gload(t) has finished)
+        win0 = ((t + 1) * kKT) / B;
+        load_window(win0);
+        __syncthreads();
+      }
+      gload(t + 1);
+    }
     const unsigned char* kb = smem + stage * SM::STAGE;
     const unsigned char* vb = kb + SM::KBYTES;
-    const int k0 = t * kKT;
-
-    // S^T = K Q^T : row r16 of key group m is key 8*(r16/4) + 4*m + r16%4 of the tile
-    f32x4 sacc[2][kNC];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int key = 8 * (r16 >> 2) + 4 * m + (r16 & 3);
-      bf16x8 kop[NST];
-#pragma unroll
-      for (int st = 0; st < NST; ++st)
-        kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + key * SM::KROW + (4 * st + gp) * 16));
-#pragma unroll
-      for (int c = 0; c < kNC; ++c) {
-        sacc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < NST; ++st)
-          sacc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], qop[c][st], sacc[m][c], 0, 0, 0);
-      }
+    for (int hs = 0; hs < kKT / kSub; ++hs) {
+      const int k0 = t * kKT + hs * kSub;
+      if (k0 >= kend) break;  // uniform
+      compute_sub(kb, vb, k0, hs);
     }
-
-    // online softmax per column tile; lane (gp, r16) owns keys k0 + 8 gp + j of row r16
-    bf16x8 pop[kNC];
-    float alpha[kNC];
-#pragma unroll
-    for (int c = 0; c < kNC; ++c) {
-      const int limit = row_tok[c] < 0 ? -1 : base + row_tok[c];  // last visible position
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = sacc[j >> 2][c][j & 3] * a.scale_log2;
-        x[j] = (k0 + 8 * gp + j <= limit) ? v : -INFINITY;
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[c], mx);
-      // rows that have seen nothing yet (m_new = -inf) keep zero weights
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      alpha[c] = exp2f(m_run[c] - m_use);
-      m_run[c] = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const __bf16 pb = static_cast<__bf16>(exp2f(x[j] - m_use));
-        pop[c][j] = pb;
-        psum += static_cast<float>(pb);
-      }
-      l_run[c] = l_run[c] * alpha[c] + psum;
-    }
-
-    // O^T += V^T P^T over the 32 keys (V of keys past kend was zeroed when staged).
-#pragma unroll
-    for (int ni = 0; ni < NNT; ++ni) {
-      const bf16x8 vop = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(vb + (16 * ni + r16) * SM::VROW + gp * 16));
-#pragma unroll
-      for (int c = 0; c < kNC; ++c) {
-        o[c][ni] *= alpha[c];
-        o[c][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[c], o[c][ni], 0, 0, 0);
-      }
-    }
-
     if (t + 1 < ntiles) lstore(stage ^ 1);
     __syncthreads();
   }
@@ -327,11 +389,11 @@ extern "C" pa_status pa_chunk_attend(void* out, const void* q, const void* k_cac
   const dim3 grid((C + a.TQ - 1) / a.TQ, Hkv, S);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 64) {
-    if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<64, 16>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((chunk::chunk_kernel<64, 32>), grid, dim3(256), 0, st, a);
+    if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<64, 16>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
+    else hipLaunchKernelGGL((chunk::chunk_kernel<64, 32>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
   } else {
-    if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<128, 16>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((chunk::chunk_kernel<128, 32>), grid, dim3(256), 0, st, a);
+    if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<128, 16>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
+    else hipLaunchKernelGGL((chunk::chunk_kernel<128, 32>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
   }
   return launch_status("pa_chunk_attend");
 }

@@ -191,12 +191,16 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     }
   };
 
-  float m_run[kNC], l_run[kNC];
+  float m_run[kNC];
+  f32x4 lsum[kNC];  // row sums: every element of lane (gp, r16) holds row r16's sum
+  bf16x8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = static_cast<__bf16>(1.f);
   f32x4 o[kNC][NNT];
 #pragma unroll
   for (int c = 0; c < kNC; ++c) {
     m_run[c] = -INFINITY;
-    l_run[c] = 0.f;
+    lsum[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NNT; ++i) o[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -232,51 +236,51 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       bool any_rescale = false;
   #pragma unroll
       for (int c = 0; c < kNC; ++c) {
+        // raw scores; the scale (> 0, checked on the host) is applied inside the exponent
         float x[8];
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = sacc[j >> 2][c][j & 3];
         if (need_mask) {
           const int limit = row_tok[c] < 0 ? INT32_MAX : base + row_tok[c];  // last visible key
   #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float v = sacc[j >> 2][c][j & 3] * a.scale_log2;
-            x[j] = (k0 + 8 * gp + j <= limit) ? v : -INFINITY;
-          }
-        } else {
-  #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = sacc[j >> 2][c][j & 3] * a.scale_log2;
+          for (int j = 0; j < 8; ++j)
+            if (k0 + 8 * gp + j > limit) x[j] = -INFINITY;
         }
-        float mx = x[0];
-  #pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
+        mx *= a.scale_log2;  // row max in log2 units (the scale is positive)
         // Lazy rescaling: the row's reference max m_run moves only when a score exceeds it by
         // more than kLazy (log2 units).  Weights exp2(x - m_run) then stay below 2^kLazy, and
-        // the rescale of the 32 accumulators of the row (held in AGPRs) is rare.  After the final
-        // division by l the result is the same softmax.
+        // the rescale of the row's accumulators is rare.  After the final division by the
+        // row sum the result is the same softmax.
         alpha[c] = 1.f;
         if (mx > m_run[c] + kLazy) {
-          alpha[c] = exp2f(m_run[c] - mx);  // 0 on the first visible key (m_run = -inf)
+          alpha[c] = fast_exp2(m_run[c] - mx);  // 0 on the first visible key (m_run = -inf)
           m_run[c] = mx;
           any_rescale = true;
         }
         const float m_use = m_run[c] == -INFINITY ? 0.f : m_run[c];
-        float psum = 0.f;
   #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const __bf16 pb = static_cast<__bf16>(exp2f(x[j] - m_use));
-          pop[c][j] = pb;
-          psum += static_cast<float>(pb);
-        }
-        l_run[c] = l_run[c] * alpha[c] + psum;
+        for (int j = 0; j < 8; ++j)
+          pop[c][j] = static_cast<__bf16>(fast_exp2(fmaf(x[j], a.scale_log2, -m_use)));
       }
 
-      // O^T += V^T P^T over the 32 keys (V of keys past kend was zeroed when staged).
+      // O^T += V^T P^T over the 32 keys (V of keys past kend was zeroed when staged), and the
+      // row sums by the same instruction against a tile of ones, so they are summed from the
+      // same bf16 weights the numerator uses.
       if (__builtin_amdgcn_ballot_w64(any_rescale)) {  // uniform: some row of the wave rescales
   #pragma unroll
-        for (int c = 0; c < kNC; ++c)
+        for (int c = 0; c < kNC; ++c) {
+          lsum[c] *= alpha[c];
   #pragma unroll
           for (int ni = 0; ni < NNT; ++ni) o[c][ni] *= alpha[c];
+        }
       }
+  #pragma unroll
+      for (int c = 0; c < kNC; ++c)
+        lsum[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[c], lsum[c], 0, 0, 0);
   #pragma unroll
       for (int ni = 0; ni < NNT; ++ni) {
         const bf16x8 vop = __builtin_bit_cast(
@@ -324,9 +328,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   // ---- normalise and store: lane holds row r16 of tile c, dims 16 ni + 4 gp + i
 #pragma unroll
   for (int c = 0; c < kNC; ++c) {
-    float l = l_run[c];
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    const float l = lsum[c][0];
     if (row_tok[c] < 0) continue;
     const float inv = (bad || any_bad) ? NAN : 1.f / l;
     uint16_t* op = a.out + ((static_cast<size_t>(s) * C + row_tok[c]) * a.Hq + kvh * G + row_head[c]) * D;
@@ -364,7 +366,8 @@ extern "C" pa_status pa_chunk_attend(void* out, const void* q, const void* k_cac
     return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: num_blocks %d, max_blocks %d", num_blocks, max_blocks);
   if (static_cast<int64_t>(C) > static_cast<int64_t>(max_blocks) * B)
     return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: chunk longer than a table row can hold");
-  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: scale is NaN");
+  if (!(scale > 0.f) || scale == INFINITY)
+    return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: scale must be positive and finite");
   if (S == 0 || C == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens)
     return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: NULL pointer");

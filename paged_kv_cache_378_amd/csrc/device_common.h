@@ -47,6 +47,10 @@ template <> struct Elem<uint16_t> {  // bf16 carried as raw bits
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// 2^x by the hardware instruction alone: exact at -inf (0), results below 2^-126 flush to 0
+// (harmless for softmax weights, which are summed against weights near 1).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Index of this wave in its workgroup, as a wave-uniform (scalar) value.  Without the
 // readfirstlane the compiler treats threadIdx.x / 64 as divergent, so every loop bounded by
 // it becomes exec-masked vector control flow instead of a scalar loop.

@@ -141,8 +141,13 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   load_window(0);
   __syncthreads();
 
-  uint4 pk[PASSES_K], pv[PASSES_V];
-  auto gload = [&](int t) {
+  // Two register sets stage tiles on their way to LDS: the loads of tile t+2 are issued while
+  // tile t is multiplied and stored at the end of iteration t+1, so each tile's global loads
+  // have two compute phases to arrive.
+  struct Regs {
+    uint4 k[PASSES_K], v[PASSES_V];
+  };
+  auto gload = [&](Regs& r, int t) {
     const int k0 = t * kKT;
 #pragma unroll
     for (int p = 0; p < PASSES_K; ++p) {
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
       const int j = min(k0 + key, kend - 1);   // clamp: never past the last needed key
       const int blk = s_tbl[j / B - win0];
-      pk[p] = *reinterpret_cast<const uint4*>(
+      r.k[p] = *reinterpret_cast<const uint4*>(
           a.kc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(j % B) * D + piece * 8);
     }
 #pragma unroll
@@ -159,35 +164,37 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       const int dim = e / VP_PER_ROW, piece = e % VP_PER_ROW;   // piece = 8 keys
       const int j = min(k0 + 8 * piece, (kend - 1) & ~7);
       const int blk = s_tbl[j / B - win0];
-      pv[p] = *reinterpret_cast<const uint4*>(
+      r.v[p] = *reinterpret_cast<const uint4*>(
           a.vc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(dim) * B + (j % B));
-      // Keys at or past kend carry weight 0, but their slots may hold anything (even NaN,
-      // and 0 * NaN = NaN inside the MFMA): zero them.
-      const int nvalid = kend - (k0 + 8 * piece);
-      if (nvalid < 8) {
-        uint16_t e8[8];
-        __builtin_memcpy(e8, &pv[p], 16);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= nvalid) e8[e] = 0;
-        __builtin_memcpy(&pv[p], e8, 16);
-      }
     }
   };
-  auto lstore = [&](int stage) {
+  auto lstore = [&](Regs& r, int stage, int t) {
     unsigned char* kb = smem + stage * SM::STAGE;
     unsigned char* vb = kb + SM::KBYTES;
+    const int k0 = t * kKT;
 #pragma unroll
     for (int p = 0; p < PASSES_K; ++p) {
       const int e = tid + p * kWaves * kWave;
       const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
-      *reinterpret_cast<uint4*>(kb + key * SM::KROW + piece * 16) = pk[p];
+      *reinterpret_cast<uint4*>(kb + key * SM::KROW + piece * 16) = r.k[p];
     }
+    // Keys at or past kend carry weight 0, but their slots may hold anything (even NaN, and
+    // 0 * NaN = NaN inside the MFMA): zero their V elements (only the last tile has any).
+    const bool tail = k0 + kKT > kend;  // uniform
 #pragma unroll
     for (int p = 0; p < PASSES_V; ++p) {
       const int e = tid + p * kWaves * kWave;
       const int dim = e / VP_PER_ROW, piece = e % VP_PER_ROW;
-      *reinterpret_cast<uint4*>(vb + dim * SM::VROW + piece * 16) = pv[p];
+      if (tail) {
+        const int nvalid = kend - (k0 + 8 * piece);
+        uint16_t e8[8];
+        __builtin_memcpy(e8, &r.v[p], 16);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (q >= nvalid) e8[q] = 0;
+        __builtin_memcpy(&r.v[p], e8, 16);
+      }
+      *reinterpret_cast<uint4*>(vb + dim * SM::VROW + piece * 16) = r.v[p];
     }
   };
 
@@ -292,25 +299,20 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
 
   };
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < ntiles) {
-      // keys of tile t+1: (t+1)*kKT .. min(kend, (t+2)*kKT) - 1
-      const int last_blk = (min(kend, (t + 2) * kKT) - 1) / B;
-      if (last_blk >= win0 + kTblWin) {  // uniform: move the window (gload(t) has finished)
-        win0 = ((t + 1) * kKT) / B;
+  // Iteration t: issue tile t+2's loads into the register set tile t used, multiply tile t
+  // (LDS stage t % 2), store tile t+1 from the other register set into the other stage.
+  auto iteration = [&](Regs& mine, Regs& next, int t) {
+    if (t + 2 < ntiles) {
+      // keys of tile t+2: (t+2)*kKT .. min(kend, (t+3)*kKT) - 1
+      const int last_blk = (min(kend, (t + 3) * kKT) - 1) / B;
+      if (last_blk >= win0 + kTblWin) {  // uniform: move the window (no load reads it now)
+        win0 = ((t + 2) * kKT) / B;
         load_window(win0);
         __syncthreads();
       }
-      gload(t + 1);
+      gload(mine, t + 2);
     }
-    const unsigned char* kb = smem + stage * SM::STAGE;
+    const unsigned char* kb = smem + (t & 1) * SM::STAGE;
     const unsigned char* vb = kb + SM::KBYTES;
 #pragma unroll
     for (int hs = 0; hs < kKT / kSub; ++hs) {
@@ -318,8 +320,18 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       if (k0 >= kend) break;  // uniform
       compute_sub(kb, vb, k0, hs);
     }
-    if (t + 1 < ntiles) lstore(stage ^ 1);
+    if (t + 1 < ntiles) lstore(next, (t + 1) & 1, t + 1);
     __syncthreads();
+  };
+
+  Regs ra, rb;
+  if (ntiles > 0) gload(ra, 0);
+  if (ntiles > 1) gload(rb, 1);
+  if (ntiles > 0) lstore(ra, 0, 0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    iteration(ra, rb, t);
+    if (t + 1 < ntiles) iteration(rb, ra, t + 1);
   }
 
   // bad table entries anywhere in the workgroup poison its outputs

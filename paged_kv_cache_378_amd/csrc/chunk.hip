@@ -15,8 +15,8 @@
 //     of 16 (the accumulators of 32 rows fit in VGPRs; 64 rows per wave spilled them to AGPRs
 //     and the loop moved them back and forth);
 //   * K/V tiles of 32 keys are staged in LDS (double-buffered: the next tile's global loads
-//     are in flight while the current one is multiplied); rows are padded by 16 bytes so the
-//     16-lane operand reads hit distinct banks;
+//     are in flight while the current one is multiplied); K rows are chunk-swizzled and V rows
+//     padded by 16 bytes so the 16-lane operand reads hit distinct banks;
 //   * S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 32 keys x 16 rows per tile pair) puts keys on the
 //     MFMA rows so a query row's scores sit in one lane column: the row max needs only two
 //     cross-lane steps; O^T = V^T P^T contracts over the 32 keys with P taken straight from
@@ -56,12 +56,22 @@ struct Args {
 
 template <int D>
 struct Smem {
-  static constexpr int KROW = D * 2 + 16;      // bytes per key row of the K tile (padded)
+  static constexpr int KROW = D * 2;           // bytes per key row of the K tile (swizzled)
   static constexpr int VROW = kKT * 2 + 16;    // bytes per dim row of the V^T tile (padded)
   static constexpr int KBYTES = kKT * KROW;
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
 };
+
+// K tile rows are stored with their 16-byte chunks permuted: chunk c of key row `key` sits at
+// chunk c ^ kswz(key).  The QK^T operand read has 16 lanes reading the same chunk of 16 keys
+// that differ in bits 0-1 and 3-4; without the permutation keys 16 apart land in the same
+// banks.  kswz maps those 16 keys to distinct values.
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+  constexpr int kMask = D * 2 / 16 - 1;  // chunks per row - 1
+  return ((key & 3) | (((key >> 3) & 3) << 2)) & kMask;
+}
 
 template <int D, int B>
 __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     for (int p = 0; p < PASSES_K; ++p) {
       const int e = tid + p * kWaves * kWave;
       const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
-      *reinterpret_cast<uint4*>(kb + key * SM::KROW + piece * 16) = r.k[p];
+      *reinterpret_cast<uint4*>(kb + key * SM::KROW + ((piece ^ kswz<D>(key)) << 4)) = r.k[p];
     }
     // Keys at or past kend carry weight 0, but their slots may hold anything (even NaN, and
     // 0 * NaN = NaN inside the MFMA): zero their V elements (only the last tile has any).
@@ -214,7 +224,6 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
 
   // One 32-key step on the staged tile: keys k0 .. k0 + 31 = rows kSub*hs .. of the tile.
   auto compute_sub = [&](const unsigned char* kb, const unsigned char* vb, int k0, int hs) {
-
       // S^T = K Q^T : row r16 of key group m is key 8*(r16/4) + 4*m + r16%4 of the tile
       f32x4 sacc[2][kNC];
   #pragma unroll
@@ -223,7 +232,8 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
         bf16x8 kop[NST];
   #pragma unroll
         for (int st = 0; st < NST; ++st)
-          kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + key * SM::KROW + (4 * st + gp) * 16));
+          kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+              kb + key * SM::KROW + (((4 * st + gp) ^ kswz<D>(key)) << 4)));
   #pragma unroll
         for (int c = 0; c < kNC; ++c) {
           sacc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -255,8 +265,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
         }
         float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+        mx = max_xor32(max_xor16(mx));
         mx *= a.scale_log2;  // row max in log2 units (the scale is positive)
         // Lazy rescaling: the row's reference max m_run moves only when a score exceeds it by
         // more than kLazy (log2 units).  Weights exp2(x - m_run) then stay below 2^kLazy, and

@@ -47,6 +47,19 @@ template <> struct Elem<uint16_t> {  // bf16 carried as raw bits
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// Max over lane pairs (i, i ^ 16) and (i, i ^ 32) with gfx950's row-swap instructions
+// (VALU, no LDS round trip as a generic shuffle has).  Swapping odd 16-lane rows of one copy of
+// v with even rows of another leaves every lane holding its own value and its xor-16
+// partner's; the 32-lane swap does the same for the xor-32 partner.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // 2^x by the hardware instruction alone: exact at -inf (0), results below 2^-126 flush to 0
 // (harmless for softmax weights, which are summed against weights near 1).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

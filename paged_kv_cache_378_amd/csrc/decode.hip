@@ -53,7 +53,7 @@ namespace pa {
 constexpr int kNW = 4;            // waves per workgroup
 constexpr int kMaxPT = 8192;      // largest partition (tokens)
 constexpr int kMinAutoPT = 256;   // smallest partition the automatic choice uses
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kMaxBuckets = kMaxPT / 32 + 1;  // partial partitions bucketed by 32-token tiles
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -66,7 +66,7 @@ struct DecodeArgs {
   const int32_t* ctx_lens;
   float* part_o;    // [S, Hq, Pmax, D]  partition outputs (normalised)
   float2* part_ml;  // [S, Hq, Pmax]     (max in log2 units, sum)
-  int2* items;      // work list: (sequence, part * Hkv + kv-head), longest first
+  int2* items;      // work list: (sequence, partition) entries, longest first; Hkv items each
   int* queue;       // [0] number of items, [1] next unclaimed item
   int S, Hq, Hkv, G, max_blocks, num_blocks, PT, Pmax;
   int len_cap;      // min(max_blocks * B, max_ctx_len): longest context the call may see
@@ -176,8 +176,8 @@ __device__ __forceinline__ void for_each_item(const DecodeArgs& a, int* s_next, 
   while (i < count) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(&a.queue[1], 1);
-    const int2 it = a.items[i];
-    body(it.x, it.y % a.Hkv, it.y / a.Hkv);
+    const int2 it = a.items[i / a.Hkv];
+    body(it.x, i % a.Hkv, it.y);
     if (threadIdx.x == 0) *s_next = nxt;
     __syncthreads();
     i = __builtin_amdgcn_readfirstlane(*s_next);
@@ -580,63 +580,75 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // Planning: the work list, longest items first.  One workgroup reads every context length,
-// counts the full partitions and buckets the partial last partitions by their length in
-// 32-token tiles, then places full partitions first and the partial ones by decreasing
-// bucket (an empty or invalid context gets one item, which writes NaN).  It also sets the
-// persistent kernel's cursor to the grid size (workgroup g starts with item g).  Positions
-// inside a bucket are claimed with LDS atomics, so the order inside a bucket can change from
-// call to call; results do not depend on it (each item's output has a fixed place).
+// places the full partitions first (positions by a prefix sum) and buckets the partial last
+// partitions by their length in 32-token tiles, in decreasing order (an empty or invalid
+// context gets one item, which writes NaN).  The list holds one (sequence, partition) entry
+// per partition; item i is entry i / Hkv for kv-head i % Hkv, so the Hkv heads of a partition
+// are consecutive items.  It also sets the persistent kernel's cursor to the grid size
+// (workgroup g starts with item g).  Positions inside a bucket are claimed with LDS atomics,
+// so the order inside a bucket can change from call to call; results do not depend on it
+// (each item's output has a fixed place).
 // ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int grid) {
+  constexpr int kPlanWaves = kPlanThreads / kWave;
   __shared__ int s_cnt[kMaxBuckets];   // partial partitions per bucket
-  __shared__ int s_base[kMaxBuckets];  // first item of each bucket (then a cursor)
-  __shared__ int s_full, s_fcur;
+  __shared__ int s_base[kMaxBuckets];  // first entry of each bucket (then a cursor)
+  __shared__ int s_wave[kPlanWaves];
+  __shared__ int s_full;               // full partitions counted so far
   const int nbk = a.PT / 32;  // a partial partition has 0 .. PT-1 tokens: buckets 0 .. nbk
   for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
-  if (threadIdx.x == 0) {
-    s_full = 0;
-    s_fcur = 0;
-  }
+  if (threadIdx.x == 0) s_full = 0;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   __syncthreads();
-  // The common case (S <= kPlanThreads) keeps each thread's length in a register for the
-  // second pass; larger batches read the lengths again.
-  int n_own = 0;
-  for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
-    bool bad;
-    const int n = eff_len(a.ctx_lens[s], a.len_cap, bad);
-    if (s == threadIdx.x) n_own = n;
-    const int full = n / a.PT, rem = n - full * a.PT;
-    if (full) atomicAdd(&s_full, full);
-    if (rem > 0 || n == 0) atomicAdd(&s_cnt[(rem + 31) / 32], 1);
+  // Pass 1, one sequence per thread per round: full partitions get consecutive entries from
+  // a block-wide prefix sum; partial ones are counted per bucket.
+  for (int s0 = 0; s0 < a.S; s0 += kPlanThreads) {
+    const int s = s0 + threadIdx.x;
+    int n = 0;
+    if (s < a.S) {
+      bool bad;
+      n = eff_len(a.ctx_lens[s], a.len_cap, bad);
+    }
+    const int full = s < a.S ? n / a.PT : 0, rem = n - full * a.PT;
+    const int incl = wave_inclusive_sum(full);
+    if (lane == kWave - 1) s_wave[w] = incl;
+    if (s < a.S && (rem > 0 || n == 0)) atomicAdd(&s_cnt[(rem + 31) / 32], 1);
+    __syncthreads();
+    int before = s_full;
+    for (int v = 0; v < w; ++v) before += s_wave[v];
+    const int f0 = before + incl - full;
+    for (int p = 0; p < full; ++p) a.items[f0 + p] = make_int2(s, p);
+    __syncthreads();
+    if (threadIdx.x == kPlanThreads - 1) s_full = before + incl;
+    __syncthreads();
   }
-  __syncthreads();
   // Buckets in decreasing order after the full partitions: base[b] = full + sum_{b' > b} cnt[b'].
   for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) {
     int above = 0;
     for (int c = b + 1; c <= nbk; ++c) above += s_cnt[c];
-    s_base[b] = (s_full + above) * a.Hkv;
+    s_base[b] = s_full + above;
     if (b == 0) {
       a.queue[0] = (s_full + above + s_cnt[0]) * a.Hkv;
       a.queue[1] = grid;
     }
   }
   __syncthreads();
+  // Pass 2: the partial partitions.
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
-    int n = n_own;
-    if (s != threadIdx.x) {
-      bool bad;
-      n = eff_len(a.ctx_lens[s], a.len_cap, bad);
-    }
+    bool bad;
+    const int n = eff_len(a.ctx_lens[s], a.len_cap, bad);
     const int full = n / a.PT, rem = n - full * a.PT;
-    if (full) {
-      const int f0 = atomicAdd(&s_fcur, full);
-      for (int p = 0; p < full; ++p)
-        for (int k = 0; k < a.Hkv; ++k) a.items[(f0 + p) * a.Hkv + k] = make_int2(s, p * a.Hkv + k);
-    }
-    if (rem > 0 || n == 0) {
-      const int pos = atomicAdd(&s_base[(rem + 31) / 32], a.Hkv);
-      for (int k = 0; k < a.Hkv; ++k) a.items[pos + k] = make_int2(s, full * a.Hkv + k);
-    }
+    if (rem > 0 || n == 0) a.items[atomicAdd(&s_base[(rem + 31) / 32], 1)] = make_int2(s, full);
   }
 }
 

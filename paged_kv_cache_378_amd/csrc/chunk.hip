@@ -63,16 +63,6 @@ struct Smem {
   static constexpr int STAGE = KBYTES + VBYTES;
 };
 
-// K tile rows are stored with their 16-byte chunks permuted: chunk c of key row `key` sits at
-// chunk c ^ kswz(key).  The QK^T operand read has 16 lanes reading the same chunk of 16 keys
-// that differ in bits 0-1 and 3-4; without the permutation keys 16 apart land in the same
-// banks.  kswz maps those 16 keys to distinct values.
-template <int D>
-__device__ __forceinline__ int kswz(int key) {
-  constexpr int kMask = D * 2 / 16 - 1;  // chunks per row - 1
-  return ((key & 3) | (((key >> 3) & 3) << 2)) & kMask;
-}
-
 template <int D, int B>
 __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   constexpr int NST = D / 32;  // QK k-steps
@@ -186,7 +176,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     for (int p = 0; p < PASSES_K; ++p) {
       const int e = tid + p * kWaves * kWave;
       const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
-      *reinterpret_cast<uint4*>(kb + key * SM::KROW + ((piece ^ kswz<D>(key)) << 4)) = r.k[p];
+      *reinterpret_cast<uint4*>(kb + key * SM::KROW + ((piece ^ pa::kswz<D>(key)) << 4)) = r.k[p];
     }
     // Keys at or past kend carry weight 0, but their slots may hold anything (even NaN, and
     // 0 * NaN = NaN inside the MFMA): zero their V elements (only the last tile has any).
@@ -233,7 +223,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   #pragma unroll
         for (int st = 0; st < NST; ++st)
           kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-              kb + key * SM::KROW + (((4 * st + gp) ^ kswz<D>(key)) << 4)));
+              kb + key * SM::KROW + (((4 * st + gp) ^ pa::kswz<D>(key)) << 4)));
   #pragma unroll
         for (int c = 0; c < kNC; ++c) {
           sacc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};

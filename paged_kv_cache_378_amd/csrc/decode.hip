@@ -189,17 +189,21 @@ __device__ __forceinline__ void for_each_item(const DecodeArgs& a, int* s_next, 
 // MFMA kernel: bf16, 1 <= G <= 16 query heads per kv-head, D in {64, 128}, B in {16, 32}.
 //
 // A wave walks its partition in tiles of 32 tokens (tiles w, w + NW, ...).  Per tile a lane
-// holds 2 x D/32 16-byte pieces of K and D/16 pieces of V^T in registers.  The loads are
-// staggered so that one tile's worth of registers is enough for a full tile in flight: the
-// next tile's K is issued as soon as QK^T has consumed the current K, and the next tile's V
-// as soon as PV has consumed the current V.  That keeps the register budget at three waves
-// per SIMD (12 waves, ~190 KB of K/V in flight per CU).
+// holds D/32 16-byte pieces of K as loaded (whole key rows, 1 KB contiguous per instruction)
+// and D/16 pieces of V^T.  The K tile is re-laid out into the QK^T operand through the wave's
+// LDS slot; V^T pieces are already in the PV operand layout.  The loads are staggered so that
+// one register set keeps a full tile in flight: the next tile's K is issued as soon as the
+// current K is staged, the next V as soon as PV has consumed the current V.  Two waves per SIMD
+// (8 per CU): at three the register budget spills, measured slower.
 // ---------------------------------------------------------------------------------------
-constexpr int kMfmaWaves = 3;  // waves per SIMD the register budget is cut for
+constexpr int kMfmaWaves = 2;  // waves per SIMD the register budget is cut for (256 VGPRs)
 
 template <int D>
 struct MfmaK {
-  bf16x8 k[2][D / 32];  // two 16-token row groups x D/32 k-steps
+  static constexpr int CH = D / 8;       // 16-byte chunks per key row
+  static constexpr int TPI = kWave / CH;  // tokens per contiguous load instruction
+  static constexpr int NI = 32 / TPI;     // load instructions per 32-token tile
+  bf16x8 raw[NI];                         // the tile as loaded: 1 KB contiguous per instruction
 };
 template <int D>
 struct MfmaV {
@@ -241,20 +245,41 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, i
   const int ntiles = t1 > t0 ? (t1 - t0 + 31) / 32 : 0;
   const size_t head_stride = static_cast<size_t>(B) * D;  // elements per (block, kv-head)
 
-  // K rows: row r16 of row group m holds token 8*(r16/4) + 4*m + r16%4 of the tile, so that
-  // after QK^T lane group gp owns tokens 8*gp .. 8*gp+7 (the PV operand layout).
-  auto load_k = [&](MfmaK<D>& kt, int tile) {
+  // K is loaded in whole rows (instruction i covers tokens TPI*i .. TPI*i + TPI-1 of the tile,
+  // 1 KB contiguous; the matrix-core layout would read 16 rows x 64 B per instruction, measured
+  // 5% slower) and re-laid out through this wave's LDS slot.  Tokens past the end repeat the
+  // last live token; their scores are masked.
+  using KT = MfmaK<D>;
+  unsigned char* kstage = reinterpret_cast<unsigned char*>(&s_o[w][0][0]);
+  static_assert(sizeof(s_o[0]) >= 32 * D * 2, "the wave's output slot holds a K tile");
+  auto load_k = [&](KT& kt, int tile) {
     const int tt = t0 + 32 * tile;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int tok = min(tt + 8 * (r16 >> 2) + 4 * m + (r16 & 3), t1 - 1);
+    for (int i = 0; i < KT::NI; ++i) {
+      const int tok = min(tt + KT::TPI * i + lane / KT::CH, t1 - 1);
       const int p = s_tbl[tok / B - b0];
       const uint16_t* kp = kc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride +
                            static_cast<size_t>(tok % B) * D;
-#pragma unroll
-      for (int st = 0; st < NST; ++st)
-        kt.k[m][st] = ld_kv16(kp + 8 * (4 * st + gp));
+      kt.raw[i] = ld_kv16(kp + 8 * (lane % KT::CH));
     }
+  };
+  // Stage the tile (row = token of the tile, chunks permuted by kswz) and read back the QK^T
+  // operand: row r16 of row group m holds token 8*(r16/4) + 4*m + r16%4 of the tile, so that
+  // after QK^T lane group gp owns tokens 8*gp .. 8*gp+7 (the PV operand layout).  The wave
+  // reads back what it wrote (LDS operations of one wave complete in order).
+  auto stage_k = [&](const KT& kt) {
+#pragma unroll
+    for (int i = 0; i < KT::NI; ++i) {
+      const int row = KT::TPI * i + lane / KT::CH, ch = lane % KT::CH;
+      *reinterpret_cast<bf16x8*>(kstage + row * (D * 2) + ((ch ^ kswz<D>(row)) << 4)) = kt.raw[i];
+    }
+  };
+  auto k_operand = [&](int m, bf16x8 (&kop)[NST]) {
+    const int row = 8 * (r16 >> 2) + 4 * m + (r16 & 3);
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+      kop[st] = *reinterpret_cast<const bf16x8*>(
+          kstage + row * (D * 2) + (((4 * st + gp) ^ kswz<D>(row)) << 4));
   };
   // V^T rows: lane (gp, r16) reads dim 16*ni + r16 at tokens 8*gp .. 8*gp+7 of the tile
   // (16 contiguous bytes of the transposed block).
@@ -271,15 +296,18 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, i
   auto step = [&](MfmaK<D>& kt, MfmaV<D>& vt, int tile, int pf) {
     const int tt = t0 + 32 * tile;
     const bool more = pf < ntiles;
+    stage_k(kt);
+    if (more) load_k(kt, pf);  // the raw registers are free once staged
     f32x4 sacc[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
+      bf16x8 kop[NST];
+      k_operand(m, kop);
       sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < NST; ++st)
-        sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt.k[m][st], qop[st], sacc[m], 0, 0, 0);
+        sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], qop[st], sacc[m], 0, 0, 0);
     }
-    if (more) load_k(kt, pf);
 
     // lane (gp, r16): scores of head r16 for tokens tt + 8*gp + j, j = 4*m + i
     const int valid = t1 - (tt + 8 * gp);  // tokens of this lane's group that exist
@@ -351,7 +379,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, i
 }
 
 template <int D, int B>
-__global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(kMfmaWaves, kMfmaWaves)))
+__global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(kMfmaWaves)))
 void decode_mfma_kernel(DecodeArgs a) {
   __shared__ int s_tbl[kMaxPT / B];
   __shared__ int s_bad, s_next;

@@ -60,6 +60,16 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Chunk permutation for K tiles staged in LDS (rows of D bf16 = D/8 16-byte chunks): chunk c
+// of key row `key` is stored at chunk c ^ kswz(key).  The matrix-core operand read has 16
+// lanes read the same chunk of 16 keys that differ in bits 0-1 and 3-4; without the
+// permutation keys 16 apart land in the same LDS banks.  kswz maps those keys to distinct values.
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+  constexpr int kMask = D / 8 - 1;  // chunks per row - 1
+  return ((key & 3) | (((key >> 3) & 3) << 2)) & kMask;
+}
+
 // 2^x by the hardware instruction alone: exact at -inf (0), results below 2^-126 flush to 0
 // (harmless for softmax weights, which are summed against weights near 1).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -10,14 +10,15 @@ One step = the whole hot path for one batch:
   host  : pa_bm_append_slots (one token per sequence, copy-on-write decisions) and
           pa_bm_seq_lens into a pinned staging buffer;
   copy  : one async host->device upload of the step's slots and lengths (2 KB);
-  device: pa_copy_blocks (if any pairs) -> pa_cache_append (cache write + the block-table
-          entries the step created, on the device-resident tables) -> pa_decode (plan,
-          split-K decode, merge).
+  device: pa_copy_blocks (if any pairs) -> pa_decode_step: one launch for the cache write +
+          the block-table entries the step created (on the device-resident tables) together
+          with the decode planning, then the split-K decode and the merge.
 The block tables are uploaded once before the timed steps and from then on live on the device.
 
 Prints one JSON line.  ``value`` is the step's algorithmic HBM traffic divided by the step
-time (GB/s); tokens/s is the batch size over the step time.  ``roofline`` reports the decode
-call alone (plan + split-K kernel + merge), timed with HIP events on the stream it runs on.
+time (GB/s); tokens/s is the batch size over the step time.  ``roofline`` reports the
+pa_decode_step call (cache write + plan, split-K kernel, merge), timed with HIP events on the
+stream it runs on.
 """
 
 from __future__ import annotations
@@ -257,13 +258,12 @@ def run_decode(args, w, st, t_setup):
         used[r] = True
         if len(pairs):
             _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).to(dev))
-        _lib.pa_cache_append(st.vals["k_step"], st.vals["v_step"], st.k_cache, st.v_cache, slots_d,
-                             tables_d, lens_d)
         if timed:
             e0, e1 = ev_pool[len(dec_events)]
             e0.record(stream)
-        _lib.pa_decode(out, st.vals["q"], st.k_cache, st.v_cache, tables_d, lens_d, max_ctx,
-                       w.scale, args.partition, ws)
+        _lib.pa_decode_step(out, st.vals["q"], st.vals["k_step"], st.vals["v_step"], st.k_cache,
+                            st.v_cache, slots_d, tables_d, lens_d, max_ctx, w.scale,
+                            args.partition, ws)
         if timed:
             e1.record(stream)
             dec_events.append((e0, e1))
@@ -280,8 +280,9 @@ def run_decode(args, w, st, t_setup):
     ms_step = 1e3 * elapsed / args.steps
     dec_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_events]))
     dec_bytes, write_bytes = zip(*[algorithmic_bytes(l, w, S) for l in step_lens])
-    dec_bytes_avg = float(np.mean(dec_bytes))
-    step_bytes_avg = dec_bytes_avg + float(np.mean(write_bytes))
+    # the timed call is pa_decode_step: decode bytes plus the new tokens' cache write
+    dec_bytes_avg = float(np.mean(dec_bytes)) + float(np.mean(write_bytes))
+    step_bytes_avg = dec_bytes_avg
     tokens = int(np.mean([l.sum() for l in step_lens]))
     shared = args.workload.startswith("shared")
     extra = {}
@@ -316,7 +317,7 @@ def run_decode(args, w, st, t_setup):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if headline and args.pool == "churned" else None,
-                     "kernel": "pa_decode (plan + persistent split-K decode + merge)",
+                     "kernel": "pa_decode_step (cache write + plan, persistent split-K decode, merge)",
                      "avg_ms": round(dec_avg_ms, 4), "algorithmic_bytes": int(dec_bytes_avg)},
         "cpu_baseline": cpu,
         "setup_s": round(t_setup, 1),

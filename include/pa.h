@@ -262,6 +262,23 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t max_ctx_len, float scale, int32_t dtype, int32_t partition_tokens,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step of a serving loop on the device, fused: the cache write and block-table patch
+ * of pa_cache_append for one new token per sequence (tokens_each = 1), then pa_decode over the
+ * updated tables.  The decode's planning work runs in the same launch as the cache write (the
+ * two are independent), so the step costs one kernel launch fewer than pa_cache_append followed
+ * by pa_decode, with bit-identical results.
+ * key, value: device [S, Hkv, D] of dtype (the new tokens); slot_mapping: device int32 [S];
+ * block_tables: device int32 [S, max_blocks], updated in place; ctx_lens: device int32 [S],
+ * the lengths AFTER the step (including the new token).  q, out, the pools, max_ctx_len, scale,
+ * partition_tokens and the workspace are as in pa_decode (the size query is the same).  Errors
+ * as in pa_cache_append and pa_decode; nothing is launched when one is returned. */
+pa_status pa_decode_step(void* out, const void* q, const void* key, const void* value,
+                         void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                         int32_t* block_tables, const int32_t* ctx_lens, int32_t S, int32_t Hq,
+                         int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks, int32_t max_blocks,
+                         int32_t max_ctx_len, float scale, int32_t dtype, int32_t partition_tokens,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunked-query paged attention (prefill of the tokens past a cached prefix, [KC]
  * "RadixAttention": only the tokens past the divergence need a prefill pass).  Each of the S
  * sequences has ctx_lens[s] tokens in the pool INCLUDING its C new ones (already written by

@@ -102,6 +102,8 @@ _SIGS = {
     "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                    _f32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "pa_decode_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                        _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp], _i32),
     "pa_chunk_attend": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _vp], _i32),
 }
@@ -388,6 +390,32 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, max_ctx_len: int
                           _dev(ctx_lens, "ctx_lens", torch.int32), S, Hq, Hkv, D, B, NB,
                           block_tables.shape[1], max_ctx_len, float(scale), _dtype_code(q),
                           partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_decode_step(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
+                   max_ctx_len: int, scale: float, partition_tokens: int = 0, workspace=None,
+                   stream=None) -> None:
+    torch = _torch()
+    NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
+    S, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise PaError(PA_ERR_INVALID_ARG, "q/out must be [S, Hq, D] of the pools' dtype")
+    if tuple(key.shape) != (S, Hkv, D) or tuple(value.shape) != (S, Hkv, D) or \
+            key.dtype != k_cache.dtype or value.dtype != k_cache.dtype:
+        raise PaError(PA_ERR_INVALID_ARG, "key and value must be [S, Hkv, D] of the pools' dtype")
+    if tuple(slot_mapping.shape) != (S,):
+        raise PaError(PA_ERR_INVALID_ARG, "slot_mapping must be [S]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(ctx_lens.shape) != (S,):
+        raise PaError(PA_ERR_INVALID_ARG, "block_tables must be [S, max_blocks], ctx_lens [S]")
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                            workspace.numel() * workspace.element_size())
+    _check(_lib.pa_decode_step(_dev(out, "out"), _dev(q, "q"), _dev(key, "key"), _dev(value, "value"),
+                               _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                               _dev(slot_mapping, "slot_mapping", torch.int32),
+                               _dev(block_tables, "block_tables", torch.int32),
+                               _dev(ctx_lens, "ctx_lens", torch.int32), S, Hq, Hkv, D, B, NB,
+                               block_tables.shape[1], max_ctx_len, float(scale), _dtype_code(q),
+                               partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
 
 
 def pa_chunk_attend(out, q, k_cache, v_cache, block_tables, ctx_lens, scale: float,

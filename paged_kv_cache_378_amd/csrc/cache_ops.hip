@@ -1,61 +1,17 @@
 // Cache write (slot scatter) and copy-on-write block copy on gfx950.
 //
-// Cache write: "Taming the Tail", "The Hidden Tax" -- each step stores only the new token's
-// K/V; "vLLM PagedAttention" (tinycto), "1. Underlying Mechanism" -- a step writes the new
-// token's entries and nothing else.  Block copy: KV-cache chapter, "PagedAttention: borrowing virtual memory" -- a
-// writer into a shared block first gets a private copy.
-//
-// Both are pure bit copies and HBM-bound.  One thread moves one 16-byte chunk of a token's
-// key row (coalesced read, coalesced write into the K pool); the same thread scatters the
-// matching value chunk into the transposed V block (one element every B elements).
+// Cache write: the device function in cache_write.h.  Block copy: KV-cache chapter,
+// "PagedAttention: borrowing virtual memory" -- a writer into a shared block first gets a
+// private copy.  Both are pure bit copies and HBM-bound.
 
+#include "cache_write.h"
 #include "device_common.h"
 
 namespace pa {
 
-// Resident block table to patch (pa_cache_append); tables == nullptr for a plain cache write.
-struct TablePatch {
-  int32_t* tables;
-  const int32_t* ctx_lens;
-  int tokens_each, max_blocks;
-};
-
 template <typename T>
-__global__ __launch_bounds__(256) void cache_write_kernel(
-    const T* __restrict__ key, const T* __restrict__ value, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, const int32_t* __restrict__ slots, int64_t n_chunks, int Hkv,
-    int D, int B, int64_t n_slots, TablePatch tp) {
-  constexpr int VEC = 16 / sizeof(T);
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n_chunks) return;
-  const int per_row = D / VEC;
-  const int c = static_cast<int>(i % per_row);
-  const int64_t th = i / per_row;
-  const int h = static_cast<int>(th % Hkv);
-  const int64_t t = th / Hkv;
-  const int32_t slot = slots[t];
-  if (slot < 0 || slot >= n_slots) return;  // padding or out of the pool: not written
-  const int64_t p = slot / B;
-  const int o = slot % B;
-  if (tp.tables && c == 0 && h == 0) {
-    // The token's logical block now lives in physical block p.  Tokens of one sequence that
-    // share a block write the same value.
-    const int64_t r = t / tp.tokens_each;
-    const int64_t pos = static_cast<int64_t>(tp.ctx_lens[r]) - tp.tokens_each + t % tp.tokens_each;
-    if (pos >= 0 && pos < static_cast<int64_t>(tp.max_blocks) * B)
-      tp.tables[r * tp.max_blocks + pos / B] = static_cast<int32_t>(p);
-  }
-  const int64_t src = (t * Hkv + h) * D + static_cast<int64_t>(c) * VEC;
-
-  const uint4 kv = *reinterpret_cast<const uint4*>(key + src);
-  *reinterpret_cast<uint4*>(k_cache + ((p * Hkv + h) * B + o) * D + static_cast<int64_t>(c) * VEC) = kv;
-
-  const uint4 vv = *reinterpret_cast<const uint4*>(value + src);
-  T vals[VEC];
-  __builtin_memcpy(vals, &vv, 16);
-  T* dst = v_cache + ((p * Hkv + h) * D + static_cast<int64_t>(c) * VEC) * B + o;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) dst[static_cast<int64_t>(e) * B] = vals[e];
+__global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(CacheWriteArgs a) {
+  cache_write_chunk<T>(a, static_cast<int64_t>(blockIdx.x) * kWriteThreads + threadIdx.x);
 }
 
 // One workgroup per pair; each copies the whole block (all kv-heads and slots) of both pools.
@@ -93,21 +49,14 @@ static pa_status launch_cache_write(const char* who, const void* key, const void
                                     int32_t T, int32_t Hkv, int32_t D, int32_t B,
                                     int32_t num_blocks, int32_t dtype, const TablePatch& tp,
                                     void* stream) {
-  const int eb = elem_bytes(dtype);
-  const int64_t n_chunks = static_cast<int64_t>(T) * Hkv * (D * eb / 16);
-  const int64_t n_slots = static_cast<int64_t>(num_blocks) * B;
-  const dim3 grid(static_cast<unsigned>((n_chunks + 255) / 256));
+  const CacheWriteArgs w = make_cache_write_args(key, value, k_cache, v_cache, slot_mapping, T,
+                                                 Hkv, D, B, num_blocks, dtype, tp);
+  const dim3 grid(static_cast<unsigned>((w.n_chunks + kWriteThreads - 1) / kWriteThreads));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == PA_DTYPE_F32)
-    hipLaunchKernelGGL(cache_write_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(key), static_cast<const float*>(value),
-                       static_cast<float*>(k_cache), static_cast<float*>(v_cache), slot_mapping,
-                       n_chunks, Hkv, D, B, n_slots, tp);
+    hipLaunchKernelGGL(cache_write_kernel<float>, grid, dim3(kWriteThreads), 0, s, w);
   else
-    hipLaunchKernelGGL(cache_write_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
-                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-                       slot_mapping, n_chunks, Hkv, D, B, n_slots, tp);
+    hipLaunchKernelGGL(cache_write_kernel<uint16_t>, grid, dim3(kWriteThreads), 0, s, w);
   return launch_status(who);
 }
 

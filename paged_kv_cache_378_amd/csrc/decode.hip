@@ -46,6 +46,7 @@
 #include <mutex>
 #include <utility>
 
+#include "cache_write.h"
 #include "device_common.h"
 
 namespace pa {
@@ -627,7 +628,7 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int grid) {
+__device__ void plan_body(const DecodeArgs& a, int grid) {
   constexpr int kPlanWaves = kPlanThreads / kWave;
   __shared__ int s_cnt[kMaxBuckets];   // partial partitions per bucket
   __shared__ int s_base[kMaxBuckets];  // first entry of each bucket (then a cursor)
@@ -678,6 +679,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int gr
     const int full = n / a.PT, rem = n - full * a.PT;
     if (rem > 0 || n == 0) a.items[atomicAdd(&s_base[(rem + 31) / 32], 1)] = make_int2(s, full);
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int grid) {
+  plan_body(a, grid);
+}
+
+// The prologue of a fused serving step: the step's cache write (and table patch) and the
+// decode planning are independent, so one launch does both -- the last workgroup plans, the
+// others scatter the new tokens.
+static_assert(kPlanThreads == kWriteThreads, "one block size for both halves of the prologue");
+
+template <typename T>
+__global__ __launch_bounds__(kPlanThreads) void step_prologue_kernel(CacheWriteArgs w,
+                                                                     DecodeArgs a, int grid) {
+  if (blockIdx.x == gridDim.x - 1) {
+    plan_body(a, grid);
+    return;
+  }
+  cache_write_chunk<T>(w, static_cast<int64_t>(blockIdx.x) * kWriteThreads + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -760,10 +780,12 @@ static KernelFn pick_valu(int32_t dtype, int G) {
 }
 
 // Picks the kernel, the partition length and the grid, lays out the workspace and launches
-// plan -> decode -> merge on `stream`.
+// plan -> decode -> merge on `stream`.  With a cache write (`wr`, pa_decode_step) the plan
+// shares its launch with the write.
 template <int D, int B>
 static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void* workspace,
-                        size_t workspace_bytes_in, hipStream_t stream) {
+                        size_t workspace_bytes_in, hipStream_t stream,
+                        const CacheWriteArgs* wr = nullptr) {
   KernelFn k = nullptr;
   if (dtype == PA_DTYPE_BF16 && a.G >= 3 && a.G <= 16)
     k = decode_mfma_kernel<D, B>;
@@ -790,8 +812,17 @@ static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void*
 
   const int64_t max_items = static_cast<int64_t>(a.S) * a.Pmax * a.Hkv;
   const int grid = static_cast<int>(max_items < cap ? max_items : cap);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, grid);
-  if (pa_status st = launch_status("pa_decode (plan)")) return st;
+  if (wr) {
+    const unsigned nw = static_cast<unsigned>((wr->n_chunks + kWriteThreads - 1) / kWriteThreads);
+    if (dtype == PA_DTYPE_F32)
+      hipLaunchKernelGGL(step_prologue_kernel<float>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, *wr, a, grid);
+    else
+      hipLaunchKernelGGL(step_prologue_kernel<uint16_t>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, *wr, a, grid);
+    if (pa_status st = launch_status("pa_decode_step (cache write + plan)")) return st;
+  } else {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, grid);
+    if (pa_status st = launch_status("pa_decode (plan)")) return st;
+  }
   hipLaunchKernelGGL(k, dim3(grid), dim3(kNW * kWave), 0, stream, a);
   if (pa_status st = launch_status("pa_decode")) return st;
   if (a.Pmax > 1) {
@@ -824,33 +855,48 @@ extern "C" pa_status pa_decode_workspace_size(int32_t S, int32_t Hq, int32_t D, 
   return ok();
 }
 
-extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, const int32_t* ctx_lens, int32_t S,
-                               int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
-                               int32_t max_blocks, int32_t max_ctx_len, float scale, int32_t dtype,
-                               int32_t partition_tokens, void* workspace, size_t workspace_bytes_in,
-                               void* stream) {
-  if (elem_bytes(dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype %d", dtype);
-  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d not in {64, 128}", D);
-  if (B != 16 && B != 32) return fail(PA_ERR_UNSUPPORTED, "pa_decode: block size %d not in {16, 32}", B);
+// Argument checks and DecodeArgs of pa_decode / pa_decode_step (everything visible on the host
+// is validated before any device work).
+static pa_status decode_setup(const char* who, void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* ctx_lens, int32_t S, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t B, int32_t num_blocks, int32_t max_blocks,
+                              int32_t max_ctx_len, float scale, int32_t dtype,
+                              int32_t partition_tokens, void* workspace, size_t workspace_bytes_in,
+                              DecodeArgs* out_args) {
+  if (elem_bytes(dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", who, dtype);
+  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", who, D);
+  if (B != 16 && B != 32) return fail(PA_ERR_UNSUPPORTED, "%s: block size %d not in {16, 32}", who, B);
   if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: S %d, Hq %d, Hkv %d (Hq must be a multiple of Hkv)", S, Hq, Hkv);
-  if (S > 65535 || Hkv > 65535) return fail(PA_ERR_INVALID_ARG, "pa_decode: S and Hkv must be <= 65535");
+    return fail(PA_ERR_INVALID_ARG, "%s: S %d, Hq %d, Hkv %d (Hq must be a multiple of Hkv)", who, S, Hq, Hkv);
+  if (S > 65535 || Hkv > 65535) return fail(PA_ERR_INVALID_ARG, "%s: S and Hkv must be <= 65535", who);
   if (num_blocks <= 0 || max_blocks <= 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: num_blocks %d, max_blocks %d", num_blocks, max_blocks);
+    return fail(PA_ERR_INVALID_ARG, "%s: num_blocks %d, max_blocks %d", who, num_blocks, max_blocks);
   if (max_ctx_len < 1 || static_cast<int64_t>(max_ctx_len) > static_cast<int64_t>(max_blocks) * B)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: max_ctx_len %d outside [1, max_blocks*B]", max_ctx_len);
+    return fail(PA_ERR_INVALID_ARG, "%s: max_ctx_len %d outside [1, max_blocks*B]", who, max_ctx_len);
   if (partition_tokens != 0 && (partition_tokens % 32 || partition_tokens < 32 || partition_tokens > kMaxPT))
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: partition_tokens %d is not a multiple of 32 in [32, %d]",
-                partition_tokens, kMaxPT);
-  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "pa_decode: scale is NaN");
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_tokens %d is not a multiple of 32 in [32, %d]",
+                who, partition_tokens, kMaxPT);
+  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is NaN", who);
   if (S == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: NULL pointer");
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: q, out and the pools must be 16-byte aligned");
+    return fail(PA_ERR_INVALID_ARG, "%s: q, out and the pools must be 16-byte aligned", who);
+  // The workspace must hold the layout for the shortest partition this call may pick (the
+  // size pa_decode_workspace_size reports), checked before anything touches the device.
+  const int pt_min = partition_tokens ? partition_tokens : kMinAutoPT;
+  const int pmax_min = (max_ctx_len + pt_min - 1) / pt_min;
+  if (static_cast<int64_t>(S) * pmax_min * Hq >= (int64_t(1) << 31))
+    return fail(PA_ERR_INVALID_ARG, "%s: S * partitions * Hq too large", who);
+  const size_t need = ws_layout(S, Hq, D, pmax_min).total;
+  if (!workspace || workspace_bytes_in < need)
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                workspace ? workspace_bytes_in : size_t(0));
+  if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", who);
 
-  DecodeArgs a{};
+  DecodeArgs& a = *out_args;
+  a = DecodeArgs{};
   a.out = out;
   a.q = q;
   a.kc = k_cache;
@@ -865,23 +911,50 @@ extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, co
   a.num_blocks = num_blocks;
   a.len_cap = max_ctx_len;  // validated above: max_ctx_len <= max_blocks * B
   a.scale_log2 = scale * kLog2e;
-  // The workspace must hold the layout for the shortest partition this call may pick (the
-  // size pa_decode_workspace_size reports), checked before anything touches the device.
-  {
-    const int pt_min = partition_tokens ? partition_tokens : kMinAutoPT;
-    const int pmax_min = (max_ctx_len + pt_min - 1) / pt_min;
-    if (static_cast<int64_t>(S) * pmax_min * Hq >= (int64_t(1) << 31))
-      return fail(PA_ERR_INVALID_ARG, "pa_decode: S * partitions * Hq too large");
-    const size_t need = ws_layout(S, Hq, D, pmax_min).total;
-    if (!workspace || workspace_bytes_in < need)
-      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given", need,
-                  workspace ? workspace_bytes_in : size_t(0));
-    if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace must be 16-byte aligned");
-  }
+  return ok();
+}
+
+static pa_status dispatch(const DecodeArgs& a, int D, int B, int32_t dtype, int pt, void* w,
+                          size_t wb, void* stream, const CacheWriteArgs* wr) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int pt = partition_tokens;
-  void* w = workspace;
-  const size_t wb = workspace_bytes_in;
-  if (D == 64) return B == 16 ? launch<64, 16>(a, dtype, pt, w, wb, st) : launch<64, 32>(a, dtype, pt, w, wb, st);
-  return B == 16 ? launch<128, 16>(a, dtype, pt, w, wb, st) : launch<128, 32>(a, dtype, pt, w, wb, st);
+  if (D == 64)
+    return B == 16 ? launch<64, 16>(a, dtype, pt, w, wb, st, wr) : launch<64, 32>(a, dtype, pt, w, wb, st, wr);
+  return B == 16 ? launch<128, 16>(a, dtype, pt, w, wb, st, wr) : launch<128, 32>(a, dtype, pt, w, wb, st, wr);
+}
+
+extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* ctx_lens, int32_t S,
+                               int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+                               int32_t max_blocks, int32_t max_ctx_len, float scale, int32_t dtype,
+                               int32_t partition_tokens, void* workspace, size_t workspace_bytes_in,
+                               void* stream) {
+  DecodeArgs a;
+  if (pa_status st = decode_setup("pa_decode", out, q, k_cache, v_cache, block_tables, ctx_lens, S,
+                                  Hq, Hkv, D, B, num_blocks, max_blocks, max_ctx_len, scale, dtype,
+                                  partition_tokens, workspace, workspace_bytes_in, &a))
+    return st;
+  if (S == 0) return ok();
+  return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, nullptr);
+}
+
+extern "C" pa_status pa_decode_step(void* out, const void* q, const void* key, const void* value,
+                                    void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                    int32_t* block_tables, const int32_t* ctx_lens, int32_t S,
+                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                    int32_t num_blocks, int32_t max_blocks, int32_t max_ctx_len,
+                                    float scale, int32_t dtype, int32_t partition_tokens,
+                                    void* workspace, size_t workspace_bytes_in, void* stream) {
+  DecodeArgs a;
+  if (pa_status st = decode_setup("pa_decode_step", out, q, k_cache, v_cache, block_tables, ctx_lens,
+                                  S, Hq, Hkv, D, B, num_blocks, max_blocks, max_ctx_len, scale,
+                                  dtype, partition_tokens, workspace, workspace_bytes_in, &a))
+    return st;
+  if (S == 0) return ok();
+  if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "pa_decode_step: NULL pointer");
+  if (!aligned16(key) || !aligned16(value))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_step: key and value must be 16-byte aligned");
+  const CacheWriteArgs wr = make_cache_write_args(key, value, k_cache, v_cache, slot_mapping, S, Hkv,
+                                                  D, B, num_blocks, dtype,
+                                                  TablePatch{block_tables, ctx_lens, 1, max_blocks});
+  return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, &wr);
 }

@@ -108,3 +108,59 @@ def test_append_keeps_tables_and_pool_exact(gpu, name):
     mt, ml = model.block_tables(ids, max_blocks)
     want = att.paged_decode(q.double().cpu().numpy(), kf, vf, np.array(mt), ml, B, w.scale)
     check(out.double().cpu().numpy(), want, w.dtype, name)
+
+
+STEP_CASES = {
+    "llama_churn": lambda: wl.llama70b(S=16, churn_steps=1500, max_len=600),
+    "shared_prefix_cow": lambda: wl.shared_prefix(B=16, n_seqs=12, prefix=100, n_families=4,
+                                                  suffix_range=(1, 60)),
+    "fp32_g1": lambda: wl.custom_decode("stepf32", 43, [1, 15, 16, 17, 300], 4, 4, 64, 16, "f32",
+                                        extra_blocks=10),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP_CASES))
+def test_fused_step_equals_append_then_decode(gpu, name):
+    """pa_decode_step (cache write + plan in one launch, then decode) gives bit-identical
+    outputs, pools and tables to pa_cache_append followed by pa_decode, step after step."""
+    from paged_kv_cache_378_amd import _lib
+    from paged_kv_cache_378_amd.runner import PagedState
+    w = STEP_CASES[name]()
+    print(f"[gpu] fused step {name}: S={w.num_seqs} B={w.block_size} {w.dtype}", flush=True)
+    n_steps = 6
+    sa = PagedState(w, "cuda", poison=True)   # two-call path
+    sb = PagedState(w, "cuda", poison=True)   # fused path
+    S, B = w.num_seqs, w.block_size
+    ids = w.step_ids
+    max_ctx = max(w.ctx_lens()) + n_steps
+    max_blocks = (max_ctx + B - 1) // B
+    ta, la = (torch.from_numpy(x).cuda() for x in sa.bm.block_tables(ids, max_blocks))
+    tb, lb = (torch.from_numpy(x).cuda() for x in sb.bm.block_tables(ids, max_blocks))
+    nbytes = _lib.pa_decode_workspace_size(S, w.hq, w.head_dim, max_ctx, 0)
+    wsa = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    it = torch.int16 if w.dtype == "bf16" else torch.int32
+    for step in range(n_steps):
+        kn, vn = (x.cuda() for x in step_values(w, step, S))
+        outs = []
+        for st, t, l, ws, fused in ((sa, ta, la, wsa, False), (sb, tb, lb, wsb, True)):
+            slots, pairs = st.bm.append_slots(ids, 1)
+            l.copy_(torch.from_numpy(st.bm.seq_lens(ids)))
+            if len(pairs):
+                _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).cuda())
+            sl = torch.from_numpy(slots).cuda()
+            out = st.new_out()
+            if fused:
+                _lib.pa_decode_step(out, st.vals["q"], kn, vn, st.k_cache, st.v_cache, sl, t, l,
+                                    max_ctx, w.scale, 0, ws)
+            else:
+                _lib.pa_cache_append(kn, vn, st.k_cache, st.v_cache, sl, t, l)
+                _lib.pa_decode(out, st.vals["q"], st.k_cache, st.v_cache, t, l, max_ctx, w.scale,
+                               0, ws)
+            outs.append(out)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0].view(it), outs[1].view(it)), f"step {step}"
+        assert torch.equal(ta, tb) and torch.equal(la, lb)
+        assert torch.isfinite(outs[1].float()).all()
+    assert torch.equal(sa.k_cache.view(it), sb.k_cache.view(it))
+    assert torch.equal(sa.v_cache.view(it), sb.v_cache.view(it))

@@ -8,17 +8,18 @@ values (N(0,1) rounded to bf16).
 
 One step = the whole hot path for one batch:
   host  : pa_bm_append_slots (one token per sequence, copy-on-write decisions) and
-          pa_bm_seq_lens into a pinned staging buffer;
-  copy  : one async host->device upload of the step's slots and lengths (2 KB);
-  device: pa_copy_blocks (if any pairs) -> pa_decode_step: one launch for the cache write +
-          the block-table entries the step created (on the device-resident tables) together
-          with the decode planning, then the split-K decode and the merge.
+          pa_bm_seq_lens into pinned host buffers (2 KB);
+  device: pa_copy_blocks (if any pairs) -> pa_decode_step: one launch that reads the pinned
+          slots and lengths directly and does the cache write + the block-table entries the
+          step created (on the device-resident tables) together with the decode planning,
+          then the split-K decode and the merge.
 The block tables are uploaded once before the timed steps and from then on live on the device.
 
 Prints one JSON line.  ``value`` is the step's algorithmic HBM traffic divided by the step
 time (GB/s); tokens/s is the batch size over the step time.  ``roofline`` reports the
-pa_decode_step call (cache write + plan, split-K kernel, merge), timed with HIP events on the
-stream it runs on.
+pa_decode_step call (cache write + plan, split-K kernel, merge): HIP events on the stream it runs
+on bracket the timed region, and the region's time over the steps is the call's average
+duration.
 """
 
 from __future__ import annotations
@@ -38,11 +39,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_llama70b_b256.md")
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_step_llama70b_b256.md")
 
 
 def measured_traffic():
-    """HBM bytes per pa_decode call from the committed rocprofv3 counter summary (FETCH_SIZE and
+    """HBM bytes per pa_decode_step call from the committed rocprofv3 counter summary (FETCH_SIZE and
     WRITE_SIZE passes, scaled by a plain copy of known size), or None when the summary is
     missing or was taken on kernel sources other than the current ones."""
     import hashlib
@@ -64,7 +65,7 @@ def measured_traffic():
 
 
 def algorithmic_bytes(lens, w, T, with_write=True):
-    """Bytes the decode step must move (SURVEY-style accounting, exact token counts):
+    """Bytes the decode step must move (exact token counts):
     K and V of every context token, q and out, table entries in use and lengths, and the
     cache write of the T new tokens (read + write)."""
     elt = 2 if w.dtype == "bf16" else 4
@@ -182,20 +183,25 @@ def main() -> int:
 def timed_loop(args, step):
     """Warm-up, then exactly args.steps timed steps between two device synchronisations, with
     the set-up's Python objects frozen and the cyclic GC off (a collection over the workload
-    script once stalled one step for tens of milliseconds)."""
+    script once stalled one step for tens of milliseconds).  Returns the wall-clock seconds of
+    the timed steps and the milliseconds between two HIP events recorded on the launch stream
+    at the start and the end of the timed region."""
     import torch
     gc.collect()
     gc.freeze()
     gc.disable()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     try:
         for i in range(args.warmup):
             step(i, False)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        ev0.record()
         for i in range(args.warmup, args.warmup + args.steps):
             step(i, True)
+        ev1.record()
         torch.cuda.synchronize()
-        return time.perf_counter() - t0
+        return time.perf_counter() - t0, ev0.elapsed_time(ev1)
     finally:
         gc.enable()
 
@@ -208,8 +214,8 @@ def base_line(args, w, ms_step):
 
 
 def run_decode(args, w, st, t_setup):
-    """One decode step of the whole path per iteration (host block manager, 2 KiB upload,
-    copy-on-write copies, cache write + table patch, plan + split-K decode + merge)."""
+    """One decode step of the whole path per iteration (host block manager, copy-on-write
+    copies, cache write + table patch, plan + split-K decode + merge)."""
     import torch
 
     from paged_kv_cache_378_amd import _lib
@@ -224,61 +230,58 @@ def run_decode(args, w, st, t_setup):
     out = st.new_out()
     ids = np.asarray(w.step_ids, np.int64)
 
-    # Block tables and lengths live on the device; each step uploads only [slots | lens] from a
-    # ring of pinned staging buffers, so the host waits only on an event recorded RING steps
-    # earlier (long complete), never on the step just enqueued.
+    # Block tables and lengths live on the device.  Each step's slots and lengths (2 KB) are
+    # written into a ring of pinned host buffers that pa_decode_step's first kernel reads
+    # directly, so there is no upload.  A buffer is rewritten RING steps after its last use; the
+    # host checks that use is over on an event recorded once every MARK steps (long complete by
+    # then), never on the step just enqueued.
     tables0, lens0 = st.bm.block_tables(ids, max_blocks)
     tables_d = torch.from_numpy(tables0).to(dev)
-    RING = 4
-    pin = [torch.empty(2 * S, dtype=torch.int32).pin_memory() for _ in range(RING)]
-    done = [torch.cuda.Event() for _ in range(RING)]
-    used = [False] * RING
-    meta_d = torch.empty(2 * S, dtype=torch.int32, device=dev)
-    slots_d, lens_d = meta_d[:S], meta_d[S:2 * S]
-    lens_d.copy_(torch.from_numpy(lens0))
+    lens_d = torch.from_numpy(lens0).to(dev)
+    RING, MARK = 16, 8
+    pin_slots = [torch.empty(S, dtype=torch.int32).pin_memory() for _ in range(RING)]
+    pin_lens = [torch.empty(S, dtype=torch.int32).pin_memory() for _ in range(RING)]
+    marks = [torch.cuda.Event() for _ in range(4)]
     stream = torch.cuda.current_stream()
-    ev_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    host_s, dec_events, step_lens, n_pairs = [], [], [], []
+    host_s, step_lens, n_pairs = [], [], []
 
     def step(i, timed):
         r = i % RING
-        if used[r]:
-            done[r].synchronize()
-        buf = pin[r].numpy()
+        if i >= RING:
+            # step i - RING read buffer r; the mark of its group of MARK steps was recorded
+            # after step i - RING + MARK - 1 < i at the latest, and is not yet re-recorded
+            marks[((i - RING) // MARK) % len(marks)].synchronize()
+        slots_h, lens_h = pin_slots[r], pin_lens[r]
         h0 = time.perf_counter()
         slots, pairs = st.bm.append_slots(ids, 1)
-        buf[:S] = slots
-        st.bm.seq_lens(ids, buf[S:])
+        slots_h.numpy()[:] = slots
+        st.bm.seq_lens(ids, lens_h.numpy())
         n_pairs.append(len(pairs))
         if timed:
             host_s.append(time.perf_counter() - h0)
-        meta_d.copy_(pin[r], non_blocking=True)
-        done[r].record(stream)
-        used[r] = True
+            step_lens.append(lens_h.numpy().copy())
         if len(pairs):
             _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).to(dev))
-        if timed:
-            e0, e1 = ev_pool[len(dec_events)]
-            e0.record(stream)
         _lib.pa_decode_step(out, st.vals["q"], st.vals["k_step"], st.vals["v_step"], st.k_cache,
-                            st.v_cache, slots_d, tables_d, lens_d, max_ctx, w.scale,
-                            args.partition, ws)
-        if timed:
-            e1.record(stream)
-            dec_events.append((e0, e1))
-            step_lens.append(buf[S:].copy())
+                            st.v_cache, slots_h, tables_d, lens_d, max_ctx, w.scale,
+                            args.partition, ws, new_ctx_lens=lens_h)
+        if i % MARK == MARK - 1:
+            marks[(i // MARK) % len(marks)].record(stream)
 
-    elapsed = timed_loop(args, step)
+    elapsed, region_ms = timed_loop(args, step)
     if not torch.isfinite(out.float()).all():
         return {"error": "non-finite decode output"}
-    # the device-resident tables must still mirror the block manager's exactly
+    # the device-resident tables and lengths must still mirror the block manager's exactly
     final_tables, final_lens = st.bm.block_tables(ids, max_blocks)
-    if not np.array_equal(tables_d.cpu().numpy(), final_tables):
+    if not np.array_equal(tables_d.cpu().numpy(), final_tables) or \
+            not np.array_equal(lens_d.cpu().numpy(), final_lens):
         return {"error": "device block tables diverged from the block manager"}
 
     ms_step = 1e3 * elapsed / args.steps
-    dec_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_events]))
+    # Each step puts one pa_decode_step call on the stream (plus pa_copy_blocks where a step
+    # has copy-on-write pairs), so the event time of the region over the steps is the call's
+    # average duration, launch gaps between calls included.
+    dec_avg_ms = region_ms / args.steps
     dec_bytes, write_bytes = zip(*[algorithmic_bytes(l, w, S) for l in step_lens])
     # the timed call is pa_decode_step: decode bytes plus the new tokens' cache write
     dec_bytes_avg = float(np.mean(dec_bytes)) + float(np.mean(write_bytes))
@@ -317,7 +320,8 @@ def run_decode(args, w, st, t_setup):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if headline and args.pool == "churned" else None,
-                     "kernel": "pa_decode_step (cache write + plan, persistent split-K decode, merge)",
+                     "kernel": "pa_decode_step (cache write + plan, persistent split-K decode, "
+                               "merge); avg_ms = HIP-event time of the timed region / steps",
                      "avg_ms": round(dec_avg_ms, 4), "algorithmic_bytes": int(dec_bytes_avg)},
         "cpu_baseline": cpu,
         "setup_s": round(t_setup, 1),
@@ -370,7 +374,7 @@ def run_chunk(args, w, st, t_setup):
             e1.record(stream)
             events.append((e0, e1))
 
-    elapsed = timed_loop(args, step)
+    elapsed, _ = timed_loop(args, step)
     if not torch.isfinite(out.float()).all():
         return {"error": "non-finite chunk output"}
     if not np.array_equal(tables_d.cpu().numpy(), st.bm.block_tables(ids, max_blocks)[0]):

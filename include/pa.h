@@ -267,17 +267,26 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * updated tables.  The decode's planning work runs in the same launch as the cache write (the
  * two are independent), so the step costs one kernel launch fewer than pa_cache_append followed
  * by pa_decode, with bit-identical results.
- * key, value: device [S, Hkv, D] of dtype (the new tokens); slot_mapping: device int32 [S];
- * block_tables: device int32 [S, max_blocks], updated in place; ctx_lens: device int32 [S],
- * the lengths AFTER the step (including the new token).  q, out, the pools, max_ctx_len, scale,
- * partition_tokens and the workspace are as in pa_decode (the size query is the same).  Errors
- * as in pa_cache_append and pa_decode; nothing is launched when one is returned. */
+ * key, value: device [S, Hkv, D] of dtype (the new tokens).
+ * slot_mapping: int32 [S], the new tokens' slots.  block_tables: device int32 [S, max_blocks],
+ * updated in place.  ctx_lens: device int32 [S], the lengths the decode reads.
+ * new_ctx_lens: int32 [S], the lengths AFTER the step (including the new token), or NULL when
+ * ctx_lens already holds them; when given, the step copies them into ctx_lens.
+ * slot_mapping and new_ctx_lens may each be device memory or page-locked host memory
+ * (hipHostMalloc, a pinned torch tensor): the step's first kernel reads host memory directly,
+ * so a serving loop needs no separate upload of its per-step metadata.  Such a host buffer
+ * must not be rewritten before the step has completed on the stream.
+ * q, out, the pools, max_ctx_len, scale, partition_tokens and the workspace are as in
+ * pa_decode (the size query is the same).  Errors as in pa_cache_append and pa_decode, and
+ * PA_ERR_INVALID_ARG when slot_mapping or new_ctx_lens is pageable host memory; nothing is
+ * launched when one is returned. */
 pa_status pa_decode_step(void* out, const void* q, const void* key, const void* value,
                          void* k_cache, void* v_cache, const int32_t* slot_mapping,
-                         int32_t* block_tables, const int32_t* ctx_lens, int32_t S, int32_t Hq,
-                         int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks, int32_t max_blocks,
-                         int32_t max_ctx_len, float scale, int32_t dtype, int32_t partition_tokens,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         int32_t* block_tables, int32_t* ctx_lens, const int32_t* new_ctx_lens,
+                         int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                         int32_t num_blocks, int32_t max_blocks, int32_t max_ctx_len, float scale,
+                         int32_t dtype, int32_t partition_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Chunked-query paged attention (prefill of the tokens past a cached prefix, [KC]
  * "RadixAttention": only the tokens past the divergence need a prefill pass).  Each of the S

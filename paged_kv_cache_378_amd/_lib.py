@@ -102,7 +102,7 @@ _SIGS = {
     "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                    _f32, _i32, _i32, _vp, _sz, _vp], _i32),
-    "pa_decode_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+    "pa_decode_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                         _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp], _i32),
     "pa_chunk_attend": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _vp], _i32),
@@ -392,9 +392,23 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, max_ctx_len: int
                           partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
 
 
+def _step_input(t, what: str):
+    """Device tensor, or a pinned host tensor (the library reads page-locked memory directly)."""
+    torch = _torch()
+    if not t.is_cuda and not t.is_pinned():
+        raise PaError(PA_ERR_INVALID_ARG, f"{what} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise PaError(PA_ERR_INVALID_ARG, f"{what} must be contiguous")
+    if t.dtype != torch.int32:
+        raise PaError(PA_ERR_INVALID_ARG, f"{what} must be {torch.int32}, got {t.dtype}")
+    return t.data_ptr()
+
+
 def pa_decode_step(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
                    max_ctx_len: int, scale: float, partition_tokens: int = 0, workspace=None,
-                   stream=None) -> None:
+                   stream=None, new_ctx_lens=None) -> None:
+    """slot_mapping and new_ctx_lens may be device tensors or pinned host tensors; with
+    new_ctx_lens given, the step copies them into ctx_lens (a device tensor) before decoding."""
     torch = _torch()
     NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
     S, Hq, Dq = q.shape
@@ -407,15 +421,18 @@ def pa_decode_step(out, q, key, value, k_cache, v_cache, slot_mapping, block_tab
         raise PaError(PA_ERR_INVALID_ARG, "slot_mapping must be [S]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(ctx_lens.shape) != (S,):
         raise PaError(PA_ERR_INVALID_ARG, "block_tables must be [S, max_blocks], ctx_lens [S]")
+    if new_ctx_lens is not None and tuple(new_ctx_lens.shape) != (S,):
+        raise PaError(PA_ERR_INVALID_ARG, "new_ctx_lens must be [S]")
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (_dev(workspace, "workspace"),
                                                             workspace.numel() * workspace.element_size())
+    new_ptr = None if new_ctx_lens is None else _step_input(new_ctx_lens, "new_ctx_lens")
     _check(_lib.pa_decode_step(_dev(out, "out"), _dev(q, "q"), _dev(key, "key"), _dev(value, "value"),
                                _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                               _dev(slot_mapping, "slot_mapping", torch.int32),
+                               _step_input(slot_mapping, "slot_mapping"),
                                _dev(block_tables, "block_tables", torch.int32),
-                               _dev(ctx_lens, "ctx_lens", torch.int32), S, Hq, Hkv, D, B, NB,
-                               block_tables.shape[1], max_ctx_len, float(scale), _dtype_code(q),
-                               partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
+                               _dev(ctx_lens, "ctx_lens", torch.int32), new_ptr, S, Hq, Hkv, D, B,
+                               NB, block_tables.shape[1], max_ctx_len, float(scale),
+                               _dtype_code(q), partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
 
 
 def pa_chunk_attend(out, q, k_cache, v_cache, block_tables, ctx_lens, scale: float,

@@ -20,6 +20,13 @@ struct TablePatch {
   int tokens_each, max_blocks;
 };
 
+// Reads a step's slot or length.  With `sys` set the value may live in page-locked host memory
+// that the host rewrites between launches: a system-scope load fetches it past the GPU caches,
+// so a line cached by an earlier launch is never reused.
+__device__ __forceinline__ int32_t ld_step(const int32_t* p, bool sys) {
+  return sys ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : *p;
+}
+
 struct CacheWriteArgs {
   const void* key;
   const void* value;
@@ -30,6 +37,7 @@ struct CacheWriteArgs {
   int Hkv, D, B;
   int64_t n_slots;   // num_blocks * B
   TablePatch tp;
+  bool sys;          // slots / tp.ctx_lens may be page-locked host memory (see ld_step)
 };
 
 constexpr int kWriteThreads = 256;
@@ -44,29 +52,33 @@ __device__ __forceinline__ void cache_write_chunk(const CacheWriteArgs& a, int64
   const int64_t th = i / per_row;
   const int h = static_cast<int>(th % Hkv);
   const int64_t t = th / Hkv;
-  const int32_t slot = a.slots[t];
-  if (slot < 0 || slot >= a.n_slots) return;  // padding or out of the pool: not written
-  const int64_t p = slot / B;
-  const int o = slot % B;
-  const TablePatch& tp = a.tp;
-  if (tp.tables && c == 0 && h == 0) {
-    // The token's logical block now lives in physical block p.  Tokens of one sequence that
-    // share a block write the same value.
-    const int64_t r = t / tp.tokens_each;
-    const int64_t pos = static_cast<int64_t>(tp.ctx_lens[r]) - tp.tokens_each + t % tp.tokens_each;
-    if (pos >= 0 && pos < static_cast<int64_t>(tp.max_blocks) * B)
-      tp.tables[r * tp.max_blocks + pos / B] = static_cast<int32_t>(p);
-  }
   const int64_t src = (t * Hkv + h) * D + static_cast<int64_t>(c) * VEC;
   const T* key = static_cast<const T*>(a.key);
   const T* value = static_cast<const T*>(a.value);
   T* k_cache = static_cast<T*>(a.k_cache);
   T* v_cache = static_cast<T*>(a.v_cache);
-
+  // The token's data, its slot and (for the table patch) its sequence's length are all
+  // requested before any of them is used: with the slots and lengths in host memory the
+  // step pays one round trip over the bus, not two.
   const uint4 kv = *reinterpret_cast<const uint4*>(key + src);
+  const uint4 vv = *reinterpret_cast<const uint4*>(value + src);
+  const TablePatch& tp = a.tp;
+  const bool patch = tp.tables && c == 0 && h == 0;
+  const int64_t r = t / tp.tokens_each;
+  const int32_t slot = ld_step(a.slots + t, a.sys);
+  const int32_t len = patch ? ld_step(tp.ctx_lens + r, a.sys) : 0;
+  if (slot < 0 || slot >= a.n_slots) return;  // padding or out of the pool: not written
+  const int64_t p = slot / B;
+  const int o = slot % B;
+  if (patch) {
+    // The token's logical block now lives in physical block p.  Tokens of one sequence that
+    // share a block write the same value.
+    const int64_t pos = static_cast<int64_t>(len) - tp.tokens_each + t % tp.tokens_each;
+    if (pos >= 0 && pos < static_cast<int64_t>(tp.max_blocks) * B)
+      tp.tables[r * tp.max_blocks + pos / B] = static_cast<int32_t>(p);
+  }
   *reinterpret_cast<uint4*>(k_cache + ((p * Hkv + h) * B + o) * D + static_cast<int64_t>(c) * VEC) = kv;
 
-  const uint4 vv = *reinterpret_cast<const uint4*>(value + src);
   T vals[VEC];
   __builtin_memcpy(vals, &vv, 16);
   T* dst = v_cache + ((p * Hkv + h) * D + static_cast<int64_t>(c) * VEC) * B + o;

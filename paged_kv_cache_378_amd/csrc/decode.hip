@@ -56,6 +56,7 @@ constexpr int kMaxPT = 8192;      // largest partition (tokens)
 constexpr int kMinAutoPT = 256;   // smallest partition the automatic choice uses
 constexpr int kPlanThreads = 256;
 constexpr int kMaxBuckets = kMaxPT / 32 + 1;  // partial partitions bucketed by 32-token tiles
+constexpr int kPlanKeep = 2048;  // sequences whose lengths the plan keeps in LDS between passes
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
@@ -628,12 +629,16 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
-__device__ void plan_body(const DecodeArgs& a, int grid) {
+// lens_src: the lengths to plan with (system-scope loads when `sys`: page-locked host memory);
+// lens_out: when not null, receives a copy of them for the decode kernel (a.ctx_lens).
+__device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src,
+                          int32_t* lens_out, bool sys) {
   constexpr int kPlanWaves = kPlanThreads / kWave;
   __shared__ int s_cnt[kMaxBuckets];   // partial partitions per bucket
   __shared__ int s_base[kMaxBuckets];  // first entry of each bucket (then a cursor)
   __shared__ int s_wave[kPlanWaves];
   __shared__ int s_full;               // full partitions counted so far
+  __shared__ int s_len[kPlanKeep];     // pass 1's lengths of the first kPlanKeep sequences
   const int nbk = a.PT / 32;  // a partial partition has 0 .. PT-1 tokens: buckets 0 .. nbk
   for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
   if (threadIdx.x == 0) s_full = 0;
@@ -646,7 +651,10 @@ __device__ void plan_body(const DecodeArgs& a, int grid) {
     int n = 0;
     if (s < a.S) {
       bool bad;
-      n = eff_len(a.ctx_lens[s], a.len_cap, bad);
+      const int raw = ld_step(lens_src + s, sys);
+      if (lens_out) lens_out[s] = raw;
+      if (s < kPlanKeep) s_len[s] = raw;
+      n = eff_len(raw, a.len_cap, bad);
     }
     const int full = s < a.S ? n / a.PT : 0, rem = n - full * a.PT;
     const int incl = wave_inclusive_sum(full);
@@ -672,32 +680,36 @@ __device__ void plan_body(const DecodeArgs& a, int grid) {
     }
   }
   __syncthreads();
-  // Pass 2: the partial partitions.
+  // Pass 2: the partial partitions (each thread revisits the sequences it read in pass 1).
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
     bool bad;
-    const int n = eff_len(a.ctx_lens[s], a.len_cap, bad);
+    const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
+    const int n = eff_len(raw, a.len_cap, bad);
     const int full = n / a.PT, rem = n - full * a.PT;
     if (rem > 0 || n == 0) a.items[atomicAdd(&s_base[(rem + 31) / 32], 1)] = make_int2(s, full);
   }
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int grid) {
-  plan_body(a, grid);
+  plan_body(a, grid, a.ctx_lens, nullptr, false);
 }
 
 // The prologue of a fused serving step: the step's cache write (and table patch) and the
-// decode planning are independent, so one launch does both -- the last workgroup plans, the
+// decode planning are independent, so one launch does both -- the first workgroup plans, the
 // others scatter the new tokens.
 static_assert(kPlanThreads == kWriteThreads, "one block size for both halves of the prologue");
 
+// The plan reads the step's lengths from w.tp.ctx_lens (where the write's table patch reads
+// them too) and, when lens_out is set, stores them for the decode kernel.
 template <typename T>
 __global__ __launch_bounds__(kPlanThreads) void step_prologue_kernel(CacheWriteArgs w,
-                                                                     DecodeArgs a, int grid) {
-  if (blockIdx.x == gridDim.x - 1) {
-    plan_body(a, grid);
+                                                                     DecodeArgs a, int grid,
+                                                                     int32_t* lens_out) {
+  if (blockIdx.x == 0) {  // dispatched first: the plan is the longer chain
+    plan_body(a, grid, w.tp.ctx_lens, lens_out, w.sys);
     return;
   }
-  cache_write_chunk<T>(w, static_cast<int64_t>(blockIdx.x) * kWriteThreads + threadIdx.x);
+  cache_write_chunk<T>(w, static_cast<int64_t>(blockIdx.x - 1) * kWriteThreads + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -785,7 +797,7 @@ static KernelFn pick_valu(int32_t dtype, int G) {
 template <int D, int B>
 static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void* workspace,
                         size_t workspace_bytes_in, hipStream_t stream,
-                        const CacheWriteArgs* wr = nullptr) {
+                        const CacheWriteArgs* wr = nullptr, int32_t* lens_out = nullptr) {
   KernelFn k = nullptr;
   if (dtype == PA_DTYPE_BF16 && a.G >= 3 && a.G <= 16)
     k = decode_mfma_kernel<D, B>;
@@ -815,9 +827,9 @@ static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void*
   if (wr) {
     const unsigned nw = static_cast<unsigned>((wr->n_chunks + kWriteThreads - 1) / kWriteThreads);
     if (dtype == PA_DTYPE_F32)
-      hipLaunchKernelGGL(step_prologue_kernel<float>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, *wr, a, grid);
+      hipLaunchKernelGGL(step_prologue_kernel<float>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, *wr, a, grid, lens_out);
     else
-      hipLaunchKernelGGL(step_prologue_kernel<uint16_t>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, *wr, a, grid);
+      hipLaunchKernelGGL(step_prologue_kernel<uint16_t>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, *wr, a, grid, lens_out);
     if (pa_status st = launch_status("pa_decode_step (cache write + plan)")) return st;
   } else {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, grid);
@@ -915,11 +927,37 @@ static pa_status decode_setup(const char* who, void* out, const void* q, const v
 }
 
 static pa_status dispatch(const DecodeArgs& a, int D, int B, int32_t dtype, int pt, void* w,
-                          size_t wb, void* stream, const CacheWriteArgs* wr) {
+                          size_t wb, void* stream, const CacheWriteArgs* wr,
+                          int32_t* lens_out = nullptr) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 64)
-    return B == 16 ? launch<64, 16>(a, dtype, pt, w, wb, st, wr) : launch<64, 32>(a, dtype, pt, w, wb, st, wr);
-  return B == 16 ? launch<128, 16>(a, dtype, pt, w, wb, st, wr) : launch<128, 32>(a, dtype, pt, w, wb, st, wr);
+    return B == 16 ? launch<64, 16>(a, dtype, pt, w, wb, st, wr, lens_out)
+                   : launch<64, 32>(a, dtype, pt, w, wb, st, wr, lens_out);
+  return B == 16 ? launch<128, 16>(a, dtype, pt, w, wb, st, wr, lens_out)
+                 : launch<128, 32>(a, dtype, pt, w, wb, st, wr, lens_out);
+}
+
+// Where a step's slots or lengths live.  Device memory is read with ordinary loads; page-locked
+// host memory, which HIP maps into the device's address space at the same address, is read
+// through system-scope loads.  Pageable host memory is rejected.
+static pa_status step_input(const char* what, const int32_t* p, bool* host) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID_ARG,
+                "pa_decode_step: %s is neither device memory nor page-locked host memory", what);
+  }
+  if (at.type == hipMemoryTypeHost) {
+    if (at.devicePointer != p || at.hostPointer != p)
+      return fail(PA_ERR_INVALID_ARG,
+                  "pa_decode_step: page-locked %s is not mapped at its host address", what);
+    *host = true;
+    return ok();
+  }
+  if (at.type == hipMemoryTypeUnregistered)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_step: %s is pageable host memory", what);
+  *host = false;
+  return ok();
 }
 
 extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -939,11 +977,12 @@ extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, co
 
 extern "C" pa_status pa_decode_step(void* out, const void* q, const void* key, const void* value,
                                     void* k_cache, void* v_cache, const int32_t* slot_mapping,
-                                    int32_t* block_tables, const int32_t* ctx_lens, int32_t S,
-                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
-                                    int32_t num_blocks, int32_t max_blocks, int32_t max_ctx_len,
-                                    float scale, int32_t dtype, int32_t partition_tokens,
-                                    void* workspace, size_t workspace_bytes_in, void* stream) {
+                                    int32_t* block_tables, int32_t* ctx_lens,
+                                    const int32_t* new_ctx_lens, int32_t S, int32_t Hq,
+                                    int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+                                    int32_t max_blocks, int32_t max_ctx_len, float scale,
+                                    int32_t dtype, int32_t partition_tokens, void* workspace,
+                                    size_t workspace_bytes_in, void* stream) {
   DecodeArgs a;
   if (pa_status st = decode_setup("pa_decode_step", out, q, k_cache, v_cache, block_tables, ctx_lens,
                                   S, Hq, Hkv, D, B, num_blocks, max_blocks, max_ctx_len, scale,
@@ -953,8 +992,17 @@ extern "C" pa_status pa_decode_step(void* out, const void* q, const void* key, c
   if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "pa_decode_step: NULL pointer");
   if (!aligned16(key) || !aligned16(value))
     return fail(PA_ERR_INVALID_ARG, "pa_decode_step: key and value must be 16-byte aligned");
-  const CacheWriteArgs wr = make_cache_write_args(key, value, k_cache, v_cache, slot_mapping, S, Hkv,
-                                                  D, B, num_blocks, dtype,
-                                                  TablePatch{block_tables, ctx_lens, 1, max_blocks});
-  return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, &wr);
+  if (new_ctx_lens == ctx_lens) new_ctx_lens = nullptr;
+  bool host_slots = false, host_lens = false;
+  if (pa_status st = step_input("slot_mapping", slot_mapping, &host_slots)) return st;
+  if (new_ctx_lens)
+    if (pa_status st = step_input("new_ctx_lens", new_ctx_lens, &host_lens)) return st;
+  // The write's table patch and the plan read the step's lengths from their source; the decode
+  // kernel reads the device copy the plan leaves in ctx_lens.
+  CacheWriteArgs wr = make_cache_write_args(
+      key, value, k_cache, v_cache, slot_mapping, S, Hkv, D, B, num_blocks, dtype,
+      TablePatch{block_tables, new_ctx_lens ? new_ctx_lens : ctx_lens, 1, max_blocks});
+  wr.sys = host_slots || host_lens;
+  return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, &wr,
+                  new_ctx_lens ? ctx_lens : nullptr);
 }

@@ -119,14 +119,18 @@ STEP_CASES = {
 }
 
 
+@pytest.mark.parametrize("meta", ["device", "pinned"])
 @pytest.mark.parametrize("name", list(STEP_CASES))
-def test_fused_step_equals_append_then_decode(gpu, name):
+def test_fused_step_equals_append_then_decode(gpu, name, meta):
     """pa_decode_step (cache write + plan in one launch, then decode) gives bit-identical
-    outputs, pools and tables to pa_cache_append followed by pa_decode, step after step."""
+    outputs, pools and tables to pa_cache_append followed by pa_decode, step after step.
+    meta="pinned": the step's slots and new lengths come from the same two pinned host buffers
+    every step (read by the kernel directly, so a stale cached copy would show)."""
     from paged_kv_cache_378_amd import _lib
     from paged_kv_cache_378_amd.runner import PagedState
     w = STEP_CASES[name]()
-    print(f"[gpu] fused step {name}: S={w.num_seqs} B={w.block_size} {w.dtype}", flush=True)
+    print(f"[gpu] fused step {name} ({meta}): S={w.num_seqs} B={w.block_size} {w.dtype}",
+          flush=True)
     n_steps = 6
     sa = PagedState(w, "cuda", poison=True)   # two-call path
     sb = PagedState(w, "cuda", poison=True)   # fused path
@@ -140,17 +144,25 @@ def test_fused_step_equals_append_then_decode(gpu, name):
     wsa = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     wsb = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     it = torch.int16 if w.dtype == "bf16" else torch.int32
+    pin_slots = torch.empty(S, dtype=torch.int32).pin_memory()
+    pin_lens = torch.empty(S, dtype=torch.int32).pin_memory()
     for step in range(n_steps):
         kn, vn = (x.cuda() for x in step_values(w, step, S))
         outs = []
         for st, t, l, ws, fused in ((sa, ta, la, wsa, False), (sb, tb, lb, wsb, True)):
             slots, pairs = st.bm.append_slots(ids, 1)
-            l.copy_(torch.from_numpy(st.bm.seq_lens(ids)))
+            if not (fused and meta == "pinned"):   # pinned: the step itself fills l
+                l.copy_(torch.from_numpy(st.bm.seq_lens(ids)))
             if len(pairs):
                 _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).cuda())
             sl = torch.from_numpy(slots).cuda()
             out = st.new_out()
-            if fused:
+            if fused and meta == "pinned":
+                pin_slots.numpy()[:] = slots
+                st.bm.seq_lens(ids, pin_lens.numpy())
+                _lib.pa_decode_step(out, st.vals["q"], kn, vn, st.k_cache, st.v_cache, pin_slots,
+                                    t, l, max_ctx, w.scale, 0, ws, new_ctx_lens=pin_lens)
+            elif fused:
                 _lib.pa_decode_step(out, st.vals["q"], kn, vn, st.k_cache, st.v_cache, sl, t, l,
                                     max_ctx, w.scale, 0, ws)
             else:
@@ -164,3 +176,32 @@ def test_fused_step_equals_append_then_decode(gpu, name):
         assert torch.isfinite(outs[1].float()).all()
     assert torch.equal(sa.k_cache.view(it), sb.k_cache.view(it))
     assert torch.equal(sa.v_cache.view(it), sb.v_cache.view(it))
+
+
+def test_fused_step_rejects_pageable_metadata(gpu):
+    """Slots in pageable host memory are refused before anything is launched."""
+    import ctypes
+    from paged_kv_cache_378_amd import _lib
+    from paged_kv_cache_378_amd.runner import PagedState
+    w = wl.custom_decode("steprej", 44, [5, 17], 4, 4, 64, 16, "f32", extra_blocks=4)
+    st = PagedState(w, "cuda", poison=True)
+    S, B = w.num_seqs, w.block_size
+    tables, lens = st.bm.block_tables(w.step_ids, 4)
+    tables_d, lens_d = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    kn, vn = (x.cuda() for x in step_values(w, 0, S))
+    out = st.new_out()
+    ws = torch.empty(_lib.pa_decode_workspace_size(S, w.hq, w.head_dim, 64, 0), dtype=torch.uint8,
+                     device="cuda")
+    before = (out.clone(), st.k_cache.clone(), tables_d.clone())
+    pageable = np.zeros(S, np.int32)
+    rc = _lib._lib.pa_decode_step(out.data_ptr(), st.vals["q"].data_ptr(), kn.data_ptr(),
+                                  vn.data_ptr(), st.k_cache.data_ptr(), st.v_cache.data_ptr(),
+                                  pageable.ctypes.data, tables_d.data_ptr(), lens_d.data_ptr(),
+                                  None, S, w.hq, w.hkv, w.head_dim, B, w.num_blocks, 4, 64,
+                                  ctypes.c_float(w.scale), _lib.PA_DTYPE_F32, 0, ws.data_ptr(),
+                                  ws.numel(), None)
+    assert rc == _lib.PA_ERR_INVALID_ARG and "host memory" in _lib._lib.pa_last_error().decode()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), before[0].view(torch.int32))
+    assert torch.equal(st.k_cache.view(torch.int32), before[1].view(torch.int32))
+    assert torch.equal(tables_d, before[2])

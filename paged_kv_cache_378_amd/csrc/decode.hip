@@ -70,6 +70,7 @@ struct DecodeArgs {
   float2* part_ml;  // [S, Hq, Pmax]     (max in log2 units, sum)
   int2* items;      // work list: (sequence, partition) entries, longest first; Hkv items each
   int* queue;       // [0] number of items, [1] next unclaimed item
+  int* done;        // [S, Hkv] partitions finished (split sequences), zeroed by the plan
   int S, Hq, Hkv, G, max_blocks, num_blocks, PT, Pmax;
   int len_cap;      // min(max_blocks * B, max_ctx_len): longest context the call may see
   float scale_log2;
@@ -107,10 +108,67 @@ __device__ void finish_partition(const DecodeArgs& a, int s, int kvh, int part, 
     if (nparts == 1) {
       static_cast<T*>(a.out)[(static_cast<size_t>(s) * a.Hq + hq) * D + d] = Elem<T>::from_f32(r);
     } else {
+      // partials are written through to memory (agent scope): the workgroup that merges them
+      // may run on another XCD, behind another L2
       const size_t row = (static_cast<size_t>(s) * a.Hq + hq) * a.Pmax + part;
-      a.part_o[row * D + d] = r;
-      if (d == 0) a.part_ml[row] = bad ? make_float2(0.f, NAN) : make_float2(M, L);
+      st_agent(a.part_o + row * D + d, r);
+      if (d == 0) {
+        float* ml = reinterpret_cast<float*>(a.part_ml + row);
+        st_agent(ml, bad ? 0.f : M);
+        st_agent(ml + 1, bad ? NAN : L);
+      }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Partition merge: m = max_p m_p; out = sum_p o_p l_p 2^(m_p - m) / sum_p l_p 2^(m_p - m).
+// It runs in the decode kernel, in the workgroup that finishes the last partition of a
+// (sequence, kv-head): each workgroup that stores a partial counts it in `done` once its
+// stores are complete, and the one that brings the count to nparts merges.  Partials are
+// stored and loaded with agent-scope accesses, which bypass the per-XCD L2s, so no cache
+// write-back or invalidation is needed; the workgroups never wait on each other.
+// The merging workgroup covers the G x D outputs, four consecutive dims per thread, summing
+// partitions in index order (the result does not depend on which workgroup merges).
+// ---------------------------------------------------------------------------------------
+template <typename T, int D>
+__device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
+  __shared__ int s_last;
+  if (nparts <= 1) return;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(a.done + s * a.Hkv + kvh, 1) == nparts - 1;
+  __syncthreads();
+  if (!s_last) return;
+  bool bad;
+  (void)eff_len(a.ctx_lens[s], a.len_cap, bad);
+  constexpr int C4 = D / 4;  // float4 chunks per head
+  for (int c = threadIdx.x; c < a.G * C4; c += kNW * kWave) {
+    const int h = c / C4, d4 = c - h * C4;
+    const int hq = kvh * a.G + h;
+    const size_t row = (static_cast<size_t>(s) * a.Hq + hq) * a.Pmax;
+    const float* ml = reinterpret_cast<const float*>(a.part_ml + row);
+    const float* po = a.part_o + row * D + 4 * d4;
+    float M = -INFINITY;
+    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ld_agent(ml + 2 * p));
+    float L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int p = 0; p < nparts; ++p) {
+      const float wgt = ld_agent(ml + 2 * p + 1) * exp2f(ld_agent(ml + 2 * p) - M);
+      const float* v = po + static_cast<size_t>(p) * D;
+      L += wgt;
+      O.x = fmaf(wgt, ld_agent(v + 0), O.x);
+      O.y = fmaf(wgt, ld_agent(v + 1), O.y);
+      O.z = fmaf(wgt, ld_agent(v + 2), O.z);
+      O.w = fmaf(wgt, ld_agent(v + 3), O.w);
+    }
+    const float inv = bad ? NAN : 1.f / L;
+    T* op = static_cast<T*>(a.out) + (static_cast<size_t>(s) * a.Hq + hq) * D + 4 * d4;
+    op[0] = Elem<T>::from_f32(O.x * inv);
+    op[1] = Elem<T>::from_f32(O.y * inv);
+    op[2] = Elem<T>::from_f32(O.z * inv);
+    op[3] = Elem<T>::from_f32(O.w * inv);
   }
 }
 
@@ -378,6 +436,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, i
     for (int i = 0; i < 4; ++i) s_o[w][r16][16 * ni + 4 * gp + i] = o[ni][i];
   __syncthreads();
   finish_partition<uint16_t, D, 16>(a, s, kvh, part, rg.nparts, rg.bad, s_ml, s_o);
+  merge_if_last<uint16_t, D>(a, s, kvh, rg.nparts);
 }
 
 template <int D, int B>
@@ -547,6 +606,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, int s, int kvh, i
   }
   __syncthreads();
   finish_partition<T, D, G>(a, s, kvh, part, rg.nparts, rg.bad, s_ml, s_o);
+  merge_if_last<T, D>(a, s, kvh, rg.nparts);
 }
 
 template <typename T, int D, int B, int G, int LPT>
@@ -560,52 +620,6 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
   for_each_item(a, &s_next, [&](int s, int kvh, int part) {
     valu_item<T, D, B, G, LPT, TPR>(a, s, kvh, part, s_tbl, &s_bad, s_ml, s_o, s_p);
   });
-}
-
-// ---------------------------------------------------------------------------------------
-// Partition merge: m = max_p m_p; out = sum_p o_p l_p 2^(m_p - m) / sum_p l_p 2^(m_p - m).
-// One workgroup per (kv-head, sequence) covers the G x D outputs of that head group, four
-// consecutive dims per thread (16-byte partial loads); sequences with one partition were
-// finished by the decode kernel already.
-// ---------------------------------------------------------------------------------------
-constexpr int kMergeThreads = 256;
-
-template <typename T, int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
-  const int kvh = blockIdx.x, s = blockIdx.y;
-  bool bad;
-  const int n = eff_len(a.ctx_lens[s], a.len_cap, bad);
-  const int nparts = n > 0 ? (n + a.PT - 1) / a.PT : 1;
-  if (nparts <= 1) return;
-  constexpr int C4 = D / 4;  // float4 chunks per head
-  for (int c = threadIdx.x; c < a.G * C4; c += kMergeThreads) {
-    const int h = c / C4, d4 = c - h * C4;
-    const int hq = kvh * a.G + h;
-    const size_t row = (static_cast<size_t>(s) * a.Hq + hq) * a.Pmax;
-    const float2* ml = a.part_ml + row;
-    const float4* po = reinterpret_cast<const float4*>(a.part_o + row * D) + d4;
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[p].x);
-    float L = 0.f;
-    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-    for (int p = 0; p < nparts; ++p) {
-      const float2 e = ml[p];
-      const float wgt = e.y * exp2f(e.x - M);
-      const float4 v = po[static_cast<size_t>(p) * C4];
-      L += wgt;
-      O.x = fmaf(wgt, v.x, O.x);
-      O.y = fmaf(wgt, v.y, O.y);
-      O.z = fmaf(wgt, v.z, O.z);
-      O.w = fmaf(wgt, v.w, O.w);
-    }
-    const float inv = bad ? NAN : 1.f / L;
-    T* op = static_cast<T*>(a.out) + (static_cast<size_t>(s) * a.Hq + hq) * D + 4 * d4;
-    op[0] = Elem<T>::from_f32(O.x * inv);
-    op[1] = Elem<T>::from_f32(O.y * inv);
-    op[2] = Elem<T>::from_f32(O.z * inv);
-    op[3] = Elem<T>::from_f32(O.w * inv);
-  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -642,6 +656,8 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   const int nbk = a.PT / 32;  // a partial partition has 0 .. PT-1 tokens: buckets 0 .. nbk
   for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
   if (threadIdx.x == 0) s_full = 0;
+  if (a.Pmax > 1)
+    for (int i = threadIdx.x; i < a.S * a.Hkv; i += kPlanThreads) a.done[i] = 0;
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   __syncthreads();
   // Pass 1, one sequence per thread per round: full partitions get consecutive entries from
@@ -730,7 +746,7 @@ static int auto_partition(int S, int Hkv, int max_ctx_len, int resident) {
 // Workspace: [queue header | work list | partition (m, l) | partition outputs].  The work
 // list is sized for Hq heads (an upper bound of Hkv) so that the size query needs no Hkv.
 struct WsLayout {
-  size_t items, ml, o, total;
+  size_t items, done, ml, o, total;
 };
 
 static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -742,6 +758,8 @@ static WsLayout ws_layout(int S, int Hq, int D, int Pmax) {
   off += round256(static_cast<size_t>(S) * Pmax * Hq * sizeof(int2));
   if (Pmax > 1) {
     const size_t rows = static_cast<size_t>(S) * Hq * Pmax;
+    L.done = off;
+    off += round256(static_cast<size_t>(S) * Hq * sizeof(int));
     L.ml = off;
     off += round256(rows * sizeof(float2));
     L.o = off;
@@ -818,6 +836,7 @@ static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void*
   a.queue = reinterpret_cast<int*>(ws);
   a.items = reinterpret_cast<int2*>(ws + L.items);
   if (a.Pmax > 1) {
+    a.done = reinterpret_cast<int*>(ws + L.done);
     a.part_ml = reinterpret_cast<float2*>(ws + L.ml);
     a.part_o = reinterpret_cast<float*>(ws + L.o);
   }
@@ -837,13 +856,6 @@ static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void*
   }
   hipLaunchKernelGGL(k, dim3(grid), dim3(kNW * kWave), 0, stream, a);
   if (pa_status st = launch_status("pa_decode")) return st;
-  if (a.Pmax > 1) {
-    if (dtype == PA_DTYPE_F32)
-      hipLaunchKernelGGL((merge_kernel<float, D>), dim3(a.Hkv, a.S), dim3(kMergeThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((merge_kernel<uint16_t, D>), dim3(a.Hkv, a.S), dim3(kMergeThreads), 0, stream, a);
-    return launch_status("pa_decode (merge)");
-  }
   return ok();
 }
 

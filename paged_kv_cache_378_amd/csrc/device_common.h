@@ -74,6 +74,16 @@ __device__ __forceinline__ int kswz(int key) {
 // (harmless for softmax weights, which are summed against weights near 1).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Agent-scope (device-coherent) 4-byte accesses: on a multi-XCD device they are performed past
+// the XCD-local L2, so values one workgroup stores are seen by a workgroup on another XCD
+// without a whole-cache write-back or invalidation.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Index of this wave in its workgroup, as a wave-uniform (scalar) value.  Without the
 // readfirstlane the compiler treats threadIdx.x / 64 as divergent, so every loop bounded by
 // it becomes exec-masked vector control flow instead of a scalar loop.

@@ -11,7 +11,7 @@ namespace pa {
 
 template <typename T>
 __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(CacheWriteArgs a) {
-  cache_write_chunk<T>(a, static_cast<int64_t>(blockIdx.x) * kWriteThreads + threadIdx.x);
+  cache_write_wg<T>(a, blockIdx.x);
 }
 
 // One workgroup per pair; each copies the whole block (all kv-heads and slots) of both pools.
@@ -51,7 +51,7 @@ static pa_status launch_cache_write(const char* who, const void* key, const void
                                     void* stream) {
   const CacheWriteArgs w = make_cache_write_args(key, value, k_cache, v_cache, slot_mapping, T,
                                                  Hkv, D, B, num_blocks, dtype, tp);
-  const dim3 grid(static_cast<unsigned>((w.n_chunks + kWriteThreads - 1) / kWriteThreads));
+  const dim3 grid(static_cast<unsigned>(cache_write_wgs(w)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == PA_DTYPE_F32)
     hipLaunchKernelGGL(cache_write_kernel<float>, grid, dim3(kWriteThreads), 0, s, w);

@@ -725,7 +725,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_prologue_kernel(CacheWriteA
     plan_body(a, grid, w.tp.ctx_lens, lens_out, w.sys);
     return;
   }
-  cache_write_chunk<T>(w, static_cast<int64_t>(blockIdx.x - 1) * kWriteThreads + threadIdx.x);
+  cache_write_wg<T>(w, blockIdx.x - 1);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -844,7 +844,7 @@ static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void*
   const int64_t max_items = static_cast<int64_t>(a.S) * a.Pmax * a.Hkv;
   const int grid = static_cast<int>(max_items < cap ? max_items : cap);
   if (wr) {
-    const unsigned nw = static_cast<unsigned>((wr->n_chunks + kWriteThreads - 1) / kWriteThreads);
+    const unsigned nw = static_cast<unsigned>(cache_write_wgs(*wr));
     if (dtype == PA_DTYPE_F32)
       hipLaunchKernelGGL(step_prologue_kernel<float>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, *wr, a, grid, lens_out);
     else

@@ -1,4 +1,4 @@
-// Paged decode attention on gfx950: split-K over context partitions, then a merge.
+// Paged decode attention on gfx950: split-K over context partitions and their merge.
 //
 // What is computed ("vLLM PagedAttention" (tinycto), FAQ: paging leaves the result of standard
 // multi-head attention unchanged; KV-cache chapter, "Common misconception": the same scores and
@@ -15,24 +15,25 @@
 //   * a work item is one partition of PT tokens of one (sequence, kv-head); NW = 4 waves split
 //     the partition's 32-token tiles round-robin and each keeps its own online-softmax state
 //     (running max m, running sum l, unnormalised output o), scores in the log2 domain;
-//   * a one-workgroup planning kernel turns the context lengths into a work list, longest
-//     first: every full partition, then the partial last partitions by decreasing length.
-//     The decode kernel is persistent (about as many workgroups as the chip holds at once)
-//     and pulls items from that list through an atomic cursor, prefetching the next index
-//     while it works on the current one.  No workgroup is launched for a partition that does
-//     not exist, and the short items fill the tail of the schedule;
+//   * one workgroup plans: it turns the context lengths into a work list, longest first --
+//     every full partition, then the partial last partitions by decreasing length.  It runs as
+//     a one-workgroup kernel (pa_decode) or as workgroup 0 of the step's first kernel beside
+//     the cache write (pa_decode_step).  The decode kernel is persistent (about as many
+//     workgroups as the chip holds at once) and pulls items from that list through an atomic
+//     cursor, prefetching the next index while it works on the current one.  No workgroup is
+//     launched for a partition that does not exist, and the short items fill the tail;
 //   * the partition's block-table slice is staged in LDS once (loaded together with the
 //     context length), so tile loads never wait on a dependent table load;
 //   * the four wave states are merged through LDS; a single-partition sequence writes its
-//     final output directly, otherwise the partition writes (m, l, o/l) and a merge kernel
-//     combines the partitions (the FlashAttention-style tiling the KV-cache chapter mentions
-//     in "Common misconception").
+//     final output directly.  Otherwise the partition stores (m, l, o/l) and the workgroup
+//     that finishes the last partition of that (sequence, kv-head) merges them (the
+//     FlashAttention-style tiling the KV-cache chapter mentions in "Common misconception");
 //   * GQA groups (bf16, g >= 3): QK^T and PV are real dense contractions of g heads against
 //     the tile, done on the matrix cores (v_mfma_f32_16x16x32_bf16).  S^T = K Q^T puts 16
 //     tokens on the rows and the (padded) 16 heads on the columns; O^T = V^T P^T contracts
-//     over tokens.  Each lane loads 16-byte runs straight into its MFMA operand registers:
-//     K rows are contiguous in the K pool, and the V pool is stored transposed per block so
-//     8 consecutive tokens of one dim are contiguous too.  No LDS round trip for K/V.
+//     over tokens.  K is loaded as whole 256-byte rows and re-laid out through LDS into the
+//     operand layout; the V pool is stored transposed per block so 8 consecutive tokens of
+//     one dim are contiguous and load straight into the PV operand registers;
 //   * one query head per kv-head (g in {1, 2}) or fp32: a VALU kernel; LPT lanes share one
 //     token's dot product (reduced with cross-lane shuffles), the round max uses shuffles, and
 //     the PV update broadcasts the round's weights through a per-wave LDS slot.
@@ -810,8 +811,8 @@ static KernelFn pick_valu(int32_t dtype, int G) {
 }
 
 // Picks the kernel, the partition length and the grid, lays out the workspace and launches
-// plan -> decode -> merge on `stream`.  With a cache write (`wr`, pa_decode_step) the plan
-// shares its launch with the write.
+// plan -> decode (which merges split partitions itself) on `stream`.  With a cache write (`wr`,
+// pa_decode_step) the plan shares its launch with the write.
 template <int D, int B>
 static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void* workspace,
                         size_t workspace_bytes_in, hipStream_t stream,

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   // tile t is multiplied and stored at the end of iteration t+1, so each tile's global loads
   // have two compute phases to arrive.
   struct Regs {
-    uint4 k[PASSES_K], v[PASSES_V];
+    u32x4 k[PASSES_K], v[PASSES_V];  // vector types: HIP's uint4 struct kept them in scratch
   };
   auto gload = [&](Regs& r, int t) {
     const int k0 = t * kKT;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
       const int j = min(k0 + key, kend - 1);   // clamp: never past the last needed key
       const int blk = s_tbl[j / B - win0];
-      r.k[p] = *reinterpret_cast<const uint4*>(
+      r.k[p] = *reinterpret_cast<const u32x4*>(
           a.kc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(j % B) * D + piece * 8);
     }
 #pragma unroll
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       const int dim = e / VP_PER_ROW, piece = e % VP_PER_ROW;   // piece = 8 keys
       const int j = min(k0 + 8 * piece, (kend - 1) & ~7);
       const int blk = s_tbl[j / B - win0];
-      r.v[p] = *reinterpret_cast<const uint4*>(
+      r.v[p] = *reinterpret_cast<const u32x4*>(
           a.vc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(dim) * B + (j % B));
     }
   };
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     for (int p = 0; p < PASSES_K; ++p) {
       const int e = tid + p * kWaves * kWave;
       const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
-      *reinterpret_cast<uint4*>(kb + key * SM::KROW + ((piece ^ pa::kswz<D>(key)) << 4)) = r.k[p];
+      *reinterpret_cast<u32x4*>(kb + key * SM::KROW + ((piece ^ pa::kswz<D>(key)) << 4)) = r.k[p];
     }
     // Keys at or past kend carry weight 0, but their slots may hold anything (even NaN, and
     // 0 * NaN = NaN inside the MFMA): zero their V elements (only the last tile has any).
@@ -185,16 +185,18 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     for (int p = 0; p < PASSES_V; ++p) {
       const int e = tid + p * kWaves * kWave;
       const int dim = e / VP_PER_ROW, piece = e % VP_PER_ROW;
+      u32x4 vv = r.v[p];
       if (tail) {
+        // element q of the piece (key k0 + 8 piece + q) is kept iff q < nvalid; a 32-bit word
+        // holds elements 2w (low half) and 2w + 1 (high half)
         const int nvalid = kend - (k0 + 8 * piece);
-        uint16_t e8[8];
-        __builtin_memcpy(e8, &r.v[p], 16);
+        auto keep = [nvalid](uint32_t word, int q) -> uint32_t {
+          return word & ((q < nvalid ? 0x0000FFFFu : 0u) | (q + 1 < nvalid ? 0xFFFF0000u : 0u));
+        };
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (q >= nvalid) e8[q] = 0;
-        __builtin_memcpy(&r.v[p], e8, 16);
+        for (int wd = 0; wd < 4; ++wd) vv[wd] = keep(vv[wd], 2 * wd);
       }
-      *reinterpret_cast<uint4*>(vb + dim * SM::VROW + piece * 16) = r.v[p];
+      *reinterpret_cast<u32x4*>(vb + dim * SM::VROW + piece * 16) = vv;
     }
   };
 

@@ -14,9 +14,10 @@
 //     all g heads (GQA) -- 256 rows per workgroup, 32 per wave (8 waves), in 2 column tiles
 //     of 16 (the accumulators of 32 rows fit in VGPRs; 64 rows per wave spilled them to AGPRs
 //     and the loop moved them back and forth);
-//   * K/V tiles of 32 keys are staged in LDS (double-buffered: the next tile's global loads
-//     are in flight while the current one is multiplied); K rows are chunk-swizzled and V rows
-//     padded by 16 bytes so the 16-lane operand reads hit distinct banks;
+//   * the query blocks of one (sequence, kv-head) run on one XCD, so they share its L2;
+//   * K/V tiles of 64 keys are staged in LDS (two stages; two register sets carry tile t+2's
+//     global loads while tile t is multiplied); K rows are chunk-swizzled and V rows padded by
+//     16 bytes so the 16-lane operand reads hit distinct banks;
 //   * S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 32 keys x 16 rows per tile pair) puts keys on the
 //     MFMA rows so a query row's scores sit in one lane column: the row max needs only two
 //     cross-lane steps; O^T = V^T P^T contracts over the 32 keys with P taken straight from
@@ -41,6 +42,7 @@ constexpr int kKT = 64;                 // keys per LDS tile (one barrier per ti
 constexpr int kSub = 32;                // keys per compute step (two steps per tile)
 constexpr int kTblWin = 512;            // block-table entries staged in LDS at a time
 constexpr float kLazy = 8.f;            // lazy-rescale threshold (log2 units: weights < 256)
+constexpr int kXcd = 8;                 // XCDs of an MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Args {
@@ -50,7 +52,7 @@ struct Args {
   const uint16_t* vc;
   const int32_t* tables;
   const int32_t* ctx_lens;
-  int S, C, Hq, Hkv, G, TQ, max_blocks, num_blocks;
+  int S, C, Hq, Hkv, G, TQ, NQB, max_blocks, num_blocks;
   float scale_log2;
 };
 
@@ -71,7 +73,13 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SM::STAGE];
   __shared__ int s_tbl[kTblWin];  // physical blocks of logical blocks win0 .. win0 + kTblWin - 1
 
-  const int qb = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  // XCD-aware order: the dispatcher deals workgroups round-robin to the kXcd XCDs, so
+  // workgroup L runs on XCD L % kXcd.  Every query block of one (sequence, kv-head) group is
+  // placed on the same XCD, where they stream the same K/V through one L2.
+  const int L = blockIdx.x, xcd = L % kXcd, j = L / kXcd;
+  const int grp = (j / a.NQB) * kXcd + xcd;
+  if (grp >= a.S * a.Hkv) return;  // padding of the last round of groups
+  const int qb = j % a.NQB, kvh = grp % a.Hkv, s = grp / a.Hkv;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = wave_id();
   const int r16 = lane & 15, gp = lane >> 4;
   const int G = a.G, C = a.C;
@@ -255,8 +263,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
           for (int j = 0; j < 8; ++j)
             if (k0 + 8 * gp + j > limit) x[j] = -INFINITY;
         }
-        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        float mx = vmax(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], vmax3(x[5], x[6], x[7])));
         mx = max_xor32(max_xor16(mx));
         mx *= a.scale_log2;  // row max in log2 units (the scale is positive)
         // Lazy rescaling: the row's reference max m_run moves only when a score exceeds it by
@@ -399,10 +406,13 @@ extern "C" pa_status pa_chunk_attend(void* out, const void* q, const void* k_cac
   a.Hkv = Hkv;
   a.G = G;
   a.TQ = chunk::kRows / G;
+  a.NQB = (C + a.TQ - 1) / a.TQ;
   a.max_blocks = max_blocks;
   a.num_blocks = num_blocks;
   a.scale_log2 = scale * chunk::kLog2e;
-  const dim3 grid((C + a.TQ - 1) / a.TQ, Hkv, S);
+  const int64_t groups = (static_cast<int64_t>(S) * Hkv + chunk::kXcd - 1) / chunk::kXcd * chunk::kXcd;
+  if (groups * a.NQB > INT_MAX) return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: grid too large");
+  const dim3 grid(static_cast<unsigned>(groups * a.NQB));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 64) {
     if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<64, 16>), grid, dim3(chunk::kWaves * kWave), 0, st, a);

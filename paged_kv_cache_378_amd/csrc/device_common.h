@@ -47,17 +47,23 @@ template <> struct Elem<uint16_t> {  // bf16 carried as raw bits
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// NaN-propagating max (llvm.maximum; v_maximum_f32 / v_maximum3_f32 on gfx950).  fmaxf is
+// IEEE maxNum, which first canonicalizes every operand the compiler cannot prove canonical --
+// one extra VALU instruction per matrix-core result it is applied to.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 // Max over lane pairs (i, i ^ 16) and (i, i ^ 32) with gfx950's row-swap instructions
 // (VALU, no LDS round trip as a generic shuffle has).  Swapping odd 16-lane rows of one copy of
 // v with even rows of another leaves every lane holding its own value and its xor-16
 // partner's; the 32-lane swap does the same for the xor-32 partner.
 __device__ __forceinline__ float max_xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Chunk permutation for K tiles staged in LDS (rows of D bf16 = D/8 16-byte chunks): chunk c

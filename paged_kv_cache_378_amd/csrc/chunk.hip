@@ -222,27 +222,33 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     for (int i = 0; i < NNT; ++i) o[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One 32-key step on the staged tile: keys k0 .. k0 + 31 = rows kSub*hs .. of the tile.
-  auto compute_sub = [&](const unsigned char* kb, const unsigned char* vb, int k0, int hs) {
-      // S^T = K Q^T : row r16 of key group m is key 8*(r16/4) + 4*m + r16%4 of the tile
-      f32x4 sacc[2][kNC];
-  #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int key = kSub * hs + 8 * (r16 >> 2) + 4 * m + (r16 & 3);
-        bf16x8 kop[NST];
-  #pragma unroll
+  // One 32-key step on the staged tile (keys k0 .. k0 + 31 = rows kSub*hs .. of the tile), in
+  // two halves: qk issues the S^T = K Q^T matrix-core work; softmax_pv turns the scores into
+  // weights and accumulates O^T += V^T P^T.  A tile's two steps are issued as qk, qk,
+  // softmax_pv, softmax_pv, so the second step's QK^T runs on the matrix cores while the first
+  // step's softmax runs on the VALU.
+  using SAcc = f32x4[2][kNC];
+  auto qk = [&](const unsigned char* kb, int hs, SAcc& sacc) {
+    // row r16 of key group m is key 8*(r16/4) + 4*m + r16%4 of the 32-key step
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int key = kSub * hs + 8 * (r16 >> 2) + 4 * m + (r16 & 3);
+      bf16x8 kop[NST];
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+        kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+            kb + key * SM::KROW + (((4 * st + gp) ^ pa::kswz<D>(key)) << 4)));
+#pragma unroll
+      for (int c = 0; c < kNC; ++c) {
+        sacc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int st = 0; st < NST; ++st)
-          kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-              kb + key * SM::KROW + (((4 * st + gp) ^ pa::kswz<D>(key)) << 4)));
-  #pragma unroll
-        for (int c = 0; c < kNC; ++c) {
-          sacc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-          for (int st = 0; st < NST; ++st)
-            sacc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], qop[c][st], sacc[m][c], 0, 0, 0);
-        }
+          sacc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], qop[c][st], sacc[m][c], 0, 0, 0);
       }
+    }
+  };
 
+  auto softmax_pv = [&](const unsigned char* vb, int k0, int hs, const SAcc& sacc) {
       // Online softmax per column tile; lane (gp, r16) owns keys k0 + 8 gp + j of row r16.
       // Masking is needed only on tiles that reach past the causal limit of the workgroup's first
       // row (which also covers every key at or past kend); padding rows are never masked, their
@@ -322,12 +328,14 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     }
     const unsigned char* kb = smem + (t & 1) * SM::STAGE;
     const unsigned char* vb = kb + SM::KBYTES;
-#pragma unroll
-    for (int hs = 0; hs < kKT / kSub; ++hs) {
-      const int k0 = t * kKT + hs * kSub;
-      if (k0 >= kend) break;  // uniform
-      compute_sub(kb, vb, k0, hs);
-    }
+    static_assert(kKT == 2 * kSub, "two steps per tile");
+    const int k0 = t * kKT;
+    const bool second = k0 + kSub < kend;  // uniform
+    SAcc s0, s1;
+    qk(kb, 0, s0);
+    if (second) qk(kb, 1, s1);
+    softmax_pv(vb, k0, 0, s0);
+    if (second) softmax_pv(vb, k0 + kSub, 1, s1);
     if (t + 1 < ntiles) lstore(next, (t + 1) & 1, t + 1);
     __syncthreads();
   };

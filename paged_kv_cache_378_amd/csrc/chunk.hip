@@ -15,9 +15,10 @@
 //     of 16 (the accumulators of 32 rows fit in VGPRs; 64 rows per wave spilled them to AGPRs
 //     and the loop moved them back and forth);
 //   * the query blocks of one (sequence, kv-head) run on one XCD, so they share its L2;
-//   * K/V tiles of 64 keys are staged in LDS (two stages; two register sets carry tile t+2's
-//     global loads while tile t is multiplied); K rows are chunk-swizzled and V rows padded by
-//     16 bytes so the 16-lane operand reads hit distinct banks;
+//   * K/V tiles of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4, no
+//     register staging), two stages: tile t+1 is requested before tile t is multiplied.  The
+//     16-byte chunks of K rows and of V^T rows are XOR-swizzled by row (the lane-to-address
+//     choice of the loads does it) so the 16-lane operand reads hit distinct banks;
 //   * S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 32 keys x 16 rows per tile pair) puts keys on the
 //     MFMA rows so a query row's scores sit in one lane column: the row max needs only two
 //     cross-lane steps; O^T = V^T P^T contracts over the 32 keys with P taken straight from
@@ -59,7 +60,7 @@ struct Args {
 template <int D>
 struct Smem {
   static constexpr int KROW = D * 2;           // bytes per key row of the K tile (swizzled)
-  static constexpr int VROW = kKT * 2 + 16;    // bytes per dim row of the V^T tile (padded)
+  static constexpr int VROW = kKT * 2;         // bytes per dim row of the V^T tile (swizzled)
   static constexpr int KBYTES = kKT * KROW;
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   constexpr int NST = D / 32;  // QK k-steps
   constexpr int NNT = D / 16;  // PV dim tiles
   using SM = Smem<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SM::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem0[SM::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem1[SM::STAGE];
   __shared__ int s_tbl[kTblWin];  // physical blocks of logical blocks win0 .. win0 + kTblWin - 1
 
   // XCD-aware order: the dispatcher deals workgroups round-robin to the kXcd XCDs, so
@@ -149,62 +151,56 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   load_window(0);
   __syncthreads();
 
-  // Two register sets stage tiles on their way to LDS: the loads of tile t+2 are issued while
-  // tile t is multiplied and stored at the end of iteration t+1, so each tile's global loads
-  // have two compute phases to arrive.
-  struct Regs {
-    u32x4 k[PASSES_K], v[PASSES_V];  // vector types: HIP's uint4 struct kept them in scratch
-  };
-  auto gload = [&](Regs& r, int t) {
-    const int k0 = t * kKT;
-#pragma unroll
-    for (int p = 0; p < PASSES_K; ++p) {
-      const int e = tid + p * kWaves * kWave;
-      const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
-      const int j = min(k0 + key, kend - 1);   // clamp: never past the last needed key
-      const int blk = s_tbl[j / B - win0];
-      r.k[p] = *reinterpret_cast<const u32x4*>(
-          a.kc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(j % B) * D + piece * 8);
-    }
-#pragma unroll
-    for (int p = 0; p < PASSES_V; ++p) {
-      const int e = tid + p * kWaves * kWave;
-      const int dim = e / VP_PER_ROW, piece = e % VP_PER_ROW;   // piece = 8 keys
-      const int j = min(k0 + 8 * piece, (kend - 1) & ~7);
-      const int blk = s_tbl[j / B - win0];
-      r.v[p] = *reinterpret_cast<const u32x4*>(
-          a.vc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride + static_cast<size_t>(dim) * B + (j % B));
-    }
-  };
-  auto lstore = [&](Regs& r, int stage, int t) {
-    unsigned char* kb = smem + stage * SM::STAGE;
+  // Tiles go from HBM straight into LDS (global_load_lds_dwordx4: lane i of a wave's load
+  // writes 16 bytes at the load's LDS base + 16 i), one stage ahead: tile t+1 is requested
+  // before tile t is multiplied.  Which global 16 bytes a lane fetches implements the LDS
+  // layout: K chunk c of key row k sits at position c ^ kswz(k); V^T chunk g (keys 8g..8g+7)
+  // of dim row d sits at position g ^ vswz(d).
+  auto vswz = [](int row) { return (row >> 1) & (VP_PER_ROW - 1); };
+
+  auto dma = [&](unsigned char* kb, int t) {
     unsigned char* vb = kb + SM::KBYTES;
     const int k0 = t * kKT;
 #pragma unroll
     for (int p = 0; p < PASSES_K; ++p) {
-      const int e = tid + p * kWaves * kWave;
-      const int key = e / KV_PER_ROW, piece = e % KV_PER_ROW;
-      *reinterpret_cast<u32x4*>(kb + key * SM::KROW + ((piece ^ pa::kswz<D>(key)) << 4)) = r.k[p];
+      const int u = w + kWaves * p;                    // this wave's 1 KiB piece of the tile
+      const int e = u * kWave + lane;
+      const int key = e / KV_PER_ROW, pos = e % KV_PER_ROW;
+      const int piece = pos ^ pa::kswz<D>(key);
+      const int j = min(k0 + key, kend - 1);   // clamp: never past the last needed key
+      const int blk = s_tbl[j / B - win0];
+      const uint16_t* src = a.kc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride +
+                            static_cast<size_t>(j % B) * D + piece * 8;
+      pa::load16_to_lds(src, kb + u * (kWave * 16));
     }
-    // Keys at or past kend carry weight 0, but their slots may hold anything (even NaN, and
-    // 0 * NaN = NaN inside the MFMA): zero their V elements (only the last tile has any).
-    const bool tail = k0 + kKT > kend;  // uniform
 #pragma unroll
     for (int p = 0; p < PASSES_V; ++p) {
-      const int e = tid + p * kWaves * kWave;
-      const int dim = e / VP_PER_ROW, piece = e % VP_PER_ROW;
-      u32x4 vv = r.v[p];
-      if (tail) {
-        // element q of the piece (key k0 + 8 piece + q) is kept iff q < nvalid; a 32-bit word
-        // holds elements 2w (low half) and 2w + 1 (high half)
-        const int nvalid = kend - (k0 + 8 * piece);
-        auto keep = [nvalid](uint32_t word, int q) -> uint32_t {
-          return word & ((q < nvalid ? 0x0000FFFFu : 0u) | (q + 1 < nvalid ? 0xFFFF0000u : 0u));
-        };
+      const int u = w + kWaves * p;
+      const int e = u * kWave + lane;
+      const int dim = e / VP_PER_ROW, pos = e % VP_PER_ROW;
+      const int piece = pos ^ vswz(dim);               // 8 keys
+      const int j = min(k0 + 8 * piece, (kend - 1) & ~7);
+      const int blk = s_tbl[j / B - win0];
+      const uint16_t* src = a.vc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride +
+                            static_cast<size_t>(dim) * B + (j % B);
+      pa::load16_to_lds(src, vb + u * (kWave * 16));
+    }
+  };
+  // Keys at or past kend carry weight 0, but their slots may hold anything (even NaN, and
+  // 0 * NaN = NaN inside the MFMA): once the last tile is in LDS, zero its V elements there.
+  auto vfix = [&](unsigned char* base, int t) {
+    unsigned char* vb = base + SM::KBYTES;
+    const int k0 = t * kKT;
+    for (int e = tid; e < VTILE_VECS; e += kWaves * kWave) {
+      const int dim = e / VP_PER_ROW, pos = e % VP_PER_ROW;
+      const int nvalid = kend - (k0 + 8 * (pos ^ vswz(dim)));
+      if (nvalid >= 8) continue;
+      u32x4* pv = reinterpret_cast<u32x4*>(vb + dim * SM::VROW + pos * 16);
+      u32x4 vv = *pv;
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) vv[wd] = keep(vv[wd], 2 * wd);
-      }
-      *reinterpret_cast<u32x4*>(vb + dim * SM::VROW + piece * 16) = vv;
+      for (int wd = 0; wd < 4; ++wd)
+        vv[wd] &= (2 * wd < nvalid ? 0x0000FFFFu : 0u) | (2 * wd + 1 < nvalid ? 0xFFFF0000u : 0u);
+      *pv = vv;
     }
   };
 
@@ -305,7 +301,8 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   #pragma unroll
       for (int ni = 0; ni < NNT; ++ni) {
         const bf16x8 vop = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(vb + (16 * ni + r16) * SM::VROW + (4 * hs + gp) * 16));
+            bf16x8, *reinterpret_cast<const u32x4*>(vb + (16 * ni + r16) * SM::VROW +
+                                                  (((4 * hs + gp) ^ vswz(16 * ni + r16)) * 16)));
   #pragma unroll
         for (int c = 0; c < kNC; ++c)
           o[c][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[c], o[c][ni], 0, 0, 0);
@@ -313,20 +310,20 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
 
   };
 
-  // Iteration t: issue tile t+2's loads into the register set tile t used, multiply tile t
-  // (LDS stage t % 2), store tile t+1 from the other register set into the other stage.
-  auto iteration = [&](Regs& mine, Regs& next, int t) {
-    if (t + 2 < ntiles) {
-      // keys of tile t+2: (t+2)*kKT .. min(kend, (t+3)*kKT) - 1
-      const int last_blk = (min(kend, (t + 3) * kKT) - 1) / B;
+  // Iteration t: request tile t+1 into the other stage (free: tile t-1 used it and the last
+  // barrier ended that), multiply tile t, then wait for the request and publish it.
+  auto iteration = [&](int t, unsigned char* cur, unsigned char* nxt) {
+    if (t + 1 < ntiles) {
+      // keys of tile t+1: (t+1)*kKT .. min(kend, (t+2)*kKT) - 1
+      const int last_blk = (min(kend, (t + 2) * kKT) - 1) / B;
       if (last_blk >= win0 + kTblWin) {  // uniform: move the window (no load reads it now)
-        win0 = ((t + 2) * kKT) / B;
+        win0 = ((t + 1) * kKT) / B;
         load_window(win0);
         __syncthreads();
       }
-      gload(mine, t + 2);
+      dma(nxt, t + 1);
     }
-    const unsigned char* kb = smem + (t & 1) * SM::STAGE;
+    const unsigned char* kb = cur;
     const unsigned char* vb = kb + SM::KBYTES;
     static_assert(kKT == 2 * kSub, "two steps per tile");
     const int k0 = t * kKT;
@@ -336,18 +333,26 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     if (second) qk(kb, 1, s1);
     softmax_pv(vb, k0, 0, s0);
     if (second) softmax_pv(vb, k0 + kSub, 1, s1);
-    if (t + 1 < ntiles) lstore(next, (t + 1) & 1, t + 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's requests for tile t+1 have landed
     __syncthreads();
+    if (t + 1 < ntiles && (t + 2) * kKT > kend) {  // uniform: tile t+1 is the last
+      vfix(nxt, t + 1);
+      __syncthreads();
+    }
   };
 
-  Regs ra, rb;
-  if (ntiles > 0) gload(ra, 0);
-  if (ntiles > 1) gload(rb, 1);
-  if (ntiles > 0) lstore(ra, 0, 0);
+  if (ntiles > 0) {
+    dma(smem0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   __syncthreads();
+  if (ntiles == 1) {
+    vfix(smem0, 0);
+    __syncthreads();
+  }
   for (int t = 0; t < ntiles; t += 2) {
-    iteration(ra, rb, t);
-    if (t + 1 < ntiles) iteration(rb, ra, t + 1);
+    iteration(t, smem0, smem1);
+    if (t + 1 < ntiles) iteration(t + 1, smem1, smem0);
   }
 
   // bad table entries anywhere in the workgroup poison its outputs

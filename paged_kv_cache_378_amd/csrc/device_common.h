@@ -90,6 +90,15 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): lane i writes at
+// lds + 16 i, where lds must be the same for the whole wave.  Asynchronous: counted by vmcnt.
+// The builtin exists only for the device; the host pass sees an empty body.
+__device__ __forceinline__ void load16_to_lds(const void* src, void* lds) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_load_to_lds(const_cast<void*>(src), (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
 // Index of this wave in its workgroup, as a wave-uniform (scalar) value.  Without the
 // readfirstlane the compiler treats threadIdx.x / 64 as divergent, so every loop bounded by
 // it becomes exec-masked vector control flow instead of a scalar loop.

@@ -53,11 +53,15 @@
 namespace pa {
 
 constexpr int kNW = 4;            // waves per workgroup
+constexpr int kXcd = 8;           // XCDs of an MI355X (one work queue each)
 constexpr int kMaxPT = 8192;      // largest partition (tokens)
 constexpr int kMinAutoPT = 256;   // smallest partition the automatic choice uses
 constexpr int kPlanThreads = 256;
 constexpr int kMaxBuckets = kMaxPT / 32 + 1;  // partial partitions bucketed by 32-token tiles
 constexpr int kPlanKeep = 2048;  // sequences whose lengths the plan keeps in LDS between passes
+constexpr int kShareBits = 10;   // first-block set of the sharing test: 1024 slots
+constexpr int kShareSlots = 1 << kShareBits;
+constexpr int kShareProbes = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
@@ -70,7 +74,7 @@ struct DecodeArgs {
   float* part_o;    // [S, Hq, Pmax, D]  partition outputs (normalised)
   float2* part_ml;  // [S, Hq, Pmax]     (max in log2 units, sum)
   int2* items;      // work list: (sequence, partition) entries, longest first; Hkv items each
-  int* queue;       // [0] number of items, [1] next unclaimed item
+  int* queue;       // [0] number of items, [2 + x] next unclaimed slot of XCD x
   int* done;        // [S, Hkv] partitions finished (split sequences), zeroed by the plan
   int S, Hq, Hkv, G, max_blocks, num_blocks, PT, Pmax;
   int len_cap;      // min(max_blocks * B, max_ctx_len): longest context the call may see
@@ -226,17 +230,27 @@ __device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, int s, int 
   return it;
 }
 
-// Persistent work loop: workgroup g starts with item g, then takes items from the shared
-// cursor (which the planning kernel set to the grid size).  The next index is claimed while
-// the current item runs, so the atomic's latency is hidden.  Every workgroup leaves once the
-// cursor passes the item count.
+// Persistent work loop.  Workgroup g starts with item g; the next item is claimed while the
+// current one runs, so the atomic's latency is hidden; every workgroup leaves once the
+// claims pass the item count.  Two ways to claim, chosen by the planner (queue[1]):
+//   * one global cursor (queue[10]): every workgroup takes the next item of the longest-first
+//     list, so the XCDs balance among themselves;
+//   * one queue per XCD (queue[2 + x]), for batches whose sequences share prefix blocks.  The
+//     dispatcher deals workgroups round-robin to the kXcd XCDs, so workgroup g runs on XCD
+//     g % kXcd; queue x holds the items i = c * kXcd + x, c = 0, 1, ... (every kXcd-th item of
+//     the list).  With kXcd | Hkv those are exactly the items of the kv-heads h = x
+//     (mod kXcd): a kv-head's blocks are read through one XCD's L2, where the shared prefix
+//     blocks stay resident.
 template <typename Body>
 __device__ __forceinline__ void for_each_item(const DecodeArgs& a, int* s_next, Body&& body) {
   const int count = a.queue[0];
+  const bool per_xcd = a.queue[1] != 0;
+  const int x = static_cast<int>(blockIdx.x % kXcd);
   int i = blockIdx.x;
   while (i < count) {
     int nxt = 0;
-    if (threadIdx.x == 0) nxt = atomicAdd(&a.queue[1], 1);
+    if (threadIdx.x == 0)
+      nxt = per_xcd ? atomicAdd(&a.queue[2 + x], 1) * kXcd + x : atomicAdd(&a.queue[2 + kXcd], 1);
     const int2 it = a.items[i / a.Hkv];
     body(it.x, i % a.Hkv, it.y);
     if (threadIdx.x == 0) *s_next = nxt;
@@ -654,9 +668,15 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   __shared__ int s_wave[kPlanWaves];
   __shared__ int s_full;               // full partitions counted so far
   __shared__ int s_len[kPlanKeep];     // pass 1's lengths of the first kPlanKeep sequences
+  __shared__ int s_first[kShareSlots];  // open-addressing set of first blocks seen
+  __shared__ int s_dups;                // sequences whose first block another one also has
   const int nbk = a.PT / 32;  // a partial partition has 0 .. PT-1 tokens: buckets 0 .. nbk
   for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
-  if (threadIdx.x == 0) s_full = 0;
+  for (int i = threadIdx.x; i < kShareSlots; i += kPlanThreads) s_first[i] = -1;
+  if (threadIdx.x == 0) {
+    s_full = 0;
+    s_dups = 0;
+  }
   if (a.Pmax > 1)
     for (int i = threadIdx.x; i < a.S * a.Hkv; i += kPlanThreads) a.done[i] = 0;
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -672,6 +692,21 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       if (lens_out) lens_out[s] = raw;
       if (s < kPlanKeep) s_len[s] = raw;
       n = eff_len(raw, a.len_cap, bad);
+      // Prefix sharing shows as one physical first block in several tables.  A set in LDS
+      // (bounded probing, so a full set only undercounts) counts the repeats.
+      const int blk = a.tables[static_cast<size_t>(s) * a.max_blocks];
+      if (blk >= 0) {
+        int h = static_cast<int>((static_cast<uint32_t>(blk) * 2654435761u) >> (32 - kShareBits));
+        for (int k = 0; k < kShareProbes; ++k) {
+          const int old = atomicCAS(&s_first[h], -1, blk);
+          if (old == -1) break;
+          if (old == blk) {
+            atomicAdd(&s_dups, 1);
+            break;
+          }
+          h = (h + 1) & (kShareSlots - 1);
+        }
+      }
     }
     const int full = s < a.S ? n / a.PT : 0, rem = n - full * a.PT;
     const int incl = wave_inclusive_sum(full);
@@ -693,7 +728,11 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     s_base[b] = s_full + above;
     if (b == 0) {
       a.queue[0] = (s_full + above + s_cnt[0]) * a.Hkv;
-      a.queue[1] = grid;
+      // per-XCD queues (kv-head affinity) when at least 1/8 of the sequences share their
+      // first block and the kv-heads split evenly over the XCDs; else one global cursor
+      a.queue[1] = (a.Hkv % kXcd == 0 && 8 * s_dups >= a.S) ? 1 : 0;
+      for (int x = 0; x < kXcd; ++x) a.queue[2 + x] = (grid - x + kXcd - 1) / kXcd;
+      a.queue[2 + kXcd] = grid;
     }
   }
   __syncthreads();

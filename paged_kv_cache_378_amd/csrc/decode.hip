@@ -19,9 +19,11 @@
 //     every full partition, then the partial last partitions by decreasing length.  It runs as
 //     a one-workgroup kernel (pa_decode) or as workgroup 0 of the step's first kernel beside
 //     the cache write (pa_decode_step).  The decode kernel is persistent (about as many
-//     workgroups as the chip holds at once) and pulls items from that list through an atomic
-//     cursor, prefetching the next index while it works on the current one.  No workgroup is
-//     launched for a partition that does not exist, and the short items fill the tail;
+//     workgroups as the chip holds at once) and pulls items from that list through atomic
+//     counters, claiming the next item while it works on the current one; a batch that
+//     shares prefix blocks is claimed per XCD so each kv-head stays in one XCD's L2.  No
+//     workgroup is launched for a partition that does not exist, and the short items fill
+//     the tail;
 //   * the partition's block-table slice is staged in LDS once (loaded together with the
 //     context length), so tile loads never wait on a dependent table load;
 //   * the four wave states are merged through LDS; a single-partition sequence writes its
@@ -643,8 +645,11 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
 // partitions by their length in 32-token tiles, in decreasing order (an empty or invalid
 // context gets one item, which writes NaN).  The list holds one (sequence, partition) entry
 // per partition; item i is entry i / Hkv for kv-head i % Hkv, so the Hkv heads of a partition
-// are consecutive items.  It also sets the persistent kernel's cursor to the grid size
-// (workgroup g starts with item g).  Positions inside a bucket are claimed with LDS atomics,
+// are consecutive items.  It also picks how the persistent kernel claims items (one global
+// cursor, or one queue per XCD when sequences share prefix blocks) and sets the claim
+// counters past the items the grid starts with (workgroup g starts with item g).  When
+// partitions will be merged it zeroes the merge counters.  Positions inside a bucket are
+// claimed with LDS atomics,
 // so the order inside a bucket can change from call to call; results do not depend on it
 // (each item's output has a fixed place).
 // ---------------------------------------------------------------------------------------

@@ -205,3 +205,81 @@ def test_fused_step_rejects_pageable_metadata(gpu):
     assert torch.equal(out.view(torch.int32), before[0].view(torch.int32))
     assert torch.equal(st.k_cache.view(torch.int32), before[1].view(torch.int32))
     assert torch.equal(tables_d, before[2])
+
+
+@pytest.mark.parametrize("where", ["pinned+pinned", "device+pinned", "pinned+device", "same"])
+def test_fused_step_padding_bad_length_and_mixed_memory(gpu, where):
+    """A padded slot (-1, its sequence keeping its old length) and an invalid length (0) inside
+    one fused step, with the slots and lengths in any mix of device and pinned host memory (or
+    new_ctx_lens == ctx_lens): outputs, pools and tables are bit-identical to pa_cache_append
+    followed by pa_decode, the padded token is not written, and the bad sequence's output is
+    NaN while the others are finite."""
+    from paged_kv_cache_378_amd import _lib
+    from paged_kv_cache_378_amd.runner import PagedState
+    w = wl.custom_decode("stepedge", 45, [5, 17, 33, 64, 100], 16, 8, 128, 16, "bf16",
+                         extra_blocks=8)
+    print(f"[gpu] fused step edge cases ({where})", flush=True)
+    S, B = w.num_seqs, w.block_size
+    ids = w.step_ids
+    max_ctx = max(w.ctx_lens()) + 1
+    max_blocks = (max_ctx + B - 1) // B
+    outs, states, tabs = [], [], []
+    kn, vn = (x.cuda() for x in step_values(w, 0, S))
+    for fused in (False, True):
+        st = PagedState(w, "cuda", poison=True)
+        t, l = (torch.from_numpy(x).cuda() for x in st.bm.block_tables(ids, max_blocks))
+        slots, pairs = st.bm.append_slots(ids, 1)
+        assert len(pairs) == 0
+        lens = st.bm.seq_lens(ids).copy()
+        slots = slots.copy()
+        slots[1] = -1          # padding: nothing written, no table entry ...
+        lens[1] -= 1           # ... and the sequence keeps its old length
+        lens[2] = 0            # invalid length: NaN output for sequence 2
+        ws = torch.empty(_lib.pa_decode_workspace_size(S, w.hq, w.head_dim, max_ctx, 0),
+                         dtype=torch.uint8, device="cuda")
+        out = st.new_out()
+        if not fused:
+            l.copy_(torch.from_numpy(lens))
+            _lib.pa_cache_append(kn, vn, st.k_cache, st.v_cache, torch.from_numpy(slots).cuda(),
+                                 t, l)
+            _lib.pa_decode(out, st.vals["q"], st.k_cache, st.v_cache, t, l, max_ctx, w.scale,
+                           0, ws)
+        else:
+            ps = torch.from_numpy(slots).pin_memory()
+            pl = torch.from_numpy(lens).pin_memory()
+            if where == "device+pinned":
+                ps = ps.cuda()
+            if where == "pinned+device":
+                pl = pl.cuda()
+            if where == "same":
+                l.copy_(torch.from_numpy(lens))
+                pl = l
+            _lib.pa_decode_step(out, st.vals["q"], kn, vn, st.k_cache, st.v_cache, ps, t, l,
+                                max_ctx, w.scale, 0, ws, new_ctx_lens=pl)
+        torch.cuda.synchronize()
+        outs.append(out)
+        states.append(st)
+        tabs.append((t, l))
+    it = torch.int16
+    assert torch.equal(outs[0].view(it), outs[1].view(it))
+    assert torch.equal(tabs[0][0], tabs[1][0]) and torch.equal(tabs[0][1], tabs[1][1])
+    assert torch.equal(states[0].k_cache.view(it), states[1].k_cache.view(it))
+    assert torch.equal(states[0].v_cache.view(it), states[1].v_cache.view(it))
+    o = outs[1].float()
+    assert torch.isnan(o[2]).all()
+    assert torch.isfinite(o[[0, 1, 3, 4]]).all()
+
+
+def test_fused_step_empty_batch(gpu):
+    """S = 0 returns without launching anything."""
+    from paged_kv_cache_378_amd import _lib
+    H, D, B, NB = 4, 64, 16, 8
+    kc = torch.zeros((NB, H, B, D), dtype=torch.float32, device="cuda")
+    vc = torch.zeros((NB, H, D, B), dtype=torch.float32, device="cuda")
+    q = torch.zeros((0, H, D), dtype=torch.float32, device="cuda")
+    kv = torch.zeros((0, H, D), dtype=torch.float32, device="cuda")
+    z = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    t = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
+    _lib.pa_decode_step(torch.empty_like(q), q, kv, kv, kc, vc, z, t, z, 32, 0.125)
+    torch.cuda.synchronize()
+    assert not kc.any() and not vc.any()

@@ -56,7 +56,8 @@ enum {
   PA_ERR_SEQ_EXISTS = -4,    /* a sequence id that is already in use                       */
   PA_ERR_UNSUPPORTED = -5,   /* dtype / head_dim / block size / group combination not built */
   PA_ERR_WORKSPACE = -6,     /* workspace missing or smaller than the size query returned  */
-  PA_ERR_HIP = -7            /* the HIP runtime reported an error at launch                */
+  PA_ERR_HIP = -7,           /* the HIP runtime reported an error at launch                */
+  PA_ERR_SWAPPED = -8        /* the sequence is swapped out (pa_bm_swap_in it first)       */
 };
 
 enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
@@ -105,6 +106,10 @@ typedef struct {
   int64_t cow_copies;       /* block copies issued by copy-on-write so far                */
   double usage;             /* used_blocks / num_blocks: the pool saturation to monitor,
                                [TT] "Summing it Up", item 3                                */
+  int32_t swapped_seqs;     /* sequences swapped out (not counted in num_seqs)            */
+  int64_t swapped_tokens;   /* tokens those sequences hold in host memory                 */
+  int64_t swap_outs;        /* pa_bm_swap_out calls so far                                */
+  int64_t swap_ins;         /* pa_bm_swap_in calls so far                                 */
 } pa_bm_stats_t;
 
 /* Create a manager over physical blocks [0, num_blocks) of block_size tokens each.
@@ -165,6 +170,37 @@ pa_status pa_bm_free_list(pa_bm* bm, int32_t* out, int32_t cap, int32_t* n_out);
 
 /* Pool statistics ([TT] "Summing it Up": monitor the physical block pool saturation). */
 pa_status pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out);
+
+/* Preemption by swapping ([TT] "Infrastructure Scale": when the pool runs out of physical
+ * blocks, a request can be paused and its KV-cache moved to CPU RAM).
+ *
+ * pa_bm_swap_out: *n_out receives k = ceil(len / B), and blocks_out[0..k) the sequence's
+ * physical blocks in logical order, as they are before the call.  Its references are then
+ * released as in pa_bm_free_seq (blocks reaching count zero rejoin the pool in logical order),
+ * and the sequence is swapped: it keeps its id and length and holds no blocks.  The caller
+ * copies those k blocks to host memory (pa_swap_blocks, to_host = 1) before anything can
+ * write into them again -- enqueued on the stream that later writes run on, that is
+ * automatic.  Only pa_bm_swap_in, pa_bm_free_seq, pa_bm_seq_len and pa_bm_seq_lens accept a
+ * swapped sequence; the other calls return PA_ERR_SWAPPED.  PA_ERR_INVALID_ARG if cap < k
+ * (*n_out still receives k; nothing changes).
+ *
+ * pa_bm_swap_in: the swapped sequence takes k fresh blocks from the front of the pool, in
+ * logical order, each with count 1, written to blocks_out (k to *n_out).  Blocks it shared
+ * before the swap come back as private copies.  The caller copies the saved K/V into them
+ * (pa_swap_blocks, to_host = 0) before a kernel reads the sequence.  PA_ERR_OUT_OF_BLOCKS if
+ * fewer than k blocks are free, PA_ERR_INVALID_ARG if the sequence is live or cap < k;
+ * nothing changes on error. */
+pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq_id, int32_t* blocks_out, int32_t cap,
+                         int32_t* n_out);
+pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq_id, int32_t* blocks_out, int32_t cap,
+                        int32_t* n_out);
+
+/* Truncate a live sequence to its first n_keep tokens (0 <= n_keep <= len), e.g. to roll back
+ * rejected speculative tokens.  Blocks past ceil(n_keep / B) are released in logical order
+ * (blocks reaching count zero rejoin the pool).  A kept last block that is shared stays
+ * shared; the next append copies it first, as for any shared partial block.  No device work:
+ * slots past the new length are simply never read. */
+pa_status pa_bm_truncate(pa_bm* bm, int64_t seq_id, int32_t n_keep);
 
 /* ---- host utilities ---------------------------------------------------------------- */
 
@@ -287,6 +323,22 @@ pa_status pa_decode_step(void* out, const void* q, const void* key, const void* 
                          int32_t num_blocks, int32_t max_blocks, int32_t max_ctx_len, float scale,
                          int32_t dtype, int32_t partition_tokens, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Whole-block copies between the pools and host memory, for swapping a paused request's
+ * KV-cache to CPU RAM and back ([TT] "Infrastructure Scale"; pa_bm_swap_out / pa_bm_swap_in
+ * give the block lists).
+ * host: page-locked host memory (hipHostMalloc, a pinned torch tensor) of n * 2 * Hkv * B * D
+ *   elements of dtype: block i's K slab (its [Hkv, B, D] part of the K pool, laid out as
+ *   there) followed by its V slab ([Hkv, D, B]).  The kernel reads or writes it directly over
+ *   the bus; nothing else may touch it until the copy has completed on the stream.
+ * blocks: int32 [n] physical block ids, device memory or page-locked host memory; ids outside
+ *   [0, num_blocks) are skipped.
+ * to_host = 1: pools -> host (swap out); 0: host -> pools (swap in).
+ * Errors: PA_ERR_INVALID_ARG for a pageable or device `host`, a pageable `blocks`, NULL or
+ * misaligned pointers; PA_ERR_UNSUPPORTED for shapes the pools do not support. */
+pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host, const int32_t* blocks,
+                         int32_t n, int32_t to_host, int32_t Hkv, int32_t D, int32_t B,
+                         int32_t num_blocks, int32_t dtype, void* stream);
 
 /* Chunked-query paged attention (prefill of the tokens past a cached prefix, [KC]
  * "RadixAttention": only the tokens past the divergence need a prefill pass).  Each of the S

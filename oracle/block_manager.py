@@ -31,6 +31,20 @@ the specification of the C++ block manager, which must match it bit for bit):
   place); a copy duplicates the whole block;
 * a batch may name a sequence only once;
 * every call is all-or-nothing: on any error nothing changes.
+
+Preemption (Taming the Tail, "Infrastructure Scale": when the pool runs out of
+physical blocks, a request can be paused and its KV-cache moved to CPU RAM) and
+truncation, read plainly:
+
+* swapping a sequence out hands back its physical blocks in logical order (their
+  contents are what goes to host memory), then drops its references as freeing
+  it would; the sequence keeps its id and length and holds no blocks;
+* swapping it back in takes ceil(n / B) fresh blocks from the front of the pool,
+  each with count 1 (blocks shared before the swap come back as private copies
+  of the same contents);
+* truncating to n_keep tokens drops the references of the blocks past
+  ceil(n_keep / B), in logical order; a shared kept block stays shared until
+  the next write copies it.
 """
 
 from __future__ import annotations
@@ -59,6 +73,10 @@ class SeqExists(BlockManagerError):
     status = -4
 
 
+class Swapped(BlockManagerError):
+    status = -8
+
+
 class _Seq:
     __slots__ = ("blocks", "n")
 
@@ -81,8 +99,11 @@ class BlockManagerModel:
         self.free = deque(order)
         self.ref = [0] * num_blocks
         self.seqs: dict[int, _Seq] = {}
+        self.swapped: dict[int, int] = {}  # swapped-out sequence -> its length
         self.forks = 0
         self.cow_copies = 0
+        self.swap_outs = 0
+        self.swap_ins = 0
 
     # -- internal helpers -------------------------------------------------
     def _take(self) -> int:
@@ -119,17 +140,24 @@ class BlockManagerModel:
     def _transaction(self, fn):
         """Run ``fn`` on the live state; restore everything if it raises."""
         saved = (copy.deepcopy(self.seqs), list(self.ref), deque(self.free),
-                 self.forks, self.cow_copies)
+                 self.forks, self.cow_copies, dict(self.swapped))
         try:
             return fn()
         except BlockManagerError:
-            self.seqs, self.ref, self.free, self.forks, self.cow_copies = saved
+            self.seqs, self.ref, self.free, self.forks, self.cow_copies, self.swapped = saved
             raise
+
+    def _live(self, seq_id: int) -> _Seq:
+        if seq_id in self.seqs:
+            return self.seqs[seq_id]
+        if seq_id in self.swapped:
+            raise Swapped(seq_id)
+        raise UnknownSeq(seq_id)
 
     # -- API ----------------------------------------------------------------
     def add_seq(self, seq_id: int, n_tokens: int) -> list[int]:
         """New sequence holding ``n_tokens`` tokens (a prefill); returns their slots."""
-        if seq_id in self.seqs:
+        if seq_id in self.seqs or seq_id in self.swapped:
             raise SeqExists(seq_id)
         if n_tokens < 0:
             raise InvalidArg("n_tokens < 0")
@@ -151,11 +179,12 @@ class BlockManagerModel:
         ids = [int(s) for s in seq_ids]
         if tokens_each < 0:
             raise InvalidArg("tokens_each < 0")
-        if len(set(ids)) != len(ids):
-            raise InvalidArg("a batch may name a sequence only once")
-        for s in ids:
-            if s not in self.seqs:
-                raise UnknownSeq(s)
+        seen = set()
+        for s in ids:  # in batch order: the first unknown, swapped or repeated id decides
+            self._live(s)
+            if s in seen:
+                raise InvalidArg("a batch may name a sequence only once")
+            seen.add(s)
 
         def run():
             slots: list[int] = []
@@ -170,11 +199,9 @@ class BlockManagerModel:
 
     def fork(self, parent: int, child: int) -> None:
         """Child shares every block of the parent (no copy); counts go up by one."""
-        if parent not in self.seqs:
-            raise UnknownSeq(parent)
-        if child in self.seqs:
+        src = self._live(parent)
+        if child in self.seqs or child in self.swapped:
             raise SeqExists(child)
-        src = self.seqs[parent]
         seq = _Seq()
         seq.blocks = list(src.blocks)
         seq.n = src.n
@@ -185,6 +212,9 @@ class BlockManagerModel:
 
     def free_seq(self, seq_id: int) -> None:
         """Drop a sequence; blocks whose count reaches zero rejoin the pool."""
+        if seq_id in self.swapped:  # holds no blocks
+            del self.swapped[seq_id]
+            return
         if seq_id not in self.seqs:
             raise UnknownSeq(seq_id)
         seq = self.seqs.pop(seq_id)
@@ -195,14 +225,63 @@ class BlockManagerModel:
         """Per-sequence rows of physical block ids, padded with -1, and lengths."""
         rows, lens = [], []
         for s in seq_ids:
-            if s not in self.seqs:
-                raise UnknownSeq(s)
-            seq = self.seqs[s]
+            seq = self._live(s)
             if len(seq.blocks) > max_blocks:
                 raise InvalidArg("sequence needs more than max_blocks blocks")
             rows.append(seq.blocks + [-1] * (max_blocks - len(seq.blocks)))
             lens.append(seq.n)
         return rows, lens
+
+    def seq_len(self, seq_id: int) -> int:
+        if seq_id in self.swapped:
+            return self.swapped[seq_id]
+        if seq_id not in self.seqs:
+            raise UnknownSeq(seq_id)
+        return self.seqs[seq_id].n
+
+    def swap_out(self, seq_id: int) -> list[int]:
+        """Pause a sequence: returns its physical blocks in logical order (the contents
+        to keep in host memory) and drops its references as freeing it would."""
+        if seq_id in self.swapped:
+            raise Swapped(seq_id)
+        if seq_id not in self.seqs:
+            raise UnknownSeq(seq_id)
+        seq = self.seqs.pop(seq_id)
+        for b in seq.blocks:
+            self._release(b)
+        self.swapped[seq_id] = seq.n
+        self.swap_outs += 1
+        return list(seq.blocks)
+
+    def swap_in(self, seq_id: int) -> list[int]:
+        """Resume a swapped sequence on ceil(n / B) fresh private blocks; returns them in
+        logical order (where its saved contents go back)."""
+        if seq_id in self.seqs:
+            raise InvalidArg("sequence is not swapped out")
+        if seq_id not in self.swapped:
+            raise UnknownSeq(seq_id)
+        n = self.swapped[seq_id]
+        k = -(-n // self.block_size)
+        if k > len(self.free):
+            raise OutOfBlocks("free pool too small for the swap-in")
+        seq = _Seq()
+        seq.blocks = [self._take() for _ in range(k)]
+        seq.n = n
+        del self.swapped[seq_id]
+        self.seqs[seq_id] = seq
+        self.swap_ins += 1
+        return list(seq.blocks)
+
+    def truncate(self, seq_id: int, n_keep: int) -> None:
+        """Keep the first ``n_keep`` tokens; blocks past them lose this reference."""
+        seq = self._live(seq_id)
+        if not 0 <= n_keep <= seq.n:
+            raise InvalidArg("n_keep outside [0, n]")
+        keep = -(-n_keep // self.block_size)
+        for b in seq.blocks[keep:]:
+            self._release(b)
+        del seq.blocks[keep:]
+        seq.n = n_keep
 
     def refcount(self, block: int) -> int:
         if not 0 <= block < self.num_blocks:
@@ -225,4 +304,8 @@ class BlockManagerModel:
             "tail_waste_slots": logical_blocks * B - tokens,
             "forks": self.forks,
             "cow_copies": self.cow_copies,
+            "swapped_seqs": len(self.swapped),
+            "swapped_tokens": sum(self.swapped.values()),
+            "swap_outs": self.swap_outs,
+            "swap_ins": self.swap_ins,
         }

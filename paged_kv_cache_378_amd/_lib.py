@@ -35,6 +35,7 @@ PA_ERR_SEQ_EXISTS = -4
 PA_ERR_UNSUPPORTED = -5
 PA_ERR_WORKSPACE = -6
 PA_ERR_HIP = -7
+PA_ERR_SWAPPED = -8
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 
@@ -61,15 +62,21 @@ class SeqExists(PaError):
     pass
 
 
+class Swapped(PaError):
+    pass
+
+
 _ERRORS = {PA_ERR_OUT_OF_BLOCKS: OutOfBlocks, PA_ERR_UNKNOWN_SEQ: UnknownSeq,
-           PA_ERR_SEQ_EXISTS: SeqExists}
+           PA_ERR_SEQ_EXISTS: SeqExists, PA_ERR_SWAPPED: Swapped}
 
 
 class pa_bm_stats_t(C.Structure):
     _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("free_blocks", _i32),
                 ("used_blocks", _i32), ("shared_blocks", _i32), ("num_seqs", _i32),
                 ("logical_blocks", _i64), ("live_tokens", _i64), ("tail_waste_slots", _i64),
-                ("forks", _i64), ("cow_copies", _i64), ("usage", C.c_double)]
+                ("forks", _i64), ("cow_copies", _i64), ("usage", C.c_double),
+                ("swapped_seqs", _i32), ("swapped_tokens", _i64), ("swap_outs", _i64),
+                ("swap_ins", _i64)]
 
 
 class pa_accounting_t(C.Structure):
@@ -93,6 +100,9 @@ _SIGS = {
     "pa_bm_refcount": ([_vp, _i32, _pi32], _i32),
     "pa_bm_free_list": ([_vp, _pi32, _i32, _pi32], _i32),
     "pa_bm_stats": ([_vp, C.POINTER(pa_bm_stats_t)], _i32),
+    "pa_bm_swap_out": ([_vp, _i64, _pi32, _i32, _pi32], _i32),
+    "pa_bm_swap_in": ([_vp, _i64, _pi32, _i32, _pi32], _i32),
+    "pa_bm_truncate": ([_vp, _i64, _i32], _i32),
     "pa_accounting": ([_pi32, _i32, _i32, _i32, C.POINTER(pa_accounting_t)], _i32),
     "pa_validate_tables": ([_pi32, _pi32, _i32, _i32, _i32, _i32], _i32),
     "pa_cache_write": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
@@ -104,6 +114,7 @@ _SIGS = {
                    _f32, _i32, _i32, _vp, _sz, _vp], _i32),
     "pa_decode_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                         _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "pa_swap_blocks": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "pa_chunk_attend": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _vp], _i32),
 }
@@ -217,6 +228,24 @@ def pa_bm_stats(h) -> dict:
     return {name: getattr(st, name) for name, _ in pa_bm_stats_t._fields_}
 
 
+def pa_bm_swap_out(h, seq_id: int, cap: int) -> np.ndarray:
+    out = np.empty(max(cap, 1), np.int32)
+    n = _i32()
+    _check(_lib.pa_bm_swap_out(h, seq_id, _ptr32(out), cap, C.byref(n)))
+    return out[:n.value].copy()
+
+
+def pa_bm_swap_in(h, seq_id: int, cap: int) -> np.ndarray:
+    out = np.empty(max(cap, 1), np.int32)
+    n = _i32()
+    _check(_lib.pa_bm_swap_in(h, seq_id, _ptr32(out), cap, C.byref(n)))
+    return out[:n.value].copy()
+
+
+def pa_bm_truncate(h, seq_id: int, n_keep: int) -> None:
+    _check(_lib.pa_bm_truncate(h, seq_id, n_keep))
+
+
 def pa_accounting(lens, block_size: int, max_seq_len: int) -> dict:
     a = _i32_host(lens)
     r = pa_accounting_t()
@@ -274,6 +303,20 @@ class BlockManager:
 
     def stats(self):
         return pa_bm_stats(self.h)
+
+    def _blocks_of(self, seq_id):
+        return -(-self.seq_len(seq_id) // self.block_size)
+
+    def swap_out(self, seq_id):
+        """The sequence's physical blocks (logical order) to copy to host memory."""
+        return pa_bm_swap_out(self.h, seq_id, self._blocks_of(seq_id))
+
+    def swap_in(self, seq_id):
+        """The fresh blocks (logical order) its saved contents go back into."""
+        return pa_bm_swap_in(self.h, seq_id, self._blocks_of(seq_id))
+
+    def truncate(self, seq_id, n_keep):
+        pa_bm_truncate(self.h, seq_id, n_keep)
 
 
 # -- device operations (torch tensors in, nothing computed here) -----------------------
@@ -433,6 +476,20 @@ def pa_decode_step(out, q, key, value, k_cache, v_cache, slot_mapping, block_tab
                                _dev(ctx_lens, "ctx_lens", torch.int32), new_ptr, S, Hq, Hkv, D, B,
                                NB, block_tables.shape[1], max_ctx_len, float(scale),
                                _dtype_code(q), partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_swap_blocks(k_cache, v_cache, host, blocks, to_host: bool, stream=None) -> None:
+    """host: pinned CPU tensor of len(blocks) * 2 * Hkv * B * D elements of the pools' dtype;
+    blocks: int32 device tensor or pinned CPU tensor."""
+    NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
+    n = blocks.numel()
+    if host.is_cuda or not host.is_pinned() or not host.is_contiguous() or \
+            host.dtype != k_cache.dtype or host.numel() < n * 2 * Hkv * B * D:
+        raise PaError(PA_ERR_INVALID_ARG, "host must be a pinned contiguous CPU tensor of the "
+                                          "pools' dtype holding 2 * n block slabs")
+    _check(_lib.pa_swap_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), host.data_ptr(),
+                               _step_input(blocks, "blocks"), n, 1 if to_host else 0, Hkv, D, B,
+                               NB, _dtype_code(k_cache), _stream(stream)))
 
 
 def pa_chunk_attend(out, q, k_cache, v_cache, block_tables, ctx_lens, scale: float,

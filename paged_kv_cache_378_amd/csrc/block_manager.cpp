@@ -43,8 +43,11 @@ struct pa_bm {
   int32_t head = 0;           // index of the front of the pool in `ring`
   int32_t nfree = 0;
   std::unordered_map<int64_t, Seq> seqs;
+  std::unordered_map<int64_t, int32_t> swapped;  // swapped-out sequence -> its length
   int64_t forks = 0;
   int64_t cow_copies = 0;
+  int64_t swap_outs = 0;
+  int64_t swap_ins = 0;
 
   int32_t take() {  // caller guarantees nfree > 0
     int32_t b = ring[head];
@@ -62,6 +65,7 @@ struct pa_bm {
     }
   }
   // New blocks a sequence of n tokens needs to grow by k tokens (block boundaries crossed).
+  bool is_swapped(int64_t id) const { return swapped.count(id) != 0; }
   int64_t boundary_blocks(int32_t n, int32_t k) const {
     if (k <= 0) return 0;
     // positions n .. n+k-1 that are multiples of B
@@ -123,7 +127,7 @@ pa_status pa_bm_destroy(pa_bm* bm) {
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id, int32_t n_tokens, int32_t* slots_out) {
   if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: NULL handle");
   if (n_tokens < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: n_tokens %d < 0", n_tokens);
-  if (bm->seqs.count(seq_id))
+  if (bm->seqs.count(seq_id) || bm->is_swapped(seq_id))
     return fail(PA_ERR_SEQ_EXISTS, "pa_bm_add_seq: sequence %lld exists", (long long)seq_id);
   const int64_t need = bm->boundary_blocks(0, n_tokens);
   if (need > bm->nfree)
@@ -170,8 +174,11 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
     for (int32_t i = 0; i < n_seqs; ++i) {
       auto it = bm->seqs.find(seq_ids[i]);
       if (it == bm->seqs.end())
-        return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_append_slots: unknown sequence %lld",
-                    (long long)seq_ids[i]);
+        return bm->is_swapped(seq_ids[i])
+                   ? fail(PA_ERR_SWAPPED, "pa_bm_append_slots: sequence %lld is swapped out",
+                          (long long)seq_ids[i])
+                   : fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_append_slots: unknown sequence %lld",
+                          (long long)seq_ids[i]);
       if (!seen.insert(seq_ids[i]).second)
         return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: sequence %lld repeats in the batch",
                     (long long)seq_ids[i]);
@@ -241,8 +248,10 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
   if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_fork: NULL handle");
   auto it = bm->seqs.find(parent_id);
   if (it == bm->seqs.end())
-    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_fork: unknown parent %lld", (long long)parent_id);
-  if (bm->seqs.count(child_id))
+    return bm->is_swapped(parent_id)
+               ? fail(PA_ERR_SWAPPED, "pa_bm_fork: parent %lld is swapped out", (long long)parent_id)
+               : fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_fork: unknown parent %lld", (long long)parent_id);
+  if (bm->seqs.count(child_id) || bm->is_swapped(child_id))
     return fail(PA_ERR_SEQ_EXISTS, "pa_bm_fork: child %lld exists", (long long)child_id);
   try {
     Seq child = it->second;  // copy of table and length
@@ -258,8 +267,10 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
 pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
   if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_free_seq: NULL handle");
   auto it = bm->seqs.find(seq_id);
-  if (it == bm->seqs.end())
+  if (it == bm->seqs.end()) {
+    if (bm->swapped.erase(seq_id)) return ok();  // a swapped sequence holds no blocks
     return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_free_seq: unknown sequence %lld", (long long)seq_id);
+  }
   for (int32_t b : it->second.blocks) bm->release(b);
   bm->seqs.erase(it);
   return ok();
@@ -275,8 +286,11 @@ pa_status pa_bm_block_tables(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end())
-      return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_block_tables: unknown sequence %lld",
-                  (long long)seq_ids[i]);
+      return bm->is_swapped(seq_ids[i])
+                 ? fail(PA_ERR_SWAPPED, "pa_bm_block_tables: sequence %lld is swapped out",
+                        (long long)seq_ids[i])
+                 : fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_block_tables: unknown sequence %lld",
+                        (long long)seq_ids[i]);
     if (static_cast<int64_t>(it->second.blocks.size()) > max_blocks)
       return fail(PA_ERR_INVALID_ARG, "pa_bm_block_tables: sequence %lld holds %zu blocks > %d",
                   (long long)seq_ids[i], it->second.blocks.size(), max_blocks);
@@ -295,8 +309,13 @@ pa_status pa_bm_block_tables(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32
 pa_status pa_bm_seq_len(pa_bm* bm, int64_t seq_id, int32_t* n_out) {
   if (!bm || !n_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_seq_len: NULL argument");
   auto it = bm->seqs.find(seq_id);
-  if (it == bm->seqs.end())
-    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_seq_len: unknown sequence %lld", (long long)seq_id);
+  if (it == bm->seqs.end()) {
+    auto sw = bm->swapped.find(seq_id);
+    if (sw == bm->swapped.end())
+      return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_seq_len: unknown sequence %lld", (long long)seq_id);
+    *n_out = sw->second;
+    return ok();
+  }
   *n_out = it->second.n;
   return ok();
 }
@@ -307,8 +326,14 @@ pa_status pa_bm_seq_lens(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* 
   if (n > 0 && (!seq_ids || !lens_out)) return fail(PA_ERR_INVALID_ARG, "pa_bm_seq_lens: NULL array");
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
-    if (it == bm->seqs.end())
-      return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_seq_lens: unknown sequence %lld", (long long)seq_ids[i]);
+    if (it == bm->seqs.end()) {
+      auto sw = bm->swapped.find(seq_ids[i]);
+      if (sw == bm->swapped.end())
+        return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_seq_lens: unknown sequence %lld",
+                    (long long)seq_ids[i]);
+      lens_out[i] = sw->second;
+      continue;
+    }
     lens_out[i] = it->second.n;
   }
   return ok();
@@ -355,7 +380,90 @@ pa_status pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out) {
   st.forks = bm->forks;
   st.cow_copies = bm->cow_copies;
   st.usage = static_cast<double>(st.used_blocks) / bm->num_blocks;
+  st.swapped_seqs = static_cast<int32_t>(bm->swapped.size());
+  for (const auto& kv : bm->swapped) st.swapped_tokens += kv.second;
+  st.swap_outs = bm->swap_outs;
+  st.swap_ins = bm->swap_ins;
   *out = st;
+  return ok();
+}
+
+pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq_id, int32_t* blocks_out, int32_t cap,
+                         int32_t* n_out) {
+  if (!bm || !n_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_swap_out: NULL argument");
+  *n_out = 0;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return bm->is_swapped(seq_id)
+               ? fail(PA_ERR_SWAPPED, "pa_bm_swap_out: sequence %lld is already swapped out",
+                      (long long)seq_id)
+               : fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_swap_out: unknown sequence %lld", (long long)seq_id);
+  const auto& blocks = it->second.blocks;
+  const int32_t k = static_cast<int32_t>(blocks.size());
+  *n_out = k;
+  if (cap < k || (k > 0 && !blocks_out))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_swap_out: %d blocks, capacity %d", k, cap);
+  try {
+    bm->swapped.reserve(bm->swapped.size() + 1);
+    bm->swapped.emplace(seq_id, it->second.n);
+  } catch (...) {
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_swap_out: out of host memory");
+  }
+  for (int32_t i = 0; i < k; ++i) blocks_out[i] = blocks[i];
+  for (int32_t b : blocks) bm->release(b);
+  bm->seqs.erase(it);
+  ++bm->swap_outs;
+  return ok();
+}
+
+pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq_id, int32_t* blocks_out, int32_t cap,
+                        int32_t* n_out) {
+  if (!bm || !n_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_swap_in: NULL argument");
+  *n_out = 0;
+  auto sw = bm->swapped.find(seq_id);
+  if (sw == bm->swapped.end())
+    return bm->seqs.count(seq_id)
+               ? fail(PA_ERR_INVALID_ARG, "pa_bm_swap_in: sequence %lld is not swapped out",
+                      (long long)seq_id)
+               : fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_swap_in: unknown sequence %lld", (long long)seq_id);
+  const int32_t n = sw->second;
+  const int32_t k = static_cast<int32_t>(bm->boundary_blocks(0, n));
+  *n_out = k;
+  if (cap < k || (k > 0 && !blocks_out))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_swap_in: %d blocks, capacity %d", k, cap);
+  if (k > bm->nfree)
+    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_swap_in: needs %d blocks, %d free", k, bm->nfree);
+  try {
+    Seq s;
+    s.blocks.reserve(k);
+    bm->seqs.reserve(bm->seqs.size() + 1);
+    for (int32_t i = 0; i < k; ++i) s.blocks.push_back(bm->take());
+    s.n = n;
+    for (int32_t i = 0; i < k; ++i) blocks_out[i] = s.blocks[i];
+    bm->seqs.emplace(seq_id, std::move(s));
+  } catch (...) {
+    // Unreachable in practice (the capacities are reserved first).
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_swap_in: out of host memory");
+  }
+  bm->swapped.erase(sw);
+  ++bm->swap_ins;
+  return ok();
+}
+
+pa_status pa_bm_truncate(pa_bm* bm, int64_t seq_id, int32_t n_keep) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_truncate: NULL handle");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return bm->is_swapped(seq_id)
+               ? fail(PA_ERR_SWAPPED, "pa_bm_truncate: sequence %lld is swapped out", (long long)seq_id)
+               : fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_truncate: unknown sequence %lld", (long long)seq_id);
+  Seq& s = it->second;
+  if (n_keep < 0 || n_keep > s.n)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_truncate: n_keep %d outside [0, %d]", n_keep, s.n);
+  const size_t keep = static_cast<size_t>(bm->boundary_blocks(0, n_keep));
+  for (size_t i = keep; i < s.blocks.size(); ++i) bm->release(s.blocks[i]);
+  s.blocks.resize(keep);
+  s.n = n_keep;
   return ok();
 }
 

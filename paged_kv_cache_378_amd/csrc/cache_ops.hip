@@ -1,11 +1,14 @@
-// Cache write (slot scatter) and copy-on-write block copy on gfx950.
+// Cache write (slot scatter), copy-on-write block copy and swap copies on gfx950.
 //
 // Cache write: the device function in cache_write.h.  Block copy: KV-cache chapter,
 // "PagedAttention: borrowing virtual memory" -- a writer into a shared block first gets a
-// private copy.  Both are pure bit copies and HBM-bound.
+// private copy.  Both are pure bit copies and HBM-bound.  Swap copies: "Taming the Tail",
+// "Infrastructure Scale" -- a paused request's KV-cache moves to CPU RAM and back; whole
+// blocks between the pools and page-locked host memory, bound by the host link.
 
 #include "cache_write.h"
 #include "device_common.h"
+#include "host_memory.h"
 
 namespace pa {
 
@@ -32,6 +35,40 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
     const uint4 b = vs[i];
     kd[i] = a;
     vd[i] = b;
+  }
+}
+
+// One workgroup per (block, K or V slab).  A block's K slab ([Hkv, B, D]) and V slab
+// ([Hkv, D, B]) are each contiguous in their pool; the host buffer holds block i's K slab then
+// its V slab.  to_host: pool -> host with ordinary stores (written back over the bus when the
+// kernel ends); else host -> pool with system-scope 8-byte loads, which never use a line an
+// earlier kernel left in a GPU cache.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(uint4* __restrict__ k_cache,
+                                                          uint4* __restrict__ v_cache,
+                                                          uint4* __restrict__ host,
+                                                          const int32_t* __restrict__ blocks,
+                                                          int num_blocks, int64_t slab_vecs,
+                                                          int to_host, int blocks_on_host) {
+  const int64_t i = blockIdx.x;
+  const int which = blockIdx.y;  // 0: K, 1: V
+  const int32_t blk = ld_step(blocks + i, blocks_on_host != 0);
+  if (blk < 0 || blk >= num_blocks) return;  // outside the pool: skipped
+  uint4* pool = (which == 0 ? k_cache : v_cache) + static_cast<int64_t>(blk) * slab_vecs;
+  uint4* hb = host + (2 * i + which) * slab_vecs;
+  if (to_host) {
+    for (int64_t e = threadIdx.x; e < slab_vecs; e += blockDim.x) hb[e] = pool[e];
+  } else {
+    const uint64_t* src = reinterpret_cast<const uint64_t*>(hb);
+    for (int64_t e = threadIdx.x; e < slab_vecs; e += blockDim.x) {
+      const uint64_t lo = __hip_atomic_load(src + 2 * e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const uint64_t hi = __hip_atomic_load(src + 2 * e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      uint4 v;
+      v.x = static_cast<uint32_t>(lo);
+      v.y = static_cast<uint32_t>(lo >> 32);
+      v.z = static_cast<uint32_t>(hi);
+      v.w = static_cast<uint32_t>(hi >> 32);
+      pool[e] = v;
+    }
   }
 }
 
@@ -115,4 +152,31 @@ extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t*
                      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), pairs, num_blocks,
                      block_vecs);
   return launch_status("pa_copy_blocks");
+}
+
+extern "C" pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host,
+                                    const int32_t* blocks, int32_t n, int32_t to_host,
+                                    int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+                                    int32_t dtype, void* stream) {
+  if (pa_status st = check_pool_shape("pa_swap_blocks", Hkv, D, B, dtype)) return st;
+  if (n < 0 || num_blocks <= 0 || (to_host != 0 && to_host != 1))
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: n %d, num_blocks %d, to_host %d", n,
+                num_blocks, to_host);
+  if (n == 0) return ok();
+  if (n > 65535 * 32768) return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: n too large");
+  if (!k_cache || !v_cache || !host || !blocks)
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(host))
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: pools and host buffer must be 16-byte aligned");
+  bool host_is_host = false, blocks_on_host = false;
+  if (pa_status st = memory_kind("pa_swap_blocks", "host", host, &host_is_host)) return st;
+  if (!host_is_host)
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: host must be page-locked host memory");
+  if (pa_status st = memory_kind("pa_swap_blocks", "blocks", blocks, &blocks_on_host)) return st;
+  const int64_t slab_vecs = static_cast<int64_t>(Hkv) * B * D * elem_bytes(dtype) / 16;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(static_cast<unsigned>(n), 2), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), static_cast<uint4*>(host), blocks, num_blocks,
+                     slab_vecs, to_host, blocks_on_host ? 1 : 0);
+  return launch_status("pa_swap_blocks");
 }

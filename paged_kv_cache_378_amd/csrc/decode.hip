@@ -51,6 +51,7 @@
 
 #include "cache_write.h"
 #include "device_common.h"
+#include "host_memory.h"
 
 namespace pa {
 
@@ -994,29 +995,6 @@ static pa_status dispatch(const DecodeArgs& a, int D, int B, int32_t dtype, int 
                  : launch<128, 32>(a, dtype, pt, w, wb, st, wr, lens_out);
 }
 
-// Where a step's slots or lengths live.  Device memory is read with ordinary loads; page-locked
-// host memory, which HIP maps into the device's address space at the same address, is read
-// through system-scope loads.  Pageable host memory is rejected.
-static pa_status step_input(const char* what, const int32_t* p, bool* host) {
-  hipPointerAttribute_t at{};
-  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(PA_ERR_INVALID_ARG,
-                "pa_decode_step: %s is neither device memory nor page-locked host memory", what);
-  }
-  if (at.type == hipMemoryTypeHost) {
-    if (at.devicePointer != p || at.hostPointer != p)
-      return fail(PA_ERR_INVALID_ARG,
-                  "pa_decode_step: page-locked %s is not mapped at its host address", what);
-    *host = true;
-    return ok();
-  }
-  if (at.type == hipMemoryTypeUnregistered)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode_step: %s is pageable host memory", what);
-  *host = false;
-  return ok();
-}
-
 extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* ctx_lens, int32_t S,
                                int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
@@ -1051,9 +1029,11 @@ extern "C" pa_status pa_decode_step(void* out, const void* q, const void* key, c
     return fail(PA_ERR_INVALID_ARG, "pa_decode_step: key and value must be 16-byte aligned");
   if (new_ctx_lens == ctx_lens) new_ctx_lens = nullptr;
   bool host_slots = false, host_lens = false;
-  if (pa_status st = step_input("slot_mapping", slot_mapping, &host_slots)) return st;
+  if (pa_status st = memory_kind("pa_decode_step", "slot_mapping", slot_mapping, &host_slots))
+    return st;
   if (new_ctx_lens)
-    if (pa_status st = step_input("new_ctx_lens", new_ctx_lens, &host_lens)) return st;
+    if (pa_status st = memory_kind("pa_decode_step", "new_ctx_lens", new_ctx_lens, &host_lens))
+      return st;
   // The write's table patch and the plan read the step's lengths from their source; the decode
   // kernel reads the device copy the plan leaves in ctx_lens.
   CacheWriteArgs wr = make_cache_write_args(

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(libpa):
 
 
 def test_abi_version(libpa):
-    assert libpa.pa_abi_version() == 1
+    assert libpa.pa_abi_version() == 2
 
 
 def _raw(libpa):

@@ -73,3 +73,27 @@ def gather_sequence(k_cache: np.ndarray, v_cache: np.ndarray, table_row,
     K = k_cache[phys, :, off, :]           # [n, Hkv, D]
     V = v_cache[phys, :, :, off]           # [n, Hkv, D]
     return K, V
+
+
+def swap_out(k_cache: np.ndarray, v_cache: np.ndarray, blocks) -> np.ndarray:
+    """Contents of whole physical blocks, as moved to host memory when a request is paused.
+
+    Taming the Tail, "Infrastructure Scale": when the pool runs out of blocks a
+    request can be paused and its KV-cache moved to CPU RAM.  The host buffer
+    layout is this library's interface: for block i of ``blocks``, its K part
+    ``k_cache[blocks[i]]`` ([Hkv, B, D]) flattened, then its V part
+    ``v_cache[blocks[i]]`` ([Hkv, D, B]) flattened.  Returns [n, 2, Hkv*B*D].
+    """
+    blocks = [int(b) for b in blocks]
+    out = np.empty((len(blocks), 2, k_cache[0].size), dtype=k_cache.dtype)
+    for i, b in enumerate(blocks):
+        out[i, 0] = k_cache[b].reshape(-1)
+        out[i, 1] = v_cache[b].reshape(-1)
+    return out
+
+
+def swap_in(k_cache: np.ndarray, v_cache: np.ndarray, host: np.ndarray, blocks) -> None:
+    """Put saved block contents (the layout ``swap_out`` returns) into physical blocks."""
+    for i, b in enumerate(int(x) for x in blocks):
+        k_cache[b] = host[i, 0].reshape(k_cache.shape[1:])
+        v_cache[b] = host[i, 1].reshape(v_cache.shape[1:])

@@ -84,3 +84,42 @@ def test_write_then_gather_round_trip_through_block_manager():
         want = np.stack(logical[sid])
         assert K.shape == want.shape
         assert np.array_equal(K, want) and np.array_equal(V, -want)
+
+
+def test_swap_layout_and_round_trip():
+    # Hand-checked layout: pool of 3 blocks, Hkv = 1, B = 2, D = 2; K block p holds
+    # 10p + (0, 1, 2, 3) row-major, V block p holds 100 + 10p + (0, 1, 2, 3).
+    k = (10 * np.arange(3)[:, None] + np.arange(4)).reshape(3, 1, 2, 2)
+    v = (100 + 10 * np.arange(3)[:, None] + np.arange(4)).reshape(3, 1, 2, 2)
+    host = cache.swap_out(k, v, [2, 0])
+    assert host.tolist() == [[[20, 21, 22, 23], [120, 121, 122, 123]],
+                             [[0, 1, 2, 3], [100, 101, 102, 103]]]
+    # back into other blocks: block 1 receives old block 2, block 2 receives old block 0
+    k2, v2 = k.copy(), v.copy()
+    cache.swap_in(k2, v2, host, [1, 2])
+    assert np.array_equal(k2[1], k[2]) and np.array_equal(v2[1], v[2])
+    assert np.array_equal(k2[2], k[0]) and np.array_equal(v2[2], v[0])
+    assert np.array_equal(k2[0], k[0]) and np.array_equal(v2[0], v[0])
+
+
+def test_swap_preserves_what_the_table_reads():
+    # a sequence swapped out and back in onto different blocks reads the same K/V
+    rng = np.random.default_rng(5)
+    NB, H, B, D = 12, 2, 4, 3
+    k = rng.integers(0, 1 << 15, (NB, H, B, D)).astype(np.int16)
+    v = rng.integers(0, 1 << 15, (NB, H, D, B)).astype(np.int16)
+    model = BlockManagerModel(NB, B)
+    model.add_seq(7, 10)                      # blocks 0, 1, 2
+    rows, _ = model.block_tables([7], 3)
+    K0, V0 = cache.gather_sequence(k, v, rows[0], 10, B)
+    host = cache.swap_out(k, v, model.swap_out(7))
+    model.add_seq(8, 12)                      # takes blocks 3, 4, 5 (front of the pool)
+    k[[3, 4, 5]] = 0
+    v[[3, 4, 5]] = 0
+    model.free_seq(8)
+    new = model.swap_in(7)                    # blocks 6, 7, 8
+    assert new == [6, 7, 8]
+    cache.swap_in(k, v, host, new)
+    rows, _ = model.block_tables([7], 3)
+    K1, V1 = cache.gather_sequence(k, v, rows[0], 10, B)
+    assert np.array_equal(K0, K1) and np.array_equal(V0, V1)

@@ -91,11 +91,14 @@ WORKLOADS = {
                 "D=128, B=32",
     "chunk": "chunked-query prefill, 8 sequences x 512 new tokens over 4096 cached, 64/8 heads, "
              "D=128, B=32, causal inside the chunk",
+    "swap": "preemption by swapping: every 8th sequence of the llama3-70b-shaped batch (32 of "
+            "256) swapped out to pinned host memory and back in",
 }
+PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
 
 def make_workload(wl, name, pool):
-    if name == "llama70b":
+    if name in ("llama70b", "swap"):
         if pool == "churned":
             return wl.llama70b()
         w = wl.llama70b(churn_steps=0)
@@ -174,7 +177,7 @@ def main() -> int:
         dst_buf.copy_(src_buf)
         torch.cuda.synchronize()
         del src_buf, dst_buf
-    run = run_chunk if w.chunk else run_decode
+    run = run_chunk if w.chunk else (run_swap if args.workload == "swap" else run_decode)
     line = run(args, w, st, t_setup)
     print(json.dumps(line), flush=True)
     return 0 if "error" not in line else 1
@@ -401,6 +404,96 @@ def run_chunk(args, w, st, t_setup):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "kernel": "pa_chunk_attend (chunk_kernel)",
                      "avg_ms": round(att_ms, 4), "algorithmic_flops": flops},
+        "cpu_baseline": None,
+        "setup_s": round(t_setup, 1),
+    })
+    return line
+
+
+def run_swap(args, w, st, t_setup):
+    """One step = pause 32 sequences (pa_bm_swap_out, then one pa_swap_blocks copy of all their
+    blocks to pinned host memory) and resume them (pa_bm_swap_in onto fresh blocks, one copy
+    back).  Each copy is timed with HIP events on its stream; the decode of the whole batch
+    after the last step must equal the decode before the first, bit for bit."""
+    import torch
+
+    from paged_kv_cache_378_amd import _lib
+
+    dev = st.device
+    S, B, H, D = w.num_seqs, w.block_size, w.hkv, w.head_dim
+    ids = [int(i) for i in w.step_ids]
+    victims = ids[::8]
+    max_ctx = max(w.ctx_lens())
+    max_blocks = (max_ctx + B - 1) // B
+    ws = torch.empty(_lib.pa_decode_workspace_size(S, w.hq, D, max_ctx, 0), dtype=torch.uint8,
+                     device=dev)
+
+    def decode():
+        t, l = (torch.from_numpy(x).to(dev) for x in st.bm.block_tables(ids, max_blocks))
+        out = st.new_out()
+        _lib.pa_decode(out, st.vals["q"], st.k_cache, st.v_cache, t, l, max_ctx, w.scale, 0, ws)
+        torch.cuda.synchronize()
+        return out
+
+    before = decode()
+    nblk = sum(-(-st.bm.seq_len(v) // B) for v in victims)
+    slab = H * B * D
+    host = torch.empty(nblk * 2 * slab, dtype=st.k_cache.dtype).pin_memory()
+    out_list = torch.empty(nblk, dtype=torch.int32).pin_memory()
+    in_list = torch.empty(nblk, dtype=torch.int32).pin_memory()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    times = []
+
+    def step(i, timed):
+        o = 0
+        for v in victims:
+            b = st.bm.swap_out(v)
+            out_list.numpy()[o:o + len(b)] = b
+            o += len(b)
+        e = ev[len(times)] if timed else None
+        if timed:
+            e[0].record(stream)
+        _lib.pa_swap_blocks(st.k_cache, st.v_cache, host, out_list, to_host=True)
+        if timed:
+            e[1].record(stream)
+        o = 0
+        for v in victims:
+            b = st.bm.swap_in(v)
+            in_list.numpy()[o:o + len(b)] = b
+            o += len(b)
+        if timed:
+            e[2].record(stream)
+        _lib.pa_swap_blocks(st.k_cache, st.v_cache, host, in_list, to_host=False)
+        if timed:
+            e[3].record(stream)
+            times.append(e)
+        # the block lists and the host buffer are reused next step: wait for this one
+        torch.cuda.synchronize()
+
+    elapsed, _ = timed_loop(args, step)
+    after = decode()
+    it = torch.int16 if w.dtype == "bf16" else torch.int32
+    if not torch.equal(before.view(it), after.view(it)):
+        return {"error": "decode changed across swap-out / swap-in"}
+    ms_step = 1e3 * elapsed / args.steps
+    d2h_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in times]))
+    h2d_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in times]))
+    nbytes = nblk * 2 * slab * st.k_cache.element_size()
+    achieved = 2 * nbytes / ((d2h_ms + h2d_ms) * 1e-3) / 1e9
+    line = {"metric": "swap: host-link GB/s (paused sequences' blocks out to pinned host memory "
+                      "and back)",
+            "value": round(2 * nbytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s"}
+    line.update(base_line(args, w, ms_step))
+    line.update({
+        "config": {"workload": WORKLOADS["swap"], "swapped_sequences": len(victims),
+                   "blocks": nblk, "bytes_each_way": nbytes, "parallelism": "none (1 GPU)"},
+        "d2h_GBps": round(nbytes / (d2h_ms * 1e-3) / 1e9, 2),
+        "h2d_GBps": round(nbytes / (h2d_ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "pcie", "achieved": round(achieved, 2), "peak": PCIE_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_swap_blocks (both directions; one direction at a time)",
+                     "avg_ms": round(d2h_ms + h2d_ms, 4), "algorithmic_bytes": 2 * nbytes},
         "cpu_baseline": None,
         "setup_s": round(t_setup, 1),
     })

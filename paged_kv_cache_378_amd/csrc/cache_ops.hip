@@ -41,8 +41,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
 // One workgroup per (block, K or V slab).  A block's K slab ([Hkv, B, D]) and V slab
 // ([Hkv, D, B]) are each contiguous in their pool; the host buffer holds block i's K slab then
 // its V slab.  to_host: pool -> host with ordinary stores (written back over the bus when the
-// kernel ends); else host -> pool with system-scope 8-byte loads, which never use a line an
-// earlier kernel left in a GPU cache.
+// kernel ends); else host -> pool with system-coherent 16-byte loads, which never use a line
+// an earlier kernel left in a GPU cache.
 __global__ __launch_bounds__(256) void swap_blocks_kernel(uint4* __restrict__ k_cache,
                                                           uint4* __restrict__ v_cache,
                                                           uint4* __restrict__ host,
@@ -58,17 +58,13 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(uint4* __restrict__ k_
   if (to_host) {
     for (int64_t e = threadIdx.x; e < slab_vecs; e += blockDim.x) hb[e] = pool[e];
   } else {
-    const uint64_t* src = reinterpret_cast<const uint64_t*>(hb);
-    for (int64_t e = threadIdx.x; e < slab_vecs; e += blockDim.x) {
-      const uint64_t lo = __hip_atomic_load(src + 2 * e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      const uint64_t hi = __hip_atomic_load(src + 2 * e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      uint4 v;
-      v.x = static_cast<uint32_t>(lo);
-      v.y = static_cast<uint32_t>(lo >> 32);
-      v.z = static_cast<uint32_t>(hi);
-      v.w = static_cast<uint32_t>(hi >> 32);
-      pool[e] = v;
-    }
+    // 16-byte loads with the system-coherence bits (sc0 sc1) through a buffer resource over
+    // the slab (raw, untyped: the resource word CDNA3/4 kernels use for plain buffers)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        hb, 0, static_cast<int>(slab_vecs * 16), 0x00020000);
+    u32x4* dst = reinterpret_cast<u32x4*>(pool);
+    for (int64_t e = threadIdx.x; e < slab_vecs; e += blockDim.x)
+      dst[e] = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(e * 16), 0, 1 | 16);
   }
 }
 
@@ -174,6 +170,8 @@ extern "C" pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host,
     return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: host must be page-locked host memory");
   if (pa_status st = memory_kind("pa_swap_blocks", "blocks", blocks, &blocks_on_host)) return st;
   const int64_t slab_vecs = static_cast<int64_t>(Hkv) * B * D * elem_bytes(dtype) / 16;
+  if (slab_vecs * 16 > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: a block slab exceeds 2 GiB");
   hipLaunchKernelGGL(swap_blocks_kernel, dim3(static_cast<unsigned>(n), 2), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
                      static_cast<uint4*>(v_cache), static_cast<uint4*>(host), blocks, num_blocks,

@@ -225,7 +225,7 @@ pa_status pa_validate_tables(const int32_t* tables, const int32_t* ctx_lens, int
 
 /* ======================================================================================
  * Device operations (HIP, gfx950).  Supported: dtype F32 or BF16; head_dim D in {64, 128};
- * block size B in {16, 32}; Hq a multiple of Hkv.  Tensors are C-contiguous; every pointer
+ * block size B in {16, 32, 64}; Hq a multiple of Hkv.  Tensors are C-contiguous; every pointer
  * must be 16-byte aligned.
  * ====================================================================================== */
 
@@ -287,7 +287,7 @@ pa_status pa_decode_workspace_size(int32_t S, int32_t Hq, int32_t D, int32_t max
  * block_tables: device int32 [S, max_blocks]; ctx_lens: device int32 [S], each in
  * [1, max_blocks * B] and <= max_ctx_len.  Positions >= ctx_len of a sequence never influence
  * its output (NaN or Inf there is harmless).  Computation: fp32 accumulation; split-K over
- * partitions of partition_tokens tokens (0 = library's choice, else a multiple of 32 in
+ * partitions of partition_tokens tokens (0 = library's choice, else a multiple of 32 and of B in
  * [32, 8192]) followed by a merge.  workspace: device buffer of at least
  * pa_decode_workspace_size(S, Hq, D, max_ctx_len, partition_tokens) bytes (may be NULL if
  * that size is 0).  Deterministic: results depend on logical positions only, not on which

@@ -73,7 +73,8 @@ static pa_status check_pool_shape(const char* who, int32_t Hkv, int32_t D, int32
   if (elem_bytes(dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, dtype);
   if (Hkv <= 0) return fail(PA_ERR_INVALID_ARG, "%s: Hkv %d <= 0", who, Hkv);
   if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", who, D);
-  if (B != 16 && B != 32) return fail(PA_ERR_UNSUPPORTED, "%s: block size %d not in {16, 32}", who, B);
+  if (B != 16 && B != 32 && B != 64)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block size %d not in {16, 32, 64}", who, B);
   return PA_OK;
 }
 

@@ -389,7 +389,8 @@ extern "C" pa_status pa_chunk_attend(void* out, const void* q, const void* k_cac
                                      int32_t max_blocks, float scale, int32_t dtype, void* stream) {
   if (dtype != PA_DTYPE_BF16) return fail(PA_ERR_UNSUPPORTED, "pa_chunk_attend: only bf16 is built");
   if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "pa_chunk_attend: head_dim %d not in {64, 128}", D);
-  if (B != 16 && B != 32) return fail(PA_ERR_UNSUPPORTED, "pa_chunk_attend: block size %d not in {16, 32}", B);
+  if (B != 16 && B != 32 && B != 64)
+    return fail(PA_ERR_UNSUPPORTED, "pa_chunk_attend: block size %d not in {16, 32, 64}", B);
   if (S < 0 || C < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv)
     return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: S %d, C %d, Hq %d, Hkv %d", S, C, Hq, Hkv);
   const int G = Hq / Hkv;
@@ -428,10 +429,12 @@ extern "C" pa_status pa_chunk_attend(void* out, const void* q, const void* k_cac
   const dim3 grid(static_cast<unsigned>(groups * a.NQB));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 64) {
-    if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<64, 16>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
+    if (B == 64) hipLaunchKernelGGL((chunk::chunk_kernel<64, 64>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
+    else if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<64, 16>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
     else hipLaunchKernelGGL((chunk::chunk_kernel<64, 32>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
   } else {
-    if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<128, 16>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
+    if (B == 64) hipLaunchKernelGGL((chunk::chunk_kernel<128, 64>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
+    else if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<128, 16>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
     else hipLaunchKernelGGL((chunk::chunk_kernel<128, 32>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
   }
   return launch_status("pa_chunk_attend");

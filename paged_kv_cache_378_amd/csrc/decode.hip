@@ -264,7 +264,7 @@ __device__ __forceinline__ void for_each_item(const DecodeArgs& a, int* s_next, 
 }
 
 // ---------------------------------------------------------------------------------------
-// MFMA kernel: bf16, 1 <= G <= 16 query heads per kv-head, D in {64, 128}, B in {16, 32}.
+// MFMA kernel: bf16, 1 <= G <= 16 query heads per kv-head, D in {64, 128}, B in {16, 32, 64}.
 //
 // A wave walks its partition in tiles of 32 tokens (tiles w, w + NW, ...).  Per tile a lane
 // holds D/32 16-byte pieces of K as loaded (whole key rows, 1 KB contiguous per instruction)
@@ -936,7 +936,8 @@ static pa_status decode_setup(const char* who, void* out, const void* q, const v
                               DecodeArgs* out_args) {
   if (elem_bytes(dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", who, dtype);
   if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", who, D);
-  if (B != 16 && B != 32) return fail(PA_ERR_UNSUPPORTED, "%s: block size %d not in {16, 32}", who, B);
+  if (B != 16 && B != 32 && B != 64)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block size %d not in {16, 32, 64}", who, B);
   if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv)
     return fail(PA_ERR_INVALID_ARG, "%s: S %d, Hq %d, Hkv %d (Hq must be a multiple of Hkv)", who, S, Hq, Hkv);
   if (S > 65535 || Hkv > 65535) return fail(PA_ERR_INVALID_ARG, "%s: S and Hkv must be <= 65535", who);
@@ -947,6 +948,9 @@ static pa_status decode_setup(const char* who, void* out, const void* q, const v
   if (partition_tokens != 0 && (partition_tokens % 32 || partition_tokens < 32 || partition_tokens > kMaxPT))
     return fail(PA_ERR_INVALID_ARG, "%s: partition_tokens %d is not a multiple of 32 in [32, %d]",
                 who, partition_tokens, kMaxPT);
+  if (partition_tokens % B)  // a partition is made of whole blocks
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_tokens %d is not a multiple of the block size %d",
+                who, partition_tokens, B);
   if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is NaN", who);
   if (S == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens)
@@ -990,9 +994,11 @@ static pa_status dispatch(const DecodeArgs& a, int D, int B, int32_t dtype, int 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 64)
     return B == 16 ? launch<64, 16>(a, dtype, pt, w, wb, st, wr, lens_out)
-                   : launch<64, 32>(a, dtype, pt, w, wb, st, wr, lens_out);
+         : B == 32 ? launch<64, 32>(a, dtype, pt, w, wb, st, wr, lens_out)
+                   : launch<64, 64>(a, dtype, pt, w, wb, st, wr, lens_out);
   return B == 16 ? launch<128, 16>(a, dtype, pt, w, wb, st, wr, lens_out)
-                 : launch<128, 32>(a, dtype, pt, w, wb, st, wr, lens_out);
+       : B == 32 ? launch<128, 32>(a, dtype, pt, w, wb, st, wr, lens_out)
+                 : launch<128, 64>(a, dtype, pt, w, wb, st, wr, lens_out);
 }
 
 extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -36,6 +36,8 @@ CASES = {
                                                    16, "bf16", extra_blocks=20), 5, 6),
     "chunk_appends_b32_f32": (lambda: wl.custom_decode("app7", 42, [1, 31, 32, 33, 200], 4, 4,
                                                        64, 32, "f32", extra_blocks=10), 7, 5),
+    "decode_b64": (lambda: wl.custom_decode("app64", 47, [1, 63, 64, 127, 300], 16, 2, 128, 64,
+                                            "bf16", extra_blocks=6), 1, 3),
 }
 
 
@@ -116,6 +118,8 @@ STEP_CASES = {
                                                   suffix_range=(1, 60)),
     "fp32_g1": lambda: wl.custom_decode("stepf32", 43, [1, 15, 16, 17, 300], 4, 4, 64, 16, "f32",
                                         extra_blocks=10),
+    "bf16_b64": lambda: wl.custom_decode("step64", 48, [1, 63, 64, 65, 500], 32, 8, 128, 64,
+                                         "bf16", extra_blocks=6),
 }
 
 

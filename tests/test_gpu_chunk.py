@@ -31,6 +31,8 @@ CASES = {
     "g6_odd": wl.chunked(S=2, cached=90, C=77, B=16, hq=12, hkv=2),
     "no_prefix": wl.chunked(S=2, cached=0, C=100, B=32),
     "single_token": wl.chunked(S=3, cached=517, C=1, B=32),
+    "g8_b64": wl.chunked(S=2, cached=300, C=40, B=64),
+    "g8_d64_b64_long_chunk": wl.chunked(S=2, cached=70, C=200, B=64, D=64),
 }
 
 

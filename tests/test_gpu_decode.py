@@ -38,6 +38,9 @@ def small_cases():
         "bf16_g8_d64": wl.custom_decode("bf16_g8_d64", 26, [1, 31, 32, 33, 513, 1024], 16, 2, 64, 16, "bf16"),
         "bf16_g16_b32": wl.custom_decode("bf16_g16", 27, [7, 40, 777], 16, 1, 128, 32, "bf16"),
         "bf16_g6_odd": wl.custom_decode("bf16_g6", 28, [9, 100, 257], 12, 2, 128, 16, "bf16"),
+        "bf16_g8_b64": wl.custom_decode("b64g8", 35, [1, 63, 64, 65, 700, 2000], 16, 2, 128, 64,
+                                        "bf16"),
+        "fp32_g1_d64_b64": wl.custom_decode("b64f32", 36, [5, 64, 129, 300], 4, 4, 64, 64, "f32"),
         "shared_prefix_b16": wl.shared_prefix(B=16, n_seqs=12, prefix=100, n_families=4,
                                               suffix_range=(1, 60)),
         "shared_prefix_b32": wl.shared_prefix(B=32, n_seqs=12, prefix=96, n_families=4,
@@ -59,6 +62,7 @@ CASES = small_cases()
 @pytest.mark.parametrize("pt", [0, 32, 96])
 def test_decode_matches_oracle(gpu, name, pt):
     w = CASES[name]
+    pt = -(-pt // w.block_size) * w.block_size  # partitions are whole blocks (B = 64: 64, 128)
     st, out, _ = run(w, pt)
     want = oracle_decode(w, st.vals)
     got = f64(out)

@@ -19,6 +19,8 @@ CASES = {
                                                        suffix_range=(1, 60)),
     "custom_b32_f32": lambda: wl.custom_decode("swapf32", 46, [3, 40, 64, 97, 130], 4, 4, 64, 32,
                                                "f32", extra_blocks=12),
+    "custom_b64_bf16": lambda: wl.custom_decode("swap64", 49, [3, 64, 65, 200, 331], 32, 8, 128,
+                                                64, "bf16", extra_blocks=10),
 }
 
 

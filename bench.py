@@ -97,11 +97,11 @@ WORKLOADS = {
 PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
 
-def make_workload(wl, name, pool):
+def make_workload(wl, name, pool, block_size=16):
     if name in ("llama70b", "swap"):
         if pool == "churned":
-            return wl.llama70b()
-        w = wl.llama70b(churn_steps=0)
+            return wl.llama70b(B=block_size)
+        w = wl.llama70b(churn_steps=0, B=block_size)
     elif name == "mistral7b":
         w = wl.mistral()
     elif name == "long32k":
@@ -148,6 +148,9 @@ def main() -> int:
                          "fragmented by 10,000 alloc/free steps); contiguous: identity free order "
                          "and no churn, so each sequence's blocks are physically consecutive (the "
                          "contiguous-cache comparison)")
+    ap.add_argument("--block-size", type=int, choices=[16, 32, 64], default=16,
+                    help="block size of the llama70b / swap batch (the block-size trade-off: "
+                         "table entries, tail waste, kernel rate)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the timed steps, run one device-to-device copy of this many MiB "
                          "(a plain copy of known size that calibrates the HBM byte counters)")
@@ -165,7 +168,10 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    w = make_workload(wl, args.workload, args.pool)
+    if args.block_size != 16 and args.workload not in ("llama70b", "swap"):
+        print(json.dumps({"error": "--block-size applies to the llama70b and swap workloads"}))
+        return 2
+    w = make_workload(wl, args.workload, args.pool, args.block_size)
     t_setup = time.perf_counter()
     st = PagedState(w, dev, poison=True)
     torch.cuda.synchronize()
@@ -320,6 +326,9 @@ def run_decode(args, w, st, t_setup):
         "tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "host_block_manager_us": round(1e6 * float(np.median(host_s)), 1),
+        "block_size": w.block_size,
+        "pool": {k: st.bm.stats()[k] for k in ("logical_blocks", "live_tokens", "tail_waste_slots",
+                                               "used_blocks", "num_blocks")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if headline and args.pool == "churned" else None,

@@ -210,16 +210,18 @@ def mistral(seed: int = 2, S: int = 64, max_len: int = 4096) -> Workload:
 
 
 def llama70b(seed: int = 3, S: int = 256, churn_steps: int = 10_000, max_len: int = 8192,
-             median: float = 1024.0, sigma: float = 1.0) -> Workload:
-    """Llama-3-70B-shaped decode layer: 64/8 heads, D=128, bf16, B=16, log-normal lengths
-    (median 1,024, clipped to [16, 8,192]) over a pool fragmented by alloc/free churn."""
+             median: float = 1024.0, sigma: float = 1.0, B: int = 16) -> Workload:
+    """Llama-3-70B-shaped decode layer: 64/8 heads, D=128, bf16, B=16 (other block sizes for
+    the block-size trade-off), log-normal lengths (median 1,024, clipped to [16, 8,192]) over
+    a pool fragmented by alloc/free churn."""
     rng = np.random.default_rng(seed)
 
     def law(r):
         return int(np.clip(np.rint(np.exp(r.normal(math.log(median), sigma))), 16, max_len))
 
     lens = [law(rng) for _ in range(S)]
-    w = _decode_workload(f"llama3_70b_b{S}", seed, lens, 64, 8, 128, 16, "bf16",
+    name = f"llama3_70b_b{S}" + ("" if B == 16 else f"_B{B}")
+    w = _decode_workload(name, seed, lens, 64, 8, 128, B, "bf16",
                          churn_steps=churn_steps, churn_law=law, rng=rng)
     w.meta["churn_steps"] = churn_steps
     return w

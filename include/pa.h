@@ -110,6 +110,9 @@ typedef struct {
   int64_t swapped_tokens;   /* tokens those sequences hold in host memory                 */
   int64_t swap_outs;        /* pa_bm_swap_out calls so far                                */
   int64_t swap_ins;         /* pa_bm_swap_in calls so far                                 */
+  int32_t cached_blocks;    /* prefix-cache tree nodes (each holds one block reference)   */
+  int64_t cache_hit_blocks; /* blocks pa_bm_add_seq_cached reused so far                  */
+  int64_t cache_evictions;  /* tree nodes evicted so far                                  */
 } pa_bm_stats_t;
 
 /* Create a manager over physical blocks [0, num_blocks) of block_size tokens each.
@@ -194,6 +197,36 @@ pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq_id, int32_t* blocks_out, int32_t
                          int32_t* n_out);
 pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq_id, int32_t* blocks_out, int32_t cap,
                         int32_t* n_out);
+
+/* Prefix cache ([KC] "RadixAttention": cached token sequences form a radix tree; a new request
+ * reuses the K/V blocks of its longest cached prefix and prefills only the rest; when memory
+ * runs low the least recently used leaves are evicted, reference counting protecting what
+ * running requests use; [KC] answer A3: only whole blocks that are entirely prefix are shared).
+ * A tree node is one full block of B token ids under its parent, and holds one reference to
+ * its physical block.
+ *
+ * pa_bm_cache_insert: the first n_tokens token ids of a live sequence (the caller vouches that
+ * they are its tokens and that their K/V are written) -- its first floor(n_tokens / B) blocks
+ * become cached, each under its content; a content already cached keeps its existing block.
+ * *n_added_out (NULL allowed) receives the number of new nodes.
+ *
+ * pa_bm_add_seq_cached: a new sequence of n_tokens token ids.  The longest chain of cached
+ * full blocks matching its first tokens is reused (each block gains a reference);
+ * *n_cached_out receives their token count (a multiple of B), and the rest get fresh blocks
+ * as in pa_bm_add_seq.  slots_out (NULL allowed): the slots of all n_tokens positions; only
+ * positions >= *n_cached_out need a prefill and a cache write.
+ *
+ * Eviction: a call that needs more blocks than the pool holds (adds, appends, swap-ins) first
+ * evicts exactly the shortfall -- each time the tree leaf with the oldest use (ties: the
+ * oldest node) among those only the tree references -- and the freed blocks join the back of
+ * the pool.  If the tree cannot cover the shortfall the call fails with PA_ERR_OUT_OF_BLOCKS
+ * and nothing changes.  An insert or a cached add marks every node it passes as used, at one
+ * step of a counter.  pa_bm_cache_evict evicts up to n_blocks such leaves on demand. */
+pa_status pa_bm_cache_insert(pa_bm* bm, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                             int32_t* n_added_out);
+pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq_id, const int32_t* tokens,
+                               int32_t n_tokens, int32_t* slots_out, int32_t* n_cached_out);
+pa_status pa_bm_cache_evict(pa_bm* bm, int32_t n_blocks, int32_t* n_evicted_out);
 
 /* Truncate a live sequence to its first n_keep tokens (0 <= n_keep <= len), e.g. to roll back
  * rejected speculative tokens.  Blocks past ceil(n_keep / B) are released in logical order

@@ -45,6 +45,27 @@ truncation, read plainly:
 * truncating to n_keep tokens drops the references of the blocks past
   ceil(n_keep / B), in logical order; a shared kept block stays shared until
   the next write copies it.
+
+Prefix cache (KV-cache chapter, "RadixAttention": cached token sequences form a
+radix tree; a new request reuses the blocks of its longest cached prefix and
+prefills only the rest; when memory runs low the least recently used leaves are
+evicted, and reference counting protects branches running requests still use;
+answer A3: only whole blocks that are entirely prefix can be shared), read at
+block granularity:
+
+* a tree node is one full block of B tokens, keyed by those token ids under its
+  parent; the tree holds one reference to each node's block;
+* inserting a live sequence's first k full blocks walks the tree by content,
+  keeps the node that already exists for a content, else adds one holding the
+  sequence's block;
+* a cached add matches the longest chain of full blocks from the root, takes a
+  reference to each matched block (before anything is evicted, so they are
+  safe), and allocates the rest like a plain add;
+* every call that allocates first evicts, if the free pool is short, exactly the
+  shortfall: each time the leaf with the oldest use (ties: oldest node) among
+  those only the tree references; its block rejoins the pool; if the tree
+  cannot cover the shortfall the call fails and nothing changes;
+* an insert or a cached add marks every node it passes as used at one tick.
 """
 
 from __future__ import annotations
@@ -77,6 +98,18 @@ class Swapped(BlockManagerError):
     status = -8
 
 
+class _Node:
+    __slots__ = ("block", "key", "parent", "children", "last_use", "nid")
+
+    def __init__(self, block, key, parent, last_use, nid):
+        self.block = block
+        self.key = key
+        self.parent = parent          # parent _Node or None (child of the root)
+        self.children: dict = {}      # token tuple -> _Node
+        self.last_use = last_use
+        self.nid = nid
+
+
 class _Seq:
     __slots__ = ("blocks", "n")
 
@@ -104,6 +137,66 @@ class BlockManagerModel:
         self.cow_copies = 0
         self.swap_outs = 0
         self.swap_ins = 0
+        self.root: dict = {}          # token tuple -> _Node
+        self.nodes: list = []         # live tree nodes
+        self.tick = 0
+        self.next_nid = 0
+        self.cache_hit_blocks = 0
+        self.cache_evictions = 0
+
+    # -- prefix-cache helpers ---------------------------------------------
+    def _evictable(self) -> int:
+        """Nodes whose whole subtree is referenced by the tree only."""
+        def count(children) -> tuple:
+            total, all_free = 0, True
+            for node in children.values():
+                sub, sub_free = count(node.children)
+                total += sub
+                if sub_free and self.ref[node.block] == 1:
+                    total += 1
+                else:
+                    all_free = False
+            return total, all_free
+        return count(self.root)[0]
+
+    def _evict_one(self) -> bool:
+        best = None
+        for node in self.nodes:
+            if not node.children and self.ref[node.block] == 1:
+                if best is None or (node.last_use, node.nid) < (best.last_use, best.nid):
+                    best = node
+        if best is None:
+            return False
+        (best.parent.children if best.parent else self.root).pop(best.key)
+        self.nodes.remove(best)
+        self._release(best.block)
+        self.cache_evictions += 1
+        return True
+
+    def _make_room(self, need: int) -> None:
+        short = need - len(self.free)
+        if short <= 0:
+            return
+        if self._evictable() < short:
+            raise OutOfBlocks("free pool and evictable cache too small")
+        for _ in range(short):
+            self._evict_one()
+
+    def _append_need(self, ids, tokens_each: int) -> int:
+        B, need, dec = self.block_size, 0, {}
+        for s in ids:
+            seq = self.seqs[s]
+            if tokens_each == 0:
+                continue
+            if seq.n % B:
+                last = seq.blocks[-1]
+                if self.ref[last] - dec.get(last, 0) > 1:
+                    dec[last] = dec.get(last, 0) + 1
+                    need += 1
+            first = -(-seq.n // B)
+            lastm = (seq.n + tokens_each - 1) // B
+            need += lastm - first + 1
+        return need
 
     # -- internal helpers -------------------------------------------------
     def _take(self) -> int:
@@ -139,12 +232,15 @@ class BlockManagerModel:
 
     def _transaction(self, fn):
         """Run ``fn`` on the live state; restore everything if it raises."""
-        saved = (copy.deepcopy(self.seqs), list(self.ref), deque(self.free),
-                 self.forks, self.cow_copies, dict(self.swapped))
+        saved = copy.deepcopy((self.seqs, self.ref, self.free, self.forks, self.cow_copies,
+                               self.swapped, self.root, self.nodes, self.tick, self.next_nid,
+                               self.cache_hit_blocks, self.cache_evictions))
         try:
             return fn()
         except BlockManagerError:
-            self.seqs, self.ref, self.free, self.forks, self.cow_copies, self.swapped = saved
+            (self.seqs, self.ref, self.free, self.forks, self.cow_copies, self.swapped, self.root,
+             self.nodes, self.tick, self.next_nid, self.cache_hit_blocks,
+             self.cache_evictions) = saved
             raise
 
     def _live(self, seq_id: int) -> _Seq:
@@ -163,6 +259,7 @@ class BlockManagerModel:
             raise InvalidArg("n_tokens < 0")
 
         def run():
+            self._make_room(-(-n_tokens // self.block_size))
             seq = _Seq()
             self.seqs[seq_id] = seq
             pairs: list = []
@@ -187,6 +284,7 @@ class BlockManagerModel:
             seen.add(s)
 
         def run():
+            self._make_room(self._append_need(ids, tokens_each))
             slots: list[int] = []
             pairs: list = []
             for s in ids:
@@ -262,15 +360,18 @@ class BlockManagerModel:
             raise UnknownSeq(seq_id)
         n = self.swapped[seq_id]
         k = -(-n // self.block_size)
-        if k > len(self.free):
-            raise OutOfBlocks("free pool too small for the swap-in")
-        seq = _Seq()
-        seq.blocks = [self._take() for _ in range(k)]
-        seq.n = n
-        del self.swapped[seq_id]
-        self.seqs[seq_id] = seq
-        self.swap_ins += 1
-        return list(seq.blocks)
+
+        def run():
+            self._make_room(k)
+            seq = _Seq()
+            seq.blocks = [self._take() for _ in range(k)]
+            seq.n = n
+            del self.swapped[seq_id]
+            self.seqs[seq_id] = seq
+            self.swap_ins += 1
+            return list(seq.blocks)
+
+        return self._transaction(run)
 
     def truncate(self, seq_id: int, n_keep: int) -> None:
         """Keep the first ``n_keep`` tokens; blocks past them lose this reference."""
@@ -282,6 +383,77 @@ class BlockManagerModel:
             self._release(b)
         del seq.blocks[keep:]
         seq.n = n_keep
+
+    def add_seq_cached(self, seq_id: int, tokens) -> tuple[list[int], int]:
+        """New sequence of the given token ids reusing its longest cached prefix of full
+        blocks; returns (slots of every position, number of cached tokens)."""
+        if seq_id in self.seqs or seq_id in self.swapped:
+            raise SeqExists(seq_id)
+        toks = [int(t) for t in tokens]
+        B = self.block_size
+        matched, children = [], self.root
+        for j in range(len(toks) // B):
+            node = children.get(tuple(toks[j * B:(j + 1) * B]))
+            if node is None:
+                break
+            matched.append(node)
+            children = node.children
+        need = -(-len(toks) // B) - len(matched)
+        # the matched blocks are referenced first, so eviction cannot take them
+        for node in matched:
+            self.ref[node.block] += 1
+        short = need - len(self.free)
+        if short > 0 and self._evictable() < short:
+            for node in matched:
+                self.ref[node.block] -= 1
+            raise OutOfBlocks("free pool and evictable cache too small")
+        for node in matched:
+            node.last_use = self.tick
+        self.tick += 1
+        self._make_room(need)
+        seq = _Seq()
+        seq.blocks = [node.block for node in matched]
+        seq.n = len(matched) * B
+        self.seqs[seq_id] = seq
+        pairs: list = []
+        for _ in range(len(toks) - seq.n):
+            self._write_one(seq, pairs)
+        self.cache_hit_blocks += len(matched)
+        slots = [seq.blocks[j // B] * B + j % B for j in range(len(toks))]
+        return slots, len(matched) * B
+
+    def cache_insert(self, seq_id: int, tokens) -> int:
+        """Cache the full blocks of a live sequence's first len(tokens) tokens (the caller
+        vouches that they are its tokens); returns the number of nodes added."""
+        seq = self._live(seq_id)
+        toks = [int(t) for t in tokens]
+        if len(toks) > seq.n:
+            raise InvalidArg("more tokens than the sequence holds")
+        B = self.block_size
+        children, parent, added = self.root, None, 0
+        for j in range(len(toks) // B):
+            key = tuple(toks[j * B:(j + 1) * B])
+            node = children.get(key)
+            if node is None:
+                node = _Node(seq.blocks[j], key, parent, self.tick, self.next_nid)
+                self.next_nid += 1
+                self.ref[node.block] += 1
+                children[key] = node
+                self.nodes.append(node)
+                added += 1
+            node.last_use = self.tick
+            children, parent = node.children, node
+        self.tick += 1
+        return added
+
+    def cache_evict(self, n_blocks: int) -> int:
+        """Evict up to n_blocks least recently used unreferenced leaves; returns how many."""
+        if n_blocks < 0:
+            raise InvalidArg("n_blocks < 0")
+        done = 0
+        while done < n_blocks and self._evict_one():
+            done += 1
+        return done
 
     def refcount(self, block: int) -> int:
         if not 0 <= block < self.num_blocks:
@@ -308,4 +480,7 @@ class BlockManagerModel:
             "swapped_tokens": sum(self.swapped.values()),
             "swap_outs": self.swap_outs,
             "swap_ins": self.swap_ins,
+            "cached_blocks": len(self.nodes),
+            "cache_hit_blocks": self.cache_hit_blocks,
+            "cache_evictions": self.cache_evictions,
         }

@@ -76,7 +76,8 @@ class pa_bm_stats_t(C.Structure):
                 ("logical_blocks", _i64), ("live_tokens", _i64), ("tail_waste_slots", _i64),
                 ("forks", _i64), ("cow_copies", _i64), ("usage", C.c_double),
                 ("swapped_seqs", _i32), ("swapped_tokens", _i64), ("swap_outs", _i64),
-                ("swap_ins", _i64)]
+                ("swap_ins", _i64), ("cached_blocks", _i32), ("cache_hit_blocks", _i64),
+                ("cache_evictions", _i64)]
 
 
 class pa_accounting_t(C.Structure):
@@ -103,6 +104,9 @@ _SIGS = {
     "pa_bm_swap_out": ([_vp, _i64, _pi32, _i32, _pi32], _i32),
     "pa_bm_swap_in": ([_vp, _i64, _pi32, _i32, _pi32], _i32),
     "pa_bm_truncate": ([_vp, _i64, _i32], _i32),
+    "pa_bm_cache_insert": ([_vp, _i64, _pi32, _i32, _pi32], _i32),
+    "pa_bm_add_seq_cached": ([_vp, _i64, _pi32, _i32, _pi32, _pi32], _i32),
+    "pa_bm_cache_evict": ([_vp, _i32, _pi32], _i32),
     "pa_accounting": ([_pi32, _i32, _i32, _i32, C.POINTER(pa_accounting_t)], _i32),
     "pa_validate_tables": ([_pi32, _pi32, _i32, _i32, _i32, _i32], _i32),
     "pa_cache_write": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
@@ -246,6 +250,27 @@ def pa_bm_truncate(h, seq_id: int, n_keep: int) -> None:
     _check(_lib.pa_bm_truncate(h, seq_id, n_keep))
 
 
+def pa_bm_cache_insert(h, seq_id: int, tokens) -> int:
+    t = _i32_host(tokens)
+    n = _i32()
+    _check(_lib.pa_bm_cache_insert(h, seq_id, _ptr32(t), len(t), C.byref(n)))
+    return n.value
+
+
+def pa_bm_add_seq_cached(h, seq_id: int, tokens):
+    t = _i32_host(tokens)
+    slots = np.empty(max(len(t), 1), np.int32)
+    n = _i32()
+    _check(_lib.pa_bm_add_seq_cached(h, seq_id, _ptr32(t), len(t), _ptr32(slots), C.byref(n)))
+    return slots[:len(t)].copy(), n.value
+
+
+def pa_bm_cache_evict(h, n_blocks: int) -> int:
+    n = _i32()
+    _check(_lib.pa_bm_cache_evict(h, n_blocks, C.byref(n)))
+    return n.value
+
+
 def pa_accounting(lens, block_size: int, max_seq_len: int) -> dict:
     a = _i32_host(lens)
     r = pa_accounting_t()
@@ -317,6 +342,16 @@ class BlockManager:
 
     def truncate(self, seq_id, n_keep):
         pa_bm_truncate(self.h, seq_id, n_keep)
+
+    def cache_insert(self, seq_id, tokens):
+        return pa_bm_cache_insert(self.h, seq_id, tokens)
+
+    def add_seq_cached(self, seq_id, tokens):
+        """(slots of every position, number of cached tokens)"""
+        return pa_bm_add_seq_cached(self.h, seq_id, tokens)
+
+    def cache_evict(self, n_blocks):
+        return pa_bm_cache_evict(self.h, n_blocks)
 
 
 # -- device operations (torch tensors in, nothing computed here) -----------------------

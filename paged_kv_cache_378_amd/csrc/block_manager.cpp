@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -31,6 +32,19 @@ namespace {
 struct Seq {
   std::vector<int32_t> blocks;  // physical ids in logical order
   int32_t n = 0;                // tokens held
+};
+
+// Prefix-cache tree node: one full block of B tokens, keyed by those token ids under its
+// parent.  Nodes live in a vector indexed by their id and are never reused; `live` is false
+// once evicted.
+using TokenKey = std::vector<int32_t>;
+struct CacheNode {
+  int32_t block = -1;
+  TokenKey key;
+  int64_t parent = -1;                    // -1: a child of the root
+  std::map<TokenKey, int64_t> children;   // token ids -> node id
+  int64_t last_use = 0;
+  bool live = true;
 };
 
 }  // namespace
@@ -48,6 +62,61 @@ struct pa_bm {
   int64_t cow_copies = 0;
   int64_t swap_outs = 0;
   int64_t swap_ins = 0;
+  std::vector<CacheNode> nodes;           // prefix-cache tree
+  std::map<TokenKey, int64_t> root;
+  int64_t tick = 0;
+  int32_t cached = 0;                     // live nodes
+  int64_t cache_hit_blocks = 0;
+  int64_t cache_evictions = 0;
+
+  std::map<TokenKey, int64_t>& children_of(int64_t parent) {
+    return parent < 0 ? root : nodes[parent].children;
+  }
+  // Nodes whose whole subtree only the tree references (what eviction could free).
+  int64_t evictable(const std::map<TokenKey, int64_t>& ch, bool* all_free) const {
+    int64_t total = 0;
+    *all_free = true;
+    for (const auto& kv : ch) {
+      const CacheNode& nd = nodes[kv.second];
+      bool sub_free = false;
+      total += evictable(nd.children, &sub_free);
+      if (sub_free && ref[nd.block] == 1)
+        ++total;
+      else
+        *all_free = false;
+    }
+    return total;
+  }
+  int64_t evictable() const {
+    bool f = false;
+    return evictable(root, &f);
+  }
+  // Evict the least recently used leaf only the tree references (ties: oldest node).
+  bool evict_one() {
+    int64_t best = -1;
+    for (int64_t i = 0; i < static_cast<int64_t>(nodes.size()); ++i) {
+      const CacheNode& nd = nodes[i];
+      if (!nd.live || !nd.children.empty() || ref[nd.block] != 1) continue;
+      if (best < 0 || nd.last_use < nodes[best].last_use) best = i;
+    }
+    if (best < 0) return false;
+    CacheNode& nd = nodes[best];
+    children_of(nd.parent).erase(nd.key);
+    nd.live = false;
+    --cached;
+    release(nd.block);
+    ++cache_evictions;
+    return true;
+  }
+  // Frees what the tree can to cover a shortfall of `need` blocks; false if it cannot (then
+  // nothing was evicted).
+  bool make_room(int64_t need) {
+    const int64_t short_by = need - nfree;
+    if (short_by <= 0) return true;
+    if (evictable() < short_by) return false;
+    for (int64_t i = 0; i < short_by; ++i) evict_one();
+    return true;
+  }
 
   int32_t take() {  // caller guarantees nfree > 0
     int32_t b = ring[head];
@@ -130,7 +199,7 @@ pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id, int32_t n_tokens, int32_t* sl
   if (bm->seqs.count(seq_id) || bm->is_swapped(seq_id))
     return fail(PA_ERR_SEQ_EXISTS, "pa_bm_add_seq: sequence %lld exists", (long long)seq_id);
   const int64_t need = bm->boundary_blocks(0, n_tokens);
-  if (need > bm->nfree)
+  if (!bm->make_room(need))
     return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_add_seq: needs %lld blocks, %d free",
                 (long long)need, bm->nfree);
   try {
@@ -208,7 +277,7 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
   if (copies > pairs_cap)
     return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: %lld copy pairs needed, capacity %d",
                 (long long)copies, pairs_cap);
-  if (need > bm->nfree)
+  if (!bm->make_room(need))
     return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append_slots: needs %lld blocks, %d free",
                 (long long)need, bm->nfree);
 
@@ -384,6 +453,9 @@ pa_status pa_bm_stats(pa_bm* bm, pa_bm_stats_t* out) {
   for (const auto& kv : bm->swapped) st.swapped_tokens += kv.second;
   st.swap_outs = bm->swap_outs;
   st.swap_ins = bm->swap_ins;
+  st.cached_blocks = bm->cached;
+  st.cache_hit_blocks = bm->cache_hit_blocks;
+  st.cache_evictions = bm->cache_evictions;
   *out = st;
   return ok();
 }
@@ -431,7 +503,7 @@ pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq_id, int32_t* blocks_out, int32_t 
   *n_out = k;
   if (cap < k || (k > 0 && !blocks_out))
     return fail(PA_ERR_INVALID_ARG, "pa_bm_swap_in: %d blocks, capacity %d", k, cap);
-  if (k > bm->nfree)
+  if (!bm->make_room(k))
     return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_swap_in: needs %d blocks, %d free", k, bm->nfree);
   try {
     Seq s;
@@ -464,6 +536,127 @@ pa_status pa_bm_truncate(pa_bm* bm, int64_t seq_id, int32_t n_keep) {
   for (size_t i = keep; i < s.blocks.size(); ++i) bm->release(s.blocks[i]);
   s.blocks.resize(keep);
   s.n = n_keep;
+  return ok();
+}
+
+pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq_id, const int32_t* tokens,
+                               int32_t n_tokens, int32_t* slots_out, int32_t* n_cached_out) {
+  if (!bm || !n_cached_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_cached: NULL argument");
+  *n_cached_out = 0;
+  if (n_tokens < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_cached: n_tokens %d < 0", n_tokens);
+  if (n_tokens > 0 && !tokens) return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_cached: tokens NULL");
+  if (bm->seqs.count(seq_id) || bm->is_swapped(seq_id))
+    return fail(PA_ERR_SEQ_EXISTS, "pa_bm_add_seq_cached: sequence %lld exists", (long long)seq_id);
+  const int32_t B = bm->B;
+  std::vector<int64_t> matched;
+  try {
+    const std::map<TokenKey, int64_t>* ch = &bm->root;
+    TokenKey key(B);
+    for (int32_t j = 0; j + 1 <= n_tokens / B; ++j) {
+      std::copy(tokens + static_cast<size_t>(j) * B, tokens + static_cast<size_t>(j + 1) * B,
+                key.begin());
+      auto it = ch->find(key);
+      if (it == ch->end()) break;
+      matched.push_back(it->second);
+      ch = &bm->nodes[it->second].children;
+    }
+  } catch (...) {
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_cached: out of host memory");
+  }
+  const int64_t m = static_cast<int64_t>(matched.size());
+  const int64_t need = bm->boundary_blocks(0, n_tokens) - m;
+  // The matched blocks are referenced before anything is evicted, so they cannot be.
+  for (int64_t id : matched) ++bm->ref[bm->nodes[id].block];
+  auto undo = [&] {
+    for (int64_t id : matched) --bm->ref[bm->nodes[id].block];
+  };
+  if (need > bm->nfree && bm->evictable() < need - bm->nfree) {
+    undo();
+    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_add_seq_cached: needs %lld blocks, %d free",
+                (long long)need, bm->nfree);
+  }
+  try {
+    Seq s;
+    s.blocks.reserve(static_cast<size_t>(m + need));
+    bm->seqs.reserve(bm->seqs.size() + 1);
+    for (int64_t id : matched) {
+      s.blocks.push_back(bm->nodes[id].block);
+      bm->nodes[id].last_use = bm->tick;
+    }
+    ++bm->tick;
+    bm->make_room(need);  // cannot fail: checked above
+    for (int64_t i = 0; i < need; ++i) s.blocks.push_back(bm->take());
+    s.n = n_tokens;
+    if (slots_out)
+      for (int32_t j = 0; j < n_tokens; ++j) slots_out[j] = s.blocks[j / B] * B + j % B;
+    bm->seqs.emplace(seq_id, std::move(s));
+  } catch (...) {
+    undo();
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_cached: out of host memory");
+  }
+  bm->cache_hit_blocks += m;
+  *n_cached_out = static_cast<int32_t>(m * B);
+  return ok();
+}
+
+pa_status pa_bm_cache_insert(pa_bm* bm, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                             int32_t* n_added_out) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_cache_insert: NULL handle");
+  if (n_added_out) *n_added_out = 0;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return bm->is_swapped(seq_id)
+               ? fail(PA_ERR_SWAPPED, "pa_bm_cache_insert: sequence %lld is swapped out", (long long)seq_id)
+               : fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_cache_insert: unknown sequence %lld", (long long)seq_id);
+  const Seq& sq = it->second;
+  if (n_tokens < 0 || n_tokens > sq.n)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_cache_insert: n_tokens %d outside [0, %d]", n_tokens, sq.n);
+  if (n_tokens > 0 && !tokens) return fail(PA_ERR_INVALID_ARG, "pa_bm_cache_insert: tokens NULL");
+  const int32_t B = bm->B;
+  const int32_t k = n_tokens / B;
+  int32_t added = 0;
+  try {
+    bm->nodes.reserve(bm->nodes.size() + k);
+    int64_t parent = -1;
+    TokenKey key(B);
+    for (int32_t j = 0; j < k; ++j) {
+      std::copy(tokens + static_cast<size_t>(j) * B, tokens + static_cast<size_t>(j + 1) * B,
+                key.begin());
+      auto& ch = bm->children_of(parent);
+      auto f = ch.find(key);
+      int64_t id;
+      if (f == ch.end()) {
+        id = static_cast<int64_t>(bm->nodes.size());
+        CacheNode nd;
+        nd.block = sq.blocks[j];
+        nd.key = key;
+        nd.parent = parent;
+        bm->nodes.push_back(std::move(nd));
+        bm->children_of(parent).emplace(key, id);
+        ++bm->ref[sq.blocks[j]];
+        ++bm->cached;
+        ++added;
+      } else {
+        id = f->second;
+      }
+      bm->nodes[id].last_use = bm->tick;
+      parent = id;
+    }
+  } catch (...) {
+    // A partial insert leaves a consistent tree (every added node holds its reference).
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_cache_insert: out of host memory");
+  }
+  ++bm->tick;
+  if (n_added_out) *n_added_out = added;
+  return ok();
+}
+
+pa_status pa_bm_cache_evict(pa_bm* bm, int32_t n_blocks, int32_t* n_evicted_out) {
+  if (!bm || !n_evicted_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_cache_evict: NULL argument");
+  if (n_blocks < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_cache_evict: n_blocks %d < 0", n_blocks);
+  int32_t done = 0;
+  while (done < n_blocks && bm->evict_one()) ++done;
+  *n_evicted_out = done;
   return ok();
 }
 

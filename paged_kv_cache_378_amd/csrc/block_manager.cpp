@@ -18,8 +18,10 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <functional>
 #include <map>
 #include <new>
+#include <queue>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
@@ -64,6 +66,12 @@ struct pa_bm {
   int64_t swap_ins = 0;
   std::vector<CacheNode> nodes;           // prefix-cache tree
   std::map<TokenKey, int64_t> root;
+  std::vector<int64_t> node_of_block;     // live tree node holding a block, or -1
+  // Eviction candidates (last use, node id), smallest first.  Every node that is evictable
+  // (a live leaf only the tree references) has an entry with its current last use; entries
+  // that no longer match are skipped when popped.
+  std::priority_queue<std::pair<int64_t, int64_t>, std::vector<std::pair<int64_t, int64_t>>,
+                      std::greater<std::pair<int64_t, int64_t>>> cand;
   int64_t tick = 0;
   int32_t cached = 0;                     // live nodes
   int64_t cache_hit_blocks = 0;
@@ -72,48 +80,60 @@ struct pa_bm {
   std::map<TokenKey, int64_t>& children_of(int64_t parent) {
     return parent < 0 ? root : nodes[parent].children;
   }
-  // Nodes whose whole subtree only the tree references (what eviction could free).
-  int64_t evictable(const std::map<TokenKey, int64_t>& ch, bool* all_free) const {
-    int64_t total = 0;
+  // Counts nodes whose whole subtree only the tree references (what eviction could free)
+  // into *total, stopping as soon as it reaches `enough`; true when it did.
+  bool evictable_at_least(const std::map<TokenKey, int64_t>& ch, int64_t enough, int64_t* total,
+                          bool* all_free) const {
     *all_free = true;
     for (const auto& kv : ch) {
       const CacheNode& nd = nodes[kv.second];
       bool sub_free = false;
-      total += evictable(nd.children, &sub_free);
-      if (sub_free && ref[nd.block] == 1)
-        ++total;
-      else
+      if (evictable_at_least(nd.children, enough, total, &sub_free)) return true;
+      if (sub_free && ref[nd.block] == 1) {
+        if (++*total >= enough) return true;
+      } else {
         *all_free = false;
+      }
     }
-    return total;
+    return false;
   }
-  int64_t evictable() const {
+  bool evictable_at_least(int64_t enough) const {
+    if (enough <= 0) return true;
+    int64_t total = 0;
     bool f = false;
-    return evictable(root, &f);
+    return evictable_at_least(root, enough, &total, &f);
   }
   // Evict the least recently used leaf only the tree references (ties: oldest node).
+  bool evictable_node(int64_t id) const {
+    const CacheNode& nd = nodes[id];
+    return nd.live && nd.children.empty() && ref[nd.block] == 1;
+  }
+  void offer(int64_t id) {  // id may have become evictable
+    if (id >= 0 && evictable_node(id)) cand.emplace(nodes[id].last_use, id);
+  }
   bool evict_one() {
-    int64_t best = -1;
-    for (int64_t i = 0; i < static_cast<int64_t>(nodes.size()); ++i) {
-      const CacheNode& nd = nodes[i];
-      if (!nd.live || !nd.children.empty() || ref[nd.block] != 1) continue;
-      if (best < 0 || nd.last_use < nodes[best].last_use) best = i;
+    while (!cand.empty()) {
+      const auto [lu, id] = cand.top();
+      cand.pop();
+      if (!evictable_node(id) || nodes[id].last_use != lu) continue;  // stale entry
+      CacheNode& nd = nodes[id];
+      children_of(nd.parent).erase(nd.key);
+      nd.live = false;
+      --cached;
+      node_of_block[nd.block] = -1;
+      release(nd.block);
+      ++cache_evictions;
+      offer(nd.parent);  // it may be a leaf now
+      return true;
     }
-    if (best < 0) return false;
-    CacheNode& nd = nodes[best];
-    children_of(nd.parent).erase(nd.key);
-    nd.live = false;
-    --cached;
-    release(nd.block);
-    ++cache_evictions;
-    return true;
+    return false;
   }
   // Frees what the tree can to cover a shortfall of `need` blocks; false if it cannot (then
   // nothing was evicted).
   bool make_room(int64_t need) {
     const int64_t short_by = need - nfree;
     if (short_by <= 0) return true;
-    if (evictable() < short_by) return false;
+    if (!evictable_at_least(short_by)) return false;
     for (int64_t i = 0; i < short_by; ++i) evict_one();
     return true;
   }
@@ -131,6 +151,8 @@ struct pa_bm {
       if (tail >= num_blocks) tail -= num_blocks;
       ring[tail] = b;
       ++nfree;
+    } else if (ref[b] == 1 && !node_of_block.empty()) {
+      offer(node_of_block[b]);  // now held by the tree alone?
     }
   }
   // New blocks a sequence of n tokens needs to grow by k tokens (block boundaries crossed).
@@ -162,6 +184,7 @@ pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* in
     bm->num_blocks = num_blocks;
     bm->B = block_size;
     bm->ref.assign(num_blocks, 0);
+    bm->node_of_block.assign(num_blocks, -1);
     bm->ring.resize(num_blocks);
     if (init_free_order) {
       std::vector<char> seen(num_blocks, 0);
@@ -292,6 +315,7 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
         const int32_t last = s->blocks.back();
         const int32_t fresh = bm->take();
         --bm->ref[last];  // stays >= 1: the dry run saw a count above one
+        if (bm->ref[last] == 1) bm->offer(bm->node_of_block[last]);
         s->blocks.back() = fresh;
         copy_pairs_out[2 * np] = last;
         copy_pairs_out[2 * np + 1] = fresh;
@@ -568,9 +592,12 @@ pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq_id, const int32_t* tokens,
   // The matched blocks are referenced before anything is evicted, so they cannot be.
   for (int64_t id : matched) ++bm->ref[bm->nodes[id].block];
   auto undo = [&] {
-    for (int64_t id : matched) --bm->ref[bm->nodes[id].block];
+    for (int64_t id : matched) {
+      --bm->ref[bm->nodes[id].block];
+      bm->offer(id);
+    }
   };
-  if (need > bm->nfree && bm->evictable() < need - bm->nfree) {
+  if (need > bm->nfree && !bm->evictable_at_least(need - bm->nfree)) {
     undo();
     return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_add_seq_cached: needs %lld blocks, %d free",
                 (long long)need, bm->nfree);
@@ -616,7 +643,6 @@ pa_status pa_bm_cache_insert(pa_bm* bm, int64_t seq_id, const int32_t* tokens, i
   const int32_t k = n_tokens / B;
   int32_t added = 0;
   try {
-    bm->nodes.reserve(bm->nodes.size() + k);
     int64_t parent = -1;
     TokenKey key(B);
     for (int32_t j = 0; j < k; ++j) {
@@ -634,12 +660,14 @@ pa_status pa_bm_cache_insert(pa_bm* bm, int64_t seq_id, const int32_t* tokens, i
         bm->nodes.push_back(std::move(nd));
         bm->children_of(parent).emplace(key, id);
         ++bm->ref[sq.blocks[j]];
+        bm->node_of_block[sq.blocks[j]] = id;
         ++bm->cached;
         ++added;
       } else {
         id = f->second;
       }
       bm->nodes[id].last_use = bm->tick;
+      bm->offer(id);  // a touched node keeps its place only with its new use
       parent = id;
     }
   } catch (...) {

@@ -111,6 +111,31 @@ def test_lru_eviction_and_protection(libpa):
     same_cache_state(bm, model)
 
 
+def test_swap_in_evicts_cached_leaves(libpa):
+    """Swap-in allocates like an add: a short pool is first topped up from the cache's least
+    recently used leaves.  Hand-traced: pool of 6 blocks, B = 2, free order 0..5."""
+    bm = libpa.BlockManager(6, 2)
+    model = BlockManagerModel(6, 2)
+    for m in (bm, model):
+        m.add_seq(1, 4)                    # blocks 0, 1
+        m.cache_insert(1, [7, 7, 8, 8])    # nodes (7,7)->0 and (8,8)->1
+        m.free_seq(1)                      # free: 2 3 4 5
+        m.add_seq(2, 6)                    # blocks 2, 3, 4; free: 5
+    assert list(bm.swap_out(2)) == [2, 3, 4] == model.swap_out(2)   # free: 5 2 3 4
+    for m in (bm, model):
+        m.add_seq(3, 6)                    # blocks 5, 2, 3; free: 4
+    with pytest.raises(libpa.OutOfBlocks):
+        bm.add_seq(4, 8)                   # needs 4, can reach 3: nothing changes
+    with pytest.raises(ModelOOB):
+        model.add_seq(4, 8)
+    assert bm.stats()["cached_blocks"] == 2
+    # 3 blocks, 1 free: (8,8) goes first (a leaf), then (7,7), a leaf once (8,8) is gone
+    assert list(bm.swap_in(2)) == [4, 1, 0] == model.swap_in(2)
+    assert bm.stats()["cache_evictions"] == 2 and bm.stats()["cached_blocks"] == 0
+    same_state(bm, model, sorted(model.seqs))
+    same_cache_state(bm, model)
+
+
 def test_random_ops_with_prefix_cache_bit_exact(libpa):
     rng = random.Random(777)
     for B in (2, 4, 16):
@@ -170,8 +195,20 @@ def test_random_ops_with_prefix_cache_bit_exact(libpa):
             elif op < 0.88:
                 n = rng.randint(0, 4)
                 assert bm.cache_evict(n) == model.cache_evict(n)
-            else:
+            elif op < 0.91:
                 s = rng.choice(live)
+                assert list(bm.swap_out(s)) == model.swap_out(s)
+            elif op < 0.94 and model.swapped:
+                s = rng.choice(sorted(model.swapped))
+                try:
+                    want = model.swap_in(s)
+                except ModelOOB:
+                    with pytest.raises(libpa.OutOfBlocks):
+                        bm.swap_in(s)
+                else:
+                    assert list(bm.swap_in(s)) == want   # private copies: may evict cached leaves
+            else:
+                s = rng.choice(live + sorted(model.swapped))
                 model.free_seq(s)
                 bm.free_seq(s)
                 tokens.pop(s, None)

@@ -5,9 +5,9 @@
 // "Taming the Tail", "The Hidden Tax" -- each step stores only the new token's K/V;
 // "vLLM PagedAttention" (tinycto), "1. Underlying Mechanism" -- a step writes the new token's
 // entries and nothing else.  A workgroup moves a group of whole tokens: it reads the group's
-// slots (and lengths) once into LDS, then each thread moves 16-byte chunks of key rows
-// (coalesced read, coalesced write into the K pool) and scatters the matching value chunks
-// into the transposed V blocks (one element every B elements).
+// slots (and lengths) once into LDS, then each thread moves a 16-byte chunk of a key row
+// (coalesced read, coalesced write into the K pool) and value elements into the transposed V
+// blocks (lanes in row order, so neighbouring lanes' elements share cache lines).
 #pragma once
 
 #include "device_common.h"
@@ -55,71 +55,99 @@ inline int write_tokens_per_wg(int Hkv, int D, int elt_bytes) {
   return static_cast<int>(t < 1 ? 1 : (t > kMaxTokPerWG ? kMaxTokPerWG : t));
 }
 
-// Workgroup wg writes tokens [wg * tok_per_wg, ...).  Each round first requests its key and
-// value chunks, then (first round) the group's slots and lengths -- one request per
-// workgroup, so with the slots in host memory the bus round trip is paid once and overlaps
-// the chunk loads -- and then stores.
+// Workgroup wg writes tokens [wg * tok_per_wg, ...).  Each round first requests its key
+// chunks and value elements, then (first round) the group's slots and lengths -- both bus
+// requests issued back to back, one round trip per workgroup when they live in host memory,
+// overlapping the HBM loads -- and then stores.  Keys move as 16-byte chunks (a key row is
+// contiguous in the pool).  Values move one element per lane: a token's value row becomes a
+// column of the transposed V block, so consecutive lanes take consecutive rows d and each
+// store instruction covers a few whole cache lines of the block rather than one element in
+// each of 64 lines.
 template <typename T>
 __device__ __forceinline__ void cache_write_wg(const CacheWriteArgs& a, int64_t wg) {
   constexpr int VEC = 16 / sizeof(T);
-  __shared__ int32_t s_slot[kMaxTokPerWG], s_len[kMaxTokPerWG];
+  static_assert(kWriteChunksPerThread == 1, "one key chunk and VEC value elements per thread");
+  typedef typename std::conditional<sizeof(T) == 2, uint32_t, T>::type Wide;
+  // Per token of the group: physical block (-1: padding or outside the pool, not written),
+  // offset in it, length after the step.
+  __shared__ int32_t s_blk[kMaxTokPerWG], s_off[kMaxTokPerWG], s_len[kMaxTokPerWG];
   const int64_t t0 = wg * a.tok_per_wg;
   if (t0 >= a.T) return;  // uniform over the workgroup
   const int ntok = static_cast<int>(a.T - t0 < a.tok_per_wg ? a.T - t0 : a.tok_per_wg);
   const int D = a.D, B = a.B, Hkv = a.Hkv;
+  // Indices within the group fit 32 bits: at most kMaxTokPerWG tokens of Hkv * D elements.
   const int per_row = D / VEC;
-  const int64_t per_token = static_cast<int64_t>(per_row) * Hkv;
-  const int64_t total = ntok * per_token;
-  const T* key = static_cast<const T*>(a.key);
-  const T* value = static_cast<const T*>(a.value);
+  const int row_elems = Hkv * D;  // a token's elements
+  const int per_token = per_row * Hkv;
+  const int total = ntok * per_token;
+  const T* key = static_cast<const T*>(a.key) + t0 * row_elems;
+  const T* value = static_cast<const T*>(a.value) + t0 * row_elems;
   T* k_cache = static_cast<T*>(a.k_cache);
   T* v_cache = static_cast<T*>(a.v_cache);
   const TablePatch& tp = a.tp;
-  for (int64_t base = 0; base < total; base += kWriteChunksPerWG) {
-    uint4 kv[kWriteChunksPerThread], vv[kWriteChunksPerThread];
+  for (int base = 0; base < total; base += kWriteChunksPerWG) {
+    const int j = base + static_cast<int>(threadIdx.x);  // this thread's key chunk
+    uint4 kv{};
+    if (j < total) kv = *reinterpret_cast<const uint4*>(key + static_cast<int64_t>(j) * VEC);
+    // Value elements in full registers (16-bit halves packed into one register would make
+    // each load wait for the previous one); a lane past the end re-reads element 0.
+    Wide vv[VEC];
 #pragma unroll
-    for (int u = 0; u < kWriteChunksPerThread; ++u) {
-      const int64_t j = base + threadIdx.x + u * kWriteThreads;
-      if (j < total) {
-        const int64_t src = (t0 * Hkv) * D + j * VEC;  // token-major rows: chunk j in order
-        kv[u] = *reinterpret_cast<const uint4*>(key + src);
-        vv[u] = *reinterpret_cast<const uint4*>(value + src);
-      }
+    for (int e = 0; e < VEC; ++e) {
+      const int i = base * VEC + static_cast<int>(threadIdx.x) + e * kWriteThreads;
+      vv[e] = static_cast<Wide>(value[i < total * VEC ? i : 0]);
     }
     if (base == 0) {
       if (static_cast<int>(threadIdx.x) < ntok) {
-        const int64_t t = t0 + threadIdx.x;
-        s_slot[threadIdx.x] = ld_step(a.slots + t, a.sys);
-        if (tp.tables) s_len[threadIdx.x] = ld_step(tp.ctx_lens + t / tp.tokens_each, a.sys);
+        const int32_t t = static_cast<int32_t>(t0) + static_cast<int32_t>(threadIdx.x);
+        const int32_t* lp = tp.tables ? tp.ctx_lens + t / tp.tokens_each : nullptr;
+        const int32_t sl = ld_step(a.slots + t, a.sys);
+        const int32_t ln = lp ? ld_step(lp, a.sys) : 0;
+        const bool ok = sl >= 0 && sl < a.n_slots;
+        s_blk[threadIdx.x] = ok ? sl / B : -1;
+        s_off[threadIdx.x] = ok ? sl % B : 0;
+        s_len[threadIdx.x] = ln;
       }
       __syncthreads();
     }
-#pragma unroll
-    for (int u = 0; u < kWriteChunksPerThread; ++u) {
-      const int64_t j = base + threadIdx.x + u * kWriteThreads;
-      if (j >= total) continue;
-      const int k = static_cast<int>(j / per_token);
-      const int rem = static_cast<int>(j - k * per_token);
+    if (j < total) {
+      const int k = j / per_token;
+      const int rem = j - k * per_token;
       const int h = rem / per_row, c = rem - h * per_row;
-      const int32_t slot = s_slot[k];
-      if (slot < 0 || slot >= a.n_slots) continue;  // padding or out of the pool: not written
-      const int64_t p = slot / B;
-      const int o = slot % B;
-      if (tp.tables && c == 0 && h == 0) {
-        // The token's logical block now lives in physical block p.  Tokens of one sequence
-        // that share a block write the same value.
-        const int64_t t = t0 + k;
-        const int64_t r = t / tp.tokens_each;
-        const int64_t pos = static_cast<int64_t>(s_len[k]) - tp.tokens_each + t % tp.tokens_each;
-        if (pos >= 0 && pos < static_cast<int64_t>(tp.max_blocks) * B)
-          tp.tables[r * tp.max_blocks + pos / B] = static_cast<int32_t>(p);
+      const int64_t p = s_blk[k];
+      if (p >= 0) {
+        const int o = s_off[k];
+        if (tp.tables && c == 0 && h == 0) {
+          // The token's logical block now lives in physical block p.  Tokens of one sequence
+          // that share a block write the same value.
+          const int64_t t = t0 + k;
+          const int64_t r = t / tp.tokens_each;
+          const int64_t pos = static_cast<int64_t>(s_len[k]) - tp.tokens_each + t % tp.tokens_each;
+          if (pos >= 0 && pos < static_cast<int64_t>(tp.max_blocks) * B)
+            tp.tables[r * tp.max_blocks + pos / B] = static_cast<int32_t>(p);
+        }
+        *reinterpret_cast<uint4*>(k_cache + ((p * Hkv + h) * B + o) * D + static_cast<int64_t>(c) * VEC) = kv;
       }
-      *reinterpret_cast<uint4*>(k_cache + ((p * Hkv + h) * B + o) * D + static_cast<int64_t>(c) * VEC) = kv[u];
-      T vals[VEC];
-      __builtin_memcpy(vals, &vv[u], 16);
-      T* dst = v_cache + ((p * Hkv + h) * D + static_cast<int64_t>(c) * VEC) * B + o;
+    }
+    // Element i = (token k, head h, row d); the next one this thread takes is kWriteThreads on.
+    int i = base * VEC + static_cast<int>(threadIdx.x);
+    int k = i / row_elems;
+    int h = (i - k * row_elems) / D;
+    int d = i - k * row_elems - h * D;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) dst[static_cast<int64_t>(e) * B] = vals[e];
+    for (int e = 0; e < VEC; ++e) {
+      if (i >= total * VEC) break;
+      const int64_t p = s_blk[k];
+      if (p >= 0) v_cache[((p * Hkv + h) * D + d) * B + s_off[k]] = static_cast<T>(vv[e]);
+      i += kWriteThreads;
+      d += kWriteThreads;
+      while (d >= D) {
+        d -= D;
+        if (++h == Hkv) {
+          h = 0;
+          ++k;
+        }
+      }
     }
   }
 }
@@ -146,7 +174,7 @@ inline CacheWriteArgs make_cache_write_args(const void* key, const void* value, 
 }
 
 // Workgroups of a cache write.
-inline int64_t cache_write_wgs(const CacheWriteArgs& w) {
+__host__ __device__ inline int64_t cache_write_wgs(const CacheWriteArgs& w) {
   return (w.T + w.tok_per_wg - 1) / w.tok_per_wg;
 }
 

@@ -694,13 +694,15 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     int n = 0;
     if (s < a.S) {
       bool bad;
+      // The table entry is requested first: it then travels with the length, which may have
+      // to come over the bus.
+      const int blk = a.tables[static_cast<size_t>(s) * a.max_blocks];
       const int raw = ld_step(lens_src + s, sys);
       if (lens_out) lens_out[s] = raw;
       if (s < kPlanKeep) s_len[s] = raw;
       n = eff_len(raw, a.len_cap, bad);
       // Prefix sharing shows as one physical first block in several tables.  A set in LDS
       // (bounded probing, so a full set only undercounts) counts the repeats.
-      const int blk = a.tables[static_cast<size_t>(s) * a.max_blocks];
       if (blk >= 0) {
         int h = static_cast<int>((static_cast<uint32_t>(blk) * 2654435761u) >> (32 - kShareBits));
         for (int k = 0; k < kShareProbes; ++k) {

@@ -120,6 +120,13 @@ STEP_CASES = {
                                         extra_blocks=10),
     "bf16_b64": lambda: wl.custom_decode("step64", 48, [1, 63, 64, 65, 500], 32, 8, 128, 64,
                                          "bf16", extra_blocks=6),
+    # more (sequence, kv-head) pairs than workgroups: some sequences' first partition comes
+    # from the plan's list, not from a workgroup's first item; lengths at and around block
+    # and partition boundaries, one-token sequences
+    "bf16_many": lambda: wl.custom_decode(
+        "stepmany", 49, [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 512, 513, 1023, 1024,
+                         1025, 1500, 2047, 2048, 2049] * 6 + [700] * 34, 64, 8, 128, 16, "bf16",
+        extra_blocks=40),
 }
 
 

@@ -20,7 +20,7 @@
 //     a one-workgroup kernel (pa_decode) or as workgroup 0 of the step's first kernel beside
 //     the cache write (pa_decode_step).  The decode kernel is persistent (about as many
 //     workgroups as the chip holds at once) and pulls items from that list through atomic
-//     counters, claiming the next item while it works on the current one; a batch that
+//     counters, claiming the next item as the current one's tiles end; a batch that
 //     shares prefix blocks is claimed per XCD so each kv-head stays in one XCD's L2.  No
 //     workgroup is launched for a partition that does not exist, and the short items fill
 //     the tail;
@@ -233,9 +233,9 @@ __device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, int s, int 
   return it;
 }
 
-// Persistent work loop.  Workgroup g starts with item g; the next item is claimed while the
-// current one runs, so the atomic's latency is hidden; every workgroup leaves once the
-// claims pass the item count.  Two ways to claim, chosen by the planner (queue[1]):
+// Persistent work loop.  Workgroup g starts with item g; the next item is claimed near the
+// end of the current one, so the atomic's latency hides behind its epilogue; every workgroup
+// leaves once the claims pass the item count.  Two ways to claim, chosen by the planner (queue[1]):
 //   * one global cursor (queue[10]): every workgroup takes the next item of the longest-first
 //     list, so the XCDs balance among themselves;
 //   * one queue per XCD (queue[2 + x]), for batches whose sequences share prefix blocks.  The
@@ -251,11 +251,20 @@ __device__ __forceinline__ void for_each_item(const DecodeArgs& a, int* s_next, 
   const int x = static_cast<int>(blockIdx.x % kXcd);
   int i = blockIdx.x;
   while (i < count) {
+    // The body calls claim() once it is nearly done (thread 0 takes the next item); a claim
+    // taken a whole item ahead commits the workgroup to work that an idle one could run, and
+    // with items of up to 2048 tokens that shows as a ragged end (1-5% of the decode).
     int nxt = 0;
-    if (threadIdx.x == 0)
-      nxt = per_xcd ? atomicAdd(&a.queue[2 + x], 1) * kXcd + x : atomicAdd(&a.queue[2 + kXcd], 1);
+    bool claimed = false;
+    auto claim = [&] {
+      if (threadIdx.x == 0 && !claimed) {
+        nxt = per_xcd ? atomicAdd(&a.queue[2 + x], 1) * kXcd + x : atomicAdd(&a.queue[2 + kXcd], 1);
+        claimed = true;
+      }
+    };
     const int2 it = a.items[i / a.Hkv];
-    body(it.x, i % a.Hkv, it.y);
+    body(it.x, i % a.Hkv, it.y, claim);
+    claim();  // a body that had no tile for wave 0
     if (threadIdx.x == 0) *s_next = nxt;
     __syncthreads();
     i = __builtin_amdgcn_readfirstlane(*s_next);
@@ -288,10 +297,10 @@ struct MfmaV {
   bf16x8 v[D / 16];     // V^T rows (16 dims per tile) x 8 tokens of this lane group
 };
 
-template <int D, int B>
+template <int D, int B, typename Claim>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, int part,
                                           int* s_tbl, int* s_bad, float (*s_ml)[16][2],
-                                          float (*s_o)[16][D]) {
+                                          float (*s_o)[16][D], Claim&& claim) {
   constexpr int NST = D / 32, NNT = D / 16;
   const int lane = threadIdx.x & (kWave - 1), w = wave_id();
   const int r16 = lane & 15, gp = lane >> 4;
@@ -441,6 +450,10 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, i
     for (int tile = w; tile < ntiles; tile += kNW) step(kt, vt, tile, tile + kNW);
   }
 
+  // Wave 0 is done with its tiles: claim the next item now (thread 0), so the atomic's latency
+  // hides behind the epilogue.  (Claiming one or two tiles earlier measured the same or up to
+  // 1% slower on long contexts; at the start of the item, 1-5% slower.)
+  claim();
   // Wave state -> LDS.  l_run is per lane (its 8 tokens); sum the four lane groups.
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
@@ -464,8 +477,8 @@ void decode_mfma_kernel(DecodeArgs a) {
   __shared__ int s_bad, s_next;
   __shared__ float s_ml[kNW][16][2];
   __shared__ float s_o[kNW][16][D];
-  for_each_item(a, &s_next, [&](int s, int kvh, int part) {
-    mfma_item<D, B>(a, s, kvh, part, s_tbl, &s_bad, s_ml, s_o);
+  for_each_item(a, &s_next, [&](int s, int kvh, int part, auto&& claim) {
+    mfma_item<D, B>(a, s, kvh, part, s_tbl, &s_bad, s_ml, s_o, claim);
   });
 }
 
@@ -635,7 +648,8 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
   __shared__ float s_ml[kNW][G][2];
   __shared__ float s_o[kNW][G][D];
   __shared__ __attribute__((aligned(16))) float s_p[kNW][G][TPR];  // weights of the round
-  for_each_item(a, &s_next, [&](int s, int kvh, int part) {
+  for_each_item(a, &s_next, [&](int s, int kvh, int part, auto&& claim) {
+    claim();  // at the start: these items are short
     valu_item<T, D, B, G, LPT, TPR>(a, s, kvh, part, s_tbl, &s_bad, s_ml, s_o, s_p);
   });
 }

@@ -59,6 +59,8 @@ constexpr int kNW = 4;            // waves per workgroup
 constexpr int kXcd = 8;           // XCDs of an MI355X (one work queue each)
 constexpr int kMaxPT = 8192;      // largest partition (tokens)
 constexpr int kMinAutoPT = 256;   // smallest partition the automatic choice uses
+constexpr int kMaxAutoPT = 4096;  // largest partition the automatic choice uses
+constexpr int kPtSlot = 11;       // queue[kPtSlot]: the partition length the plan used
 constexpr int kPlanThreads = 256;
 constexpr int kMaxBuckets = kMaxPT / 32 + 1;  // partial partitions bucketed by 32-token tiles
 constexpr int kPlanKeep = 2048;  // sequences whose lengths the plan keeps in LDS between passes
@@ -473,6 +475,8 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, i
 template <int D, int B>
 __global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(kMfmaWaves)))
 void decode_mfma_kernel(DecodeArgs a) {
+  a.PT = a.queue[kPtSlot];                        // the plan's choice
+  a.Pmax = (a.len_cap + a.PT - 1) / a.PT;  // partial results packed for it
   __shared__ int s_tbl[kMaxPT / B];
   __shared__ int s_bad, s_next;
   __shared__ float s_ml[kNW][16][2];
@@ -642,6 +646,8 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, int s, int kvh, i
 
 template <typename T, int D, int B, int G, int LPT>
 __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) {
+  a.PT = a.queue[kPtSlot];                        // the plan's choice
+  a.Pmax = (a.len_cap + a.PT - 1) / a.PT;  // partial results packed for it
   constexpr int TPR = kWave / LPT;      // tokens per round
   __shared__ int s_tbl[kMaxPT / B];
   __shared__ int s_bad, s_next;
@@ -690,47 +696,81 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   __shared__ int s_len[kPlanKeep];     // pass 1's lengths of the first kPlanKeep sequences
   __shared__ int s_first[kShareSlots];  // open-addressing set of first blocks seen
   __shared__ int s_dups;                // sequences whose first block another one also has
-  const int nbk = a.PT / 32;  // a partial partition has 0 .. PT-1 tokens: buckets 0 .. nbk
-  for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
+  __shared__ unsigned long long s_total;  // sum of the context lengths
+  __shared__ int s_pt;
   for (int i = threadIdx.x; i < kShareSlots; i += kPlanThreads) s_first[i] = -1;
   if (threadIdx.x == 0) {
     s_full = 0;
     s_dups = 0;
+    s_total = 0;
   }
   if (a.Pmax > 1)
     for (int i = threadIdx.x; i < a.S * a.Hkv; i += kPlanThreads) a.done[i] = 0;
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   __syncthreads();
-  // Pass 1, one sequence per thread per round: full partitions get consecutive entries from
-  // a block-wide prefix sum; partial ones are counted per bucket.
+  // Pass 0, one sequence per thread per round: lengths (kept in LDS, copied to lens_out), the
+  // sharing test and the total.
+  unsigned long long my_total = 0;
+  for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
+    bool bad;
+    // The table entry is requested first: it then travels with the length, which may have to
+    // come over the bus.
+    const int blk = a.tables[static_cast<size_t>(s) * a.max_blocks];
+    const int raw = ld_step(lens_src + s, sys);
+    if (lens_out) lens_out[s] = raw;
+    if (s < kPlanKeep) s_len[s] = raw;
+    my_total += static_cast<unsigned long long>(eff_len(raw, a.len_cap, bad));
+    // Prefix sharing shows as one physical first block in several tables.  A set in LDS
+    // (bounded probing, so a full set only undercounts) counts the repeats.
+    if (blk >= 0) {
+      int h = static_cast<int>((static_cast<uint32_t>(blk) * 2654435761u) >> (32 - kShareBits));
+      for (int k = 0; k < kShareProbes; ++k) {
+        const int old = atomicCAS(&s_first[h], -1, blk);
+        if (old == -1) break;
+        if (old == blk) {
+          atomicAdd(&s_dups, 1);
+          break;
+        }
+        h = (h + 1) & (kShareSlots - 1);
+      }
+    }
+  }
+  if (my_total) atomicAdd(&s_total, my_total);
+  __syncthreads();
+  // Partition length: the caller's, or the longest power of two in [kMinAutoPT, kMaxAutoPT]
+  // that is at most 3/4 of one workgroup's share of the work (token-heads / grid).  Longer
+  // partitions mean fewer partial results and item start-ups; the bound keeps the longest
+  // items short enough for the tail to even out.
+  if (threadIdx.x == 0) {
+    int pt = a.PT;
+    if (pt == 0) {
+      const unsigned long long share = s_total * static_cast<unsigned long long>(a.Hkv) /
+                                       static_cast<unsigned long long>(grid > 0 ? grid : 1);
+      pt = kMinAutoPT;
+      for (int c = kMaxAutoPT; c > kMinAutoPT; c /= 2)
+        if (4ull * c <= 3ull * share) {
+          pt = c;
+          break;
+        }
+    }
+    s_pt = pt;
+  }
+  __syncthreads();
+  const int PT = s_pt;
+  const int nbk = PT / 32;  // a partial partition has 0 .. PT-1 tokens: buckets 0 .. nbk
+  for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
+  __syncthreads();
+  // Pass 1: full partitions get consecutive entries from a block-wide prefix sum; partial ones
+  // are counted per bucket.
   for (int s0 = 0; s0 < a.S; s0 += kPlanThreads) {
     const int s = s0 + threadIdx.x;
     int n = 0;
     if (s < a.S) {
       bool bad;
-      // The table entry is requested first: it then travels with the length, which may have
-      // to come over the bus.
-      const int blk = a.tables[static_cast<size_t>(s) * a.max_blocks];
-      const int raw = ld_step(lens_src + s, sys);
-      if (lens_out) lens_out[s] = raw;
-      if (s < kPlanKeep) s_len[s] = raw;
+      const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
       n = eff_len(raw, a.len_cap, bad);
-      // Prefix sharing shows as one physical first block in several tables.  A set in LDS
-      // (bounded probing, so a full set only undercounts) counts the repeats.
-      if (blk >= 0) {
-        int h = static_cast<int>((static_cast<uint32_t>(blk) * 2654435761u) >> (32 - kShareBits));
-        for (int k = 0; k < kShareProbes; ++k) {
-          const int old = atomicCAS(&s_first[h], -1, blk);
-          if (old == -1) break;
-          if (old == blk) {
-            atomicAdd(&s_dups, 1);
-            break;
-          }
-          h = (h + 1) & (kShareSlots - 1);
-        }
-      }
     }
-    const int full = s < a.S ? n / a.PT : 0, rem = n - full * a.PT;
+    const int full = s < a.S ? n / PT : 0, rem = n - full * PT;
     const int incl = wave_inclusive_sum(full);
     if (lane == kWave - 1) s_wave[w] = incl;
     if (s < a.S && (rem > 0 || n == 0)) atomicAdd(&s_cnt[(rem + 31) / 32], 1);
@@ -755,6 +795,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       a.queue[1] = (a.Hkv % kXcd == 0 && 8 * s_dups >= a.S) ? 1 : 0;
       for (int x = 0; x < kXcd; ++x) a.queue[2 + x] = (grid - x + kXcd - 1) / kXcd;
       a.queue[2 + kXcd] = grid;
+      a.queue[kPtSlot] = PT;
     }
   }
   __syncthreads();
@@ -763,7 +804,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     bool bad;
     const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
     const int n = eff_len(raw, a.len_cap, bad);
-    const int full = n / a.PT, rem = n - full * a.PT;
+    const int full = n / PT, rem = n - full * PT;
     if (rem > 0 || n == 0) a.items[atomicAdd(&s_base[(rem + 31) / 32], 1)] = make_int2(s, full);
   }
 }
@@ -793,17 +834,6 @@ __global__ __launch_bounds__(kPlanThreads) void step_prologue_kernel(CacheWriteA
 // ---------------------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------------------
-// Partition length when the caller leaves it to the library: the longest of 2048 .. 256
-// tokens that still gives the persistent grid several items per workgroup (judged from the
-// longest context; shorter contexts only add items).  Longer partitions mean fewer partial
-// results to write and merge and fewer item start-ups; shorter ones balance small batches.
-static int auto_partition(int S, int Hkv, int max_ctx_len, int resident) {
-  for (int pt = 2048; pt > kMinAutoPT; pt /= 2) {
-    const int64_t items = static_cast<int64_t>(S) * Hkv * ((max_ctx_len + pt - 1) / pt);
-    if (items >= 4 * static_cast<int64_t>(resident)) return pt;
-  }
-  return kMinAutoPT;
-}
 
 // Workspace: [queue header | work list | partition (m, l) | partition outputs].  The work
 // list is sized for Hq heads (an upper bound of Hkv) so that the size query needs no Hkv.
@@ -889,8 +919,11 @@ static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void*
                 "(bf16: 1..16, f32: 1, 2, 4, 8)", a.G, dtype);
   const int cap = resident_grid(reinterpret_cast<const void*>(k), kNW * kWave, 0);
   if (cap <= 0) return fail(PA_ERR_HIP, "pa_decode: cannot query the device's compute units");
-  a.PT = partition_tokens ? partition_tokens : auto_partition(a.S, a.Hkv, a.len_cap, cap);
-  a.Pmax = (a.len_cap + a.PT - 1) / a.PT;
+  // partition_tokens = 0: the plan picks the length from the batch (at least kMinAutoPT, which
+  // bounds the partitions per sequence; the size query assumed the same).
+  a.PT = partition_tokens;
+  const int pt_min = partition_tokens ? partition_tokens : kMinAutoPT;
+  a.Pmax = (a.len_cap + pt_min - 1) / pt_min;
   if (static_cast<int64_t>(a.S) * a.Pmax * a.Hq >= (int64_t(1) << 31))
     return fail(PA_ERR_INVALID_ARG, "pa_decode: S * partitions * Hq too large");
   const WsLayout L = ws_layout(a.S, a.Hq, D, a.Pmax);  // fits: PT >= the size query's choice

@@ -157,7 +157,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the decode path needs no "
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the decode path needs no "
                           "collective; run with --gpus 1"}), flush=True)
         return 2
 
@@ -189,12 +189,18 @@ def main() -> int:
     return 0 if "error" not in line else 1
 
 
-def timed_loop(args, step):
+SPREAD_BLOCKS = 5  # blocks of steps timed after the main region, for the per-step spread
+
+
+def timed_loop(args, step, spread=False, on_timed_end=None):
     """Warm-up, then exactly args.steps timed steps between two device synchronisations, with
     the set-up's Python objects frozen and the cyclic GC off (a collection over the workload
     script once stalled one step for tens of milliseconds).  Returns the wall-clock seconds of
     the timed steps and the milliseconds between two HIP events recorded on the launch stream
-    at the start and the end of the timed region."""
+    at the start and the end of the timed region.  With `spread`, SPREAD_BLOCKS more blocks of
+    spread_steps(args) steps follow the timed region, each between its own pair of events (an
+    event per step would add its own gap to every step), and a third value lists their
+    per-step milliseconds."""
     import torch
     gc.collect()
     gc.freeze()
@@ -210,9 +216,43 @@ def timed_loop(args, step):
             step(i, True)
         ev1.record()
         torch.cuda.synchronize()
-        return time.perf_counter() - t0, ev0.elapsed_time(ev1)
+        elapsed = time.perf_counter() - t0
+        if on_timed_end:
+            on_timed_end()
+        blocks = []
+        if spread:
+            # the blocks follow each other with no synchronisation between them, so the stream
+            # never runs dry; the events are read once all have completed
+            n = spread_steps(args)
+            i = args.warmup + args.steps
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(SPREAD_BLOCKS)]
+            for e0, e1 in evs:
+                e0.record()
+                for _ in range(n):
+                    step(i, False)
+                    i += 1
+                e1.record()
+            torch.cuda.synchronize()
+            blocks = [e0.elapsed_time(e1) / n for e0, e1 in evs]
+        if spread:
+            return elapsed, ev0.elapsed_time(ev1), blocks
+        return elapsed, ev0.elapsed_time(ev1)
     finally:
         gc.enable()
+
+
+def spread_steps(args):
+    return max(1, args.steps // SPREAD_BLOCKS)
+
+
+def spread_summary(blocks):
+    """Per-step milliseconds of the spread blocks: p10, median, p90."""
+    b = np.asarray(blocks, np.float64)
+    return {"p10_ms": round(float(np.percentile(b, 10)), 4),
+            "median_ms": round(float(np.median(b)), 4),
+            "p90_ms": round(float(np.percentile(b, 90)), 4),
+            "blocks": len(blocks), "steps_per_block": None}
 
 
 def base_line(args, w, ms_step):
@@ -231,7 +271,7 @@ def run_decode(args, w, st, t_setup):
 
     dev = st.device
     S, B = w.num_seqs, w.block_size
-    total = args.warmup + args.steps
+    total = args.warmup + args.steps + SPREAD_BLOCKS * spread_steps(args)
     max_ctx = st.max_ctx + total
     max_blocks = (max_ctx + B - 1) // B
     nbytes = _lib.pa_decode_workspace_size(S, w.hq, w.head_dim, max_ctx, args.partition)
@@ -277,7 +317,13 @@ def run_decode(args, w, st, t_setup):
         if i % MARK == MARK - 1:
             marks[(i // MARK) % len(marks)].record(stream)
 
-    elapsed, region_ms = timed_loop(args, step)
+    pool_end, tables_end = {}, []
+
+    def at_timed_end():  # pool statistics and tables as the last timed step left them
+        pool_end.update(st.bm.stats())
+        tables_end.extend(st.bm.block_tables(ids, max_blocks))
+
+    elapsed, region_ms, blocks = timed_loop(args, step, spread=True, on_timed_end=at_timed_end)
     if not torch.isfinite(out.float()).all():
         return {"error": "non-finite decode output"}
     # the device-resident tables and lengths must still mirror the block manager's exactly
@@ -303,7 +349,7 @@ def run_decode(args, w, st, t_setup):
         # counts each physical block once; the logical (per-sequence) rate is "effective"
         elt = 2
         logical_kv = tokens * w.hkv * w.head_dim * 2 * elt
-        uniq = unique_kv_bytes(final_tables, final_lens, w)
+        uniq = unique_kv_bytes(tables_end[0], tables_end[1], w)
         extra = {"effective_logical_GBps": round(dec_bytes_avg / (dec_avg_ms * 1e-3) / 1e9, 1),
                  "unique_kv_bytes": uniq, "logical_kv_bytes": logical_kv,
                  "cow_pairs_first_step": n_pairs[0], "cow_pairs_later_steps": sum(n_pairs[1:])}
@@ -327,15 +373,20 @@ def run_decode(args, w, st, t_setup):
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "host_block_manager_us": round(1e6 * float(np.median(host_s)), 1),
         "block_size": w.block_size,
-        "pool": {k: st.bm.stats()[k] for k in ("logical_blocks", "live_tokens", "tail_waste_slots",
-                                               "used_blocks", "num_blocks")},
+        "pool": {k: pool_end[k] for k in ("logical_blocks", "live_tokens", "tail_waste_slots",
+                                          "used_blocks", "num_blocks")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if headline and args.pool == "churned" else None,
+                     "traffic": measured_traffic()
+                     if headline and args.pool == "churned" and w.block_size == 16 else None,
                      "kernel": "pa_decode_step (cache write + plan, persistent split-K decode, "
                                "merge); avg_ms = HIP-event time of the timed region / steps",
                      "avg_ms": round(dec_avg_ms, 4), "algorithmic_bytes": int(dec_bytes_avg)},
         "cpu_baseline": cpu,
+        "step_ms_spread": dict(spread_summary(blocks), steps_per_block=spread_steps(args),
+                               note="per-step time of %d further blocks of steps after the "
+                                    "timed region, each between its own HIP events"
+                                    % SPREAD_BLOCKS),
         "setup_s": round(t_setup, 1),
     })
     line.update(extra)

@@ -17,6 +17,98 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(CacheWriteAr
   cache_write_wg<T>(a, blockIdx.x);
 }
 
+// Prefill-sized writes (many tokens, usually consecutive slots of each sequence): a workgroup
+// takes kTileTok consecutive tokens of one kv-head.  Key rows go from the loaded registers to
+// the pool (each a contiguous row of its block).  Value rows are staged in LDS and then stored
+// transposed: the lanes of a 32-thread group take the tile's tokens at one dim, so the stores
+// of consecutive slots of a block land in one contiguous run of its V^T row (the per-token
+// path stores one element per lane of a single token).  Bit copy, like the per-token path;
+// slot < 0 or outside the pool: not written.
+constexpr int kTileTok = 32;
+constexpr int kTiledMinTokens = 1024;  // fewer tokens: the per-token path (decode steps)
+
+template <typename T>
+__global__ __launch_bounds__(kWriteThreads) void cache_write_tiled_kernel(CacheWriteArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int kMaxPer = kTileTok * (128 * 4 / 16) / kWriteThreads;  // chunks per thread, max
+  // V rows of the tile's tokens: row j at word j * stride; one pad word per row puts the
+  // transposed reads (32 tokens at one dim) on 32 different banks
+  extern __shared__ uint32_t s_v[];
+  __shared__ int32_t s_blk[kTileTok], s_off[kTileTok], s_len[kTileTok];
+  const int D = a.D, B = a.B, Hkv = a.Hkv;
+  const int h = blockIdx.y;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTileTok;
+  const int ntok = static_cast<int>(a.T - t0 < kTileTok ? a.T - t0 : kTileTok);
+  const int row_words = D * static_cast<int>(sizeof(T)) / 4, stride = row_words + 1;
+  const int chunks = D / VEC;  // 16-byte chunks of a (token, kv-head) row
+  const int total = ntok * chunks;
+  const int tid = static_cast<int>(threadIdx.x);
+  const T* key = static_cast<const T*>(a.key);
+  const T* value = static_cast<const T*>(a.value);
+  const TablePatch& tp = a.tp;
+  u32x4 kr[kMaxPer], vr[kMaxPer];  // vector types: HIP's uint4 struct kept these in scratch
+#pragma unroll
+  for (int r = 0; r < kMaxPer; ++r) {
+    const int c = tid + r * kWriteThreads;
+    if (c < total) {
+      const int j = c / chunks, q = c - j * chunks;
+      const int64_t src = ((t0 + j) * Hkv + h) * D + static_cast<int64_t>(q) * VEC;
+      kr[r] = *reinterpret_cast<const u32x4*>(key + src);
+      vr[r] = *reinterpret_cast<const u32x4*>(value + src);
+    }
+  }
+  if (tid < ntok) {  // slots (and lengths) after the row loads: one bus round trip overlaps them
+    const int32_t t = static_cast<int32_t>(t0) + tid;
+    const int32_t* lp = tp.tables ? tp.ctx_lens + t / tp.tokens_each : nullptr;
+    const int32_t sl = ld_step(a.slots + t, a.sys);
+    const int32_t ln = lp ? ld_step(lp, a.sys) : 0;
+    const bool ok = sl >= 0 && sl < a.n_slots;
+    s_blk[tid] = ok ? sl / B : -1;
+    s_off[tid] = ok ? sl % B : 0;
+    s_len[tid] = ln;
+  }
+  __syncthreads();
+  T* k_cache = static_cast<T*>(a.k_cache);
+  T* v_cache = static_cast<T*>(a.v_cache);
+#pragma unroll
+  for (int r = 0; r < kMaxPer; ++r) {
+    const int c = tid + r * kWriteThreads;
+    if (c < total) {
+      const int j = c / chunks, q = c - j * chunks;
+      const int64_t p = s_blk[j];
+      if (p >= 0)
+        *reinterpret_cast<u32x4*>(k_cache + ((p * Hkv + h) * B + s_off[j]) * D +
+                                  static_cast<int64_t>(q) * VEC) = kr[r];
+      uint32_t* row = s_v + j * stride + q * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) row[k] = vr[r][k];
+    }
+  }
+  if (tp.tables && h == 0 && tid < ntok && s_blk[tid] >= 0) {
+    // the token's logical block now lives in physical block s_blk (tokens of one sequence that
+    // share a block write the same value)
+    const int64_t t = t0 + tid;
+    const int64_t rr = t / tp.tokens_each;
+    const int64_t pos = static_cast<int64_t>(s_len[tid]) - tp.tokens_each + t % tp.tokens_each;
+    if (pos >= 0 && pos < static_cast<int64_t>(tp.max_blocks) * B)
+      tp.tables[rr * tp.max_blocks + pos / B] = s_blk[tid];
+  }
+  __syncthreads();
+  const int j = tid % kTileTok;
+  if (j < ntok) {
+    const int64_t p = s_blk[j];
+    if (p >= 0) {
+      const int o = s_off[j];
+      for (int d = tid / kTileTok; d < D; d += kWriteThreads / kTileTok) {
+        const uint32_t wv = s_v[j * stride + (sizeof(T) == 2 ? d >> 1 : d)];
+        const uint32_t e = sizeof(T) == 2 ? (d & 1 ? wv >> 16 : wv & 0xFFFFu) : wv;
+        v_cache[((p * Hkv + h) * D + d) * B + o] = __builtin_bit_cast(T, static_cast<
+            typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type>(e));
+      }
+    }
+  }
+}
+
 // One workgroup per pair; each copies the whole block (all kv-heads and slots) of both pools.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
                                                           uint4* __restrict__ v_cache,
@@ -85,8 +177,17 @@ static pa_status launch_cache_write(const char* who, const void* key, const void
                                     void* stream) {
   const CacheWriteArgs w = make_cache_write_args(key, value, k_cache, v_cache, slot_mapping, T,
                                                  Hkv, D, B, num_blocks, dtype, tp);
-  const dim3 grid(static_cast<unsigned>(cache_write_wgs(w)));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T >= kTiledMinTokens && Hkv <= 65535) {
+    const dim3 tg(static_cast<unsigned>((T + kTileTok - 1) / kTileTok), static_cast<unsigned>(Hkv));
+    const size_t lds = static_cast<size_t>(kTileTok) * (D * elem_bytes(dtype) / 4 + 1) * 4;
+    if (dtype == PA_DTYPE_F32)
+      hipLaunchKernelGGL(cache_write_tiled_kernel<float>, tg, dim3(kWriteThreads), lds, s, w);
+    else
+      hipLaunchKernelGGL(cache_write_tiled_kernel<uint16_t>, tg, dim3(kWriteThreads), lds, s, w);
+    return launch_status(who);
+  }
+  const dim3 grid(static_cast<unsigned>(cache_write_wgs(w)));
   if (dtype == PA_DTYPE_F32)
     hipLaunchKernelGGL(cache_write_kernel<float>, grid, dim3(kWriteThreads), 0, s, w);
   else

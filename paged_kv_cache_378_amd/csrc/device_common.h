@@ -22,6 +22,12 @@ __device__ __forceinline__ bf16x8 ld_kv16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
 
+// The same load without the non-temporal hint, for K/V lines other workgroups will read again
+// soon (blocks shared by several sequences).
+__device__ __forceinline__ bf16x8 ld_kv16_keep(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
   return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }

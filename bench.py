@@ -97,15 +97,16 @@ WORKLOADS = {
 PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
 
-def make_workload(wl, name, pool, block_size=16):
+def make_workload(wl, name, pool, block_size=16, batch=0):
     if name in ("llama70b", "swap"):
+        kw = {"S": batch} if batch else {}
         if pool == "churned":
-            return wl.llama70b(B=block_size)
-        w = wl.llama70b(churn_steps=0, B=block_size)
+            return wl.llama70b(B=block_size, **kw)
+        w = wl.llama70b(churn_steps=0, B=block_size, **kw)
     elif name == "mistral7b":
         w = wl.mistral()
     elif name == "long32k":
-        w = wl.long_context()
+        w = wl.long_context(**({"S": batch} if batch else {}))
     elif name == "shared16":
         w = wl.shared_prefix(B=16)
     elif name == "shared32":
@@ -151,6 +152,9 @@ def main() -> int:
     ap.add_argument("--block-size", type=int, choices=[16, 32, 64], default=16,
                     help="block size of the llama70b / swap batch (the block-size trade-off: "
                          "table entries, tail waste, kernel rate)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="llama70b / long32k: number of sequences (0 = the workload's own: 256 / "
+                         "32); e.g. 1 for the batch-1 paging-overhead comparison with --pool")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the timed steps, run one device-to-device copy of this many MiB "
                          "(a plain copy of known size that calibrates the HBM byte counters)")
@@ -171,7 +175,10 @@ def main() -> int:
     if args.block_size != 16 and args.workload not in ("llama70b", "swap"):
         print(json.dumps({"error": "--block-size applies to the llama70b and swap workloads"}))
         return 2
-    w = make_workload(wl, args.workload, args.pool, args.block_size)
+    if args.batch and args.workload not in ("llama70b", "long32k"):
+        print(json.dumps({"error": "--batch applies to the llama70b and long32k workloads"}))
+        return 2
+    w = make_workload(wl, args.workload, args.pool, args.block_size, args.batch)
     t_setup = time.perf_counter()
     st = PagedState(w, dev, poison=True)
     torch.cuda.synchronize()
@@ -357,7 +364,7 @@ def run_decode(args, w, st, t_setup):
         step_bytes_avg = step_bytes_avg - logical_kv + uniq
     achieved = dec_bytes_avg / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes_avg / (ms_step * 1e-3) / 1e9
-    headline = args.workload == "llama70b"
+    headline = args.workload == "llama70b" and not args.batch
     cpu = None
     if args.cpu_seqs > 0 and headline:
         cpu = cpu_baseline(w, st, args.cpu_seqs, args.cpu_seconds)

@@ -153,6 +153,68 @@ __device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
   bool bad;
   (void)eff_len(a.ctx_lens[s], a.len_cap, bad);
   constexpr int C4 = D / 4;  // float4 chunks per head
+  const size_t row0 = (static_cast<size_t>(s) * a.Hq + kvh * a.G) * a.Pmax;  // head 0, partition 0
+  const int64_t o_bytes = static_cast<int64_t>(a.G) * a.Pmax * D * 4;
+  if (o_bytes < (int64_t(1) << 31)) {
+    // The partials are read with the device-scope cache bit an agent-scope atomic load carries
+    // (sc1), but as plain buffer loads: the compiler issued the atomic loads one at a time,
+    // each waiting for the previous, so a merge of many partitions became a serial tail
+    // (32,768 tokens at batch 1: 128 partitions per head).  Buffer loads stay in flight
+    // together, and an output chunk is one 16-byte load.
+    constexpr int kSc1 = 16;  // cache-policy bit sc1 (gfx940+ encoding)
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+        a.part_ml + row0, 0, static_cast<int>(static_cast<int64_t>(a.G) * a.Pmax * 8), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        a.part_o + row0 * D, 0, static_cast<int>(o_bytes), 0x00020000);
+    for (int c = threadIdx.x; c < a.G * C4; c += kNW * kWave) {
+      const int h = c / C4, d4 = c - h * C4;
+      const int hr = h * a.Pmax;  // partition 0 of head h inside the (sequence, kv-head) block
+      // groups of kGrp partitions: every load of a group is issued before any is used; the
+      // indices of a short last group are clamped to the last partition and skipped
+      constexpr int kGrp = 8;
+      float M = -INFINITY;
+      for (int p0 = 0; p0 < nparts; p0 += kGrp) {
+        float mv[kGrp];
+#pragma unroll
+        for (int k = 0; k < kGrp; ++k)
+          mv[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                rm, (hr + min(p0 + k, nparts - 1)) * 8, 0, kSc1));
+#pragma unroll
+        for (int k = 0; k < kGrp; ++k) M = fmaxf(M, mv[k]);  // a clamped repeat changes nothing
+      }
+      float L = 0.f;
+      float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p0 = 0; p0 < nparts; p0 += kGrp) {
+        decltype(__builtin_amdgcn_raw_buffer_load_b64(rm, 0, 0, 0)) mlv[kGrp];
+        u32x4 ov[kGrp];
+#pragma unroll
+        for (int k = 0; k < kGrp; ++k) {
+          const int r = hr + min(p0 + k, nparts - 1);
+          mlv[k] = __builtin_amdgcn_raw_buffer_load_b64(rm, r * 8, 0, kSc1);
+          ov[k] = __builtin_amdgcn_raw_buffer_load_b128(ro, (r * D + 4 * d4) * 4, 0, kSc1);
+        }
+#pragma unroll
+        for (int k = 0; k < kGrp; ++k) {  // partitions in index order
+          // a clamped repeat gets weight 0: fmaf(0, v, O) == O for finite v, and a row whose
+          // partials hold NaN is NaN anyway
+          const float wgt = p0 + k < nparts
+              ? __uint_as_float(mlv[k][1]) * exp2f(__uint_as_float(mlv[k][0]) - M) : 0.f;
+          L += wgt;
+          O.x = fmaf(wgt, __uint_as_float(ov[k][0]), O.x);
+          O.y = fmaf(wgt, __uint_as_float(ov[k][1]), O.y);
+          O.z = fmaf(wgt, __uint_as_float(ov[k][2]), O.z);
+          O.w = fmaf(wgt, __uint_as_float(ov[k][3]), O.w);
+        }
+      }
+      const float inv = bad ? NAN : 1.f / L;
+      T* op = static_cast<T*>(a.out) + (static_cast<size_t>(s) * a.Hq + kvh * a.G + h) * D + 4 * d4;
+      op[0] = Elem<T>::from_f32(O.x * inv);
+      op[1] = Elem<T>::from_f32(O.y * inv);
+      op[2] = Elem<T>::from_f32(O.z * inv);
+      op[3] = Elem<T>::from_f32(O.w * inv);
+    }
+    return;
+  }
   for (int c = threadIdx.x; c < a.G * C4; c += kNW * kWave) {
     const int h = c / C4, d4 = c - h * C4;
     const int hq = kvh * a.G + h;

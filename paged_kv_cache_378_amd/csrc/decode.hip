@@ -197,15 +197,15 @@ __device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
         }
 #pragma unroll
         for (int k = 0; k < kGrp; ++k) {  // partitions in index order
-          // a clamped repeat gets weight 0: fmaf(0, v, O) == O for finite v, and a row whose
-          // partials hold NaN is NaN anyway
-          const float wgt = p0 + k < nparts
-              ? __uint_as_float(mlv[k][1]) * exp2f(__uint_as_float(mlv[k][0]) - M) : 0.f;
-          L += wgt;
-          O.x = fmaf(wgt, __uint_as_float(ov[k][0]), O.x);
-          O.y = fmaf(wgt, __uint_as_float(ov[k][1]), O.y);
-          O.z = fmaf(wgt, __uint_as_float(ov[k][2]), O.z);
-          O.w = fmaf(wgt, __uint_as_float(ov[k][3]), O.w);
+          // a clamped repeat is dropped by selects (no branch, so the group's loads stay
+          // together; no 0 * Inf either)
+          const bool use = p0 + k < nparts;
+          const float wgt = __uint_as_float(mlv[k][1]) * exp2f(__uint_as_float(mlv[k][0]) - M);
+          L = use ? L + wgt : L;
+          O.x = use ? fmaf(wgt, __uint_as_float(ov[k][0]), O.x) : O.x;
+          O.y = use ? fmaf(wgt, __uint_as_float(ov[k][1]), O.y) : O.y;
+          O.z = use ? fmaf(wgt, __uint_as_float(ov[k][2]), O.z) : O.z;
+          O.w = use ? fmaf(wgt, __uint_as_float(ov[k][3]), O.w) : O.w;
         }
       }
       const float inv = bad ? NAN : 1.f / L;

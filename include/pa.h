@@ -246,9 +246,14 @@ typedef struct {
   double memory_reduction_factor;  /* naive / paged                  (unrounded) */
 } pa_accounting_t;
 
-/* Slot accounting of [KC] "Worked Example 1" for n request lengths (host arrays). */
-pa_status pa_accounting(const int32_t* lens, int32_t n, int32_t block_size, int32_t max_seq_len,
-                        pa_accounting_t* out);
+/* Slot accounting of n request lengths (host arrays), as [KC] "Worked Example 1" computes it for
+ * its four requests: the tokens held, the slots paged blocks of block_size reserve, the slots a
+ * contiguous reservation of max_seq_len per request reserves, both waste percentages and their
+ * ratio.  No manager state is read (the name groups it with the block-manager calls).
+ * PA_ERR_INVALID_ARG for n, block_size or max_seq_len <= 0, a negative length, or all lengths
+ * zero. */
+pa_status pa_bm_accounting(const int32_t* lens, int32_t n, int32_t block_size,
+                           int32_t max_seq_len, pa_accounting_t* out);
 
 /* Host check of a block table before upload: every entry a sequence uses (the first
  * ceil(ctx_len/B)) lies in [0, num_blocks), 1 <= ctx_len <= max_blocks * B.  PA_OK or

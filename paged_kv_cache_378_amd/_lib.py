@@ -107,7 +107,7 @@ _SIGS = {
     "pa_bm_cache_insert": ([_vp, _i64, _pi32, _i32, _pi32], _i32),
     "pa_bm_add_seq_cached": ([_vp, _i64, _pi32, _i32, _pi32, _pi32], _i32),
     "pa_bm_cache_evict": ([_vp, _i32, _pi32], _i32),
-    "pa_accounting": ([_pi32, _i32, _i32, _i32, C.POINTER(pa_accounting_t)], _i32),
+    "pa_bm_accounting": ([_pi32, _i32, _i32, _i32, C.POINTER(pa_accounting_t)], _i32),
     "pa_validate_tables": ([_pi32, _pi32, _i32, _i32, _i32, _i32], _i32),
     "pa_cache_write": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "pa_cache_append": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
@@ -271,10 +271,10 @@ def pa_bm_cache_evict(h, n_blocks: int) -> int:
     return n.value
 
 
-def pa_accounting(lens, block_size: int, max_seq_len: int) -> dict:
+def pa_bm_accounting(lens, block_size: int, max_seq_len: int) -> dict:
     a = _i32_host(lens)
     r = pa_accounting_t()
-    _check(_lib.pa_accounting(_ptr32(a), len(a), block_size, max_seq_len, C.byref(r)))
+    _check(_lib.pa_bm_accounting(_ptr32(a), len(a), block_size, max_seq_len, C.byref(r)))
     return {name: getattr(r, name) for name, _ in pa_accounting_t._fields_}
 
 

@@ -688,14 +688,14 @@ pa_status pa_bm_cache_evict(pa_bm* bm, int32_t n_blocks, int32_t* n_evicted_out)
   return ok();
 }
 
-pa_status pa_accounting(const int32_t* lens, int32_t n, int32_t block_size, int32_t max_seq_len,
-                        pa_accounting_t* out) {
-  if (!out || (n > 0 && !lens)) return fail(PA_ERR_INVALID_ARG, "pa_accounting: NULL argument");
+pa_status pa_bm_accounting(const int32_t* lens, int32_t n, int32_t block_size,
+                           int32_t max_seq_len, pa_accounting_t* out) {
+  if (!out || (n > 0 && !lens)) return fail(PA_ERR_INVALID_ARG, "pa_bm_accounting: NULL argument");
   if (n <= 0 || block_size <= 0 || max_seq_len <= 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_accounting: n, block_size and max_seq_len must be > 0");
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_accounting: n, block_size and max_seq_len must be > 0");
   int64_t actual = 0, blocks = 0;
   for (int32_t i = 0; i < n; ++i) {
-    if (lens[i] < 0) return fail(PA_ERR_INVALID_ARG, "pa_accounting: length %d < 0", lens[i]);
+    if (lens[i] < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_accounting: length %d < 0", lens[i]);
     actual += lens[i];
     blocks += (static_cast<int64_t>(lens[i]) + block_size - 1) / block_size;
   }
@@ -703,7 +703,7 @@ pa_status pa_accounting(const int32_t* lens, int32_t n, int32_t block_size, int3
   r.total_actual_tokens = actual;
   r.paged_slots = blocks * block_size;
   r.naive_slots = static_cast<int64_t>(max_seq_len) * n;
-  if (r.paged_slots == 0) return fail(PA_ERR_INVALID_ARG, "pa_accounting: all lengths are zero");
+  if (r.paged_slots == 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_accounting: all lengths are zero");
   r.paged_fragmentation_pct =
       100.0 * static_cast<double>(r.paged_slots - actual) / static_cast<double>(r.paged_slots);
   r.naive_fragmentation_pct =

@@ -13,4 +13,4 @@ std::string& last_error_slot() {
 
 extern "C" const char* pa_last_error(void) { return pa::last_error_slot().c_str(); }
 
-extern "C" int32_t pa_abi_version(void) { return 2; }
+extern "C" int32_t pa_abi_version(void) { return 3; }

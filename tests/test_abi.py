@@ -18,10 +18,13 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for must in ("pa_cache_write", "pa_decode", "pa_chunk_attend", "pa_bm_create",
-                 "pa_bm_append_slots", "pa_bm_fork", "pa_bm_free_seq", "pa_bm_block_tables",
-                 "pa_copy_blocks", "pa_bm_stats"):
-        assert must in names
+    # the boundary's calls: block manager (create/destroy, prefill, append, fork, free,
+    # tables, stats, reference counts, slot accounting), host table check, device calls
+    for must in ("pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots",
+                 "pa_bm_fork", "pa_bm_free_seq", "pa_bm_block_tables", "pa_bm_stats",
+                 "pa_bm_refcount", "pa_bm_accounting", "pa_validate_tables", "pa_cache_write",
+                 "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode", "pa_chunk_attend"):
+        assert must in names, must
 
 
 def test_library_exports_every_declared_symbol(libpa):
@@ -37,7 +40,7 @@ def test_library_exports_every_declared_symbol(libpa):
 
 
 def test_abi_version(libpa):
-    assert libpa.pa_abi_version() == 2
+    assert libpa.pa_abi_version() == 3
 
 
 def _raw(libpa):

@@ -131,11 +131,11 @@ def test_shared_prefix_cow_counts(libpa):
 
 def test_accounting_matches_pages(libpa):
     g = GOLD["worked_example_1"]
-    r = libpa.pa_accounting(g["seq_lengths"], g["block_size"], g["max_seq_len"])
+    r = libpa.pa_bm_accounting(g["seq_lengths"], g["block_size"], g["max_seq_len"])
     assert acc.rounded(r) == g["printed"]
     for key in ("answer_a2",):
         g = GOLD[key]
-        r = libpa.pa_accounting(g["seq_lengths"], g["block_size"], g["max_seq_len"])
+        r = libpa.pa_bm_accounting(g["seq_lengths"], g["block_size"], g["max_seq_len"])
         assert round(r["paged_fragmentation_pct"], 2) == g["paged_fragmentation_pct"]
         assert round(r["naive_fragmentation_pct"], 2) == g["naive_fragmentation_pct"]
         assert round(r["memory_reduction_factor"], 2) == g["memory_reduction_factor"]
@@ -144,7 +144,7 @@ def test_accounting_matches_pages(libpa):
         lens = rng.integers(0, 5000, size=int(rng.integers(1, 20)))
         lens[0] = max(lens[0], 1)
         B = int(rng.choice([1, 16, 32, 64]))
-        r = libpa.pa_accounting(lens, B, 8192)
+        r = libpa.pa_bm_accounting(lens, B, 8192)
         o = acc.paged_vs_naive(lens, B, 8192)
         assert r == o
 

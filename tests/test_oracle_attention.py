@@ -204,3 +204,84 @@ def test_bf16_bits_exact():
     t = torch.from_numpy(vals).to(torch.bfloat16)
     bits = t.view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(att.bf16_bits_to_f64(bits), t.to(torch.float64).numpy())
+
+
+# -- paged_chunk_attend: the chunk of new tokens read through block tables ---------------
+#
+# Pins that do not go through chunk_attend's own arithmetic: a hand-computed case on a
+# scattered pool, masked torch SDPA on the logical K/V, and bitwise invariance to relabelling
+# the physical blocks.  The chunk is appended with the block manager model after a prefill
+# that ends mid-block, so the chunk starts inside a shared-with-prefix block.
+
+def _paged_chunk_setup(rng, S, Hkv, D, B, NB, cached, C):
+    bm = BlockManagerModel(NB, B, free_order=rng.permutation(NB))
+    k = np.full((NB, Hkv, B, D), np.nan)
+    v = np.full((NB, Hkv, D, B), np.nan)
+    logical = []
+    for s in range(S):
+        K, V = rand(rng, cached[s] + C, Hkv, D), rand(rng, cached[s] + C, Hkv, D)
+        cache.write_kv(k, v, K[:cached[s]], V[:cached[s]], bm.add_seq(s, cached[s]), B)
+        logical.append((K, V))
+    slots, pairs = bm.append_slots(list(range(S)), C)
+    assert not pairs
+    for s in range(S):
+        K, V = logical[s]
+        cache.write_kv(k, v, K[cached[s]:], V[cached[s]:], slots[s * C:(s + 1) * C], B)
+    maxb = max((n + C + B - 1) // B for n in cached)
+    tables, ctx = bm.block_tables(range(S), maxb)
+    return k, v, np.array(tables), np.array(ctx), logical
+
+
+def test_paged_chunk_hand_case():
+    # One head, D = 1, scale 1, B = 2; the sequence's three tokens live in physical blocks 5
+    # and 2 of a NaN-filled pool.  Keys 0, ln 3, 0 and values 1, 2, 6: chunk row 0 (position
+    # 1) weighs keys 0..1 as 1 : 3, row 1 (position 2) weighs keys 0..2 as 1 : 3 : 1.
+    B, NB = 2, 8
+    k = np.full((NB, 1, B, 1), np.nan)
+    v = np.full((NB, 1, 1, B), np.nan)
+    keys, vals = [0.0, math.log(3.0), 0.0], [1.0, 2.0, 6.0]
+    for j, blk in enumerate([5, 5, 2]):
+        k[blk, 0, j % B, 0] = keys[j]
+        v[blk, 0, 0, j % B] = vals[j]
+    tables = np.array([[5, 2, -1]])
+    q = np.ones((1, 2, 1, 1))
+    got = att.paged_chunk_attend(q, k, v, tables, np.array([3]), B, 1.0)
+    assert np.allclose(got[0, :, 0, 0], [(1 + 3 * 2) / 4, (1 + 3 * 2 + 6) / 5], rtol=0, atol=1e-15)
+
+
+def test_paged_chunk_matches_masked_sdpa_on_logical_kv():
+    rng = np.random.default_rng(17)
+    S, Hq, Hkv, D, B, C = 3, 8, 2, 16, 16, 21
+    cached = [0, 37, 100]
+    k, v, tables, ctx, logical = _paged_chunk_setup(rng, S, Hkv, D, B, 64, cached, C)
+    assert list(ctx) == [n + C for n in cached]
+    q = rand(rng, S, C, Hq, D)
+    got = att.paged_chunk_attend(q, k, v, tables, ctx, B, 0.25)
+    assert np.isfinite(got).all()
+    g = Hq // Hkv
+    for s in range(S):
+        K, V = logical[s]
+        n = K.shape[0]
+        mask = torch.arange(n)[None, :] <= (cached[s] + torch.arange(C))[:, None]
+        qt = torch.from_numpy(q[s]).permute(1, 0, 2)
+        Kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(g, 0)
+        Vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(g, 0)
+        want = torch.nn.functional.scaled_dot_product_attention(
+            qt, Kt, Vt, attn_mask=mask, scale=0.25).permute(1, 0, 2).numpy()
+        assert np.max(np.abs(got[s] - want)) <= 1e-12
+        assert np.array_equal(got[s], att.chunk_attend(q[s], K, V, 0.25))
+
+
+def test_paged_chunk_layout_permutation_invariance_bitwise():
+    rng = np.random.default_rng(18)
+    S, Hq, Hkv, D, B, C, NB = 2, 4, 2, 8, 4, 9, 60
+    k, v, tables, ctx, _ = _paged_chunk_setup(rng, S, Hkv, D, B, NB, [13, 30], C)
+    q = rand(rng, S, C, Hq, D)
+    base = att.paged_chunk_attend(q, k, v, tables, ctx, B, 0.5)
+    pi = rng.permutation(NB)
+    k2 = np.empty_like(k)
+    v2 = np.empty_like(v)
+    k2[pi] = k
+    v2[pi] = v
+    t2 = np.where(tables >= 0, pi[np.maximum(tables, 0)], -1)
+    assert np.array_equal(att.paged_chunk_attend(q, k2, v2, t2, ctx, B, 0.5), base)

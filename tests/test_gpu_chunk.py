@@ -69,3 +69,35 @@ def test_chunk_layout_invariance_bitwise(gpu):
     _, a, _ = run(w)
     _, b, _ = run(w, free_order=np.arange(w.num_blocks, dtype=np.int32))
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# Contexts longer than the kernel's LDS window of 512 block-table entries: the window is moved
+# forward when a tile passes its end.  At B = 16 that happens past 8,192 keys, at B = 32 past
+# 16,384 and at B = 64 past 32,768; each case has rows whose keys lie on both sides of the move.
+WINDOW_CASES = {
+    "window_b16": lambda: wl.chunked(S=2, cached=9000, C=96, B=16, hq=32, hkv=4),
+    "window_b32": lambda: wl.chunked(S=1, cached=17000, C=64, B=32, hq=32, hkv=4),
+    "window_b64": lambda: wl.chunked(S=1, cached=32900, C=40, B=64, hq=16, hkv=2),
+}
+
+
+@pytest.mark.parametrize("name", list(WINDOW_CASES))
+def test_chunk_past_the_table_window(gpu, name):
+    from oracle import attention as att
+    w = WINDOW_CASES[name]()
+    B, C = w.block_size, w.step_tokens
+    assert max(w.ctx_lens()) > 512 * B
+    st, out, _ = run(w)
+    got = f64(out)
+    for i in range(w.num_seqs):
+        ks, vs = wl.logical_kv(w, w.step_ids[i], st.vals)
+        K = np.concatenate([f64(k) for k in ks])
+        V = np.concatenate([f64(v) for v in vs])
+        n = K.shape[0]
+        for r in (0, 1, C // 2, C - 2, C - 1):
+            vis = n - C + r + 1
+            want = att.dense_decode(f64(st.vals["q"][i, r]), K[:vis], V[:vis], w.scale)
+            check(got[i, r], want, "bf16", f"{name} seq {i} row {r} ({vis} keys)")
+    # the same chunk over physically consecutive blocks: bit-identical
+    _, b, _ = run(w, free_order=np.arange(w.num_blocks, dtype=np.int32))
+    assert torch.equal(out.view(torch.int16), b.view(torch.int16))

@@ -1,0 +1,242 @@
+"""GPU parity of two flows that reuse blocks already in the pool.
+
+* Rollback of speculative tokens ("Taming the Tail", "The Future: Speculative Decoding and
+  Beyond": rejected speculative tokens are discarded and their blocks go back to the pool).
+  Sequences speculate, are truncated with pa_bm_truncate (the kept last block partly filled and
+  still holding rejected K/V; in one case that block is shared with a fork), then append real
+  tokens (pa_copy_blocks for the copy-on-write pairs, then pa_cache_write) and decode.  The
+  decode must see the new tokens, never the rejected ones left in the kept blocks, and a fork's
+  view must stay what it was.
+* RadixAttention's prefill of the suffix only (KV-cache chapter, "RadixAttention": a request
+  whose prompt is cached prefills only the tokens past the point of divergence).  Requests are
+  admitted with pa_bm_add_seq_cached; only positions past the cached blocks are written, and
+  pa_chunk_attend runs over the cached prefix plus the new tokens.
+
+Every operation runs on the library and, in step, on the oracle's block-manager model and its
+numpy scatter: slots, copy pairs and tables must agree exactly, the pools must agree bit for
+bit, and the attention outputs must match the fp64 oracle on each sequence's logical K/V,
+which the test tracks row by row (truncation drops rows, a fork copies them).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as att
+from oracle import cache as ocache
+from oracle.block_manager import BlockManagerModel
+
+from parity import check, f64
+
+pytestmark = pytest.mark.gpu
+
+NAN_BITS = {"f32": (np.int32, torch.int32, 0x7FC00000), "bf16": (np.int16, torch.int16, 0x7FC0)}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+class Mirror:
+    """The library's block manager and pools next to the oracle's model and numpy pools."""
+
+    def __init__(self, NB, B, Hkv, D, dtype, seed):
+        from paged_kv_cache_378_amd import _lib
+        self.lib = _lib
+        self.B, self.Hkv, self.D, self.dtype = B, Hkv, D, dtype
+        order = np.random.default_rng(seed).permutation(NB).astype(np.int32)
+        self.bm = _lib.BlockManager(NB, B, order)
+        self.model = BlockManagerModel(NB, B, order)
+        npt, self.tt, nan = NAN_BITS[dtype]
+        dt = TORCH_DT[dtype]
+        self.kc = torch.empty((NB, Hkv, B, D), dtype=dt, device="cuda")
+        self.vc = torch.empty((NB, Hkv, D, B), dtype=dt, device="cuda")
+        self.kc.view(self.tt).fill_(nan)
+        self.vc.view(self.tt).fill_(nan)
+        self.k_or = np.full((NB, Hkv, B, D), nan, npt)
+        self.v_or = np.full((NB, Hkv, D, B), nan, npt)
+        self.gen = torch.Generator().manual_seed(seed)
+        self.rows = {}  # sequence -> (list of key rows, list of value rows), fp64 [Hkv, D]
+
+    def values(self, T):
+        dt = TORCH_DT[self.dtype]
+        k = torch.randn((T, self.Hkv, self.D), generator=self.gen).to(dt)
+        v = torch.randn((T, self.Hkv, self.D), generator=self.gen).to(dt)
+        return k, v
+
+    def store(self, k, v, slots, pairs):
+        """Copy-on-write pairs, then the scatter: on the device and on the oracle's pools."""
+        pairs = np.asarray(pairs, np.int32).reshape(-1, 2)
+        if len(pairs):
+            self.lib.pa_copy_blocks(self.kc, self.vc, torch.from_numpy(pairs).cuda())
+        sl = np.asarray(slots, np.int32)
+        self.lib.pa_cache_write(k.cuda(), v.cuda(), self.kc, self.vc, torch.from_numpy(sl).cuda())
+        ocache.copy_blocks(self.k_or, self.v_or, [tuple(p) for p in pairs])
+        ocache.write_kv(self.k_or, self.v_or, k.view(self.tt).numpy(), v.view(self.tt).numpy(),
+                        sl, self.B)
+
+    def add(self, sid, n):
+        slots = self.bm.add_seq(sid, n)
+        assert list(slots) == self.model.add_seq(sid, n)
+        k, v = self.values(n)
+        self.store(k, v, slots, [])
+        self.rows[sid] = (list(f64(k)), list(f64(v)))
+
+    def append(self, ids, each):
+        slots, pairs = self.bm.append_slots(ids, each)
+        ms, mp = self.model.append_slots(ids, each)
+        assert list(slots) == ms and [tuple(p) for p in pairs] == [tuple(p) for p in mp]
+        k, v = self.values(len(ids) * each)
+        self.store(k, v, slots, pairs)
+        kf, vf = f64(k), f64(v)
+        for j, sid in enumerate(ids):
+            self.rows[sid][0].extend(kf[j * each:(j + 1) * each])
+            self.rows[sid][1].extend(vf[j * each:(j + 1) * each])
+        return pairs
+
+    def fork(self, parent, child):
+        self.bm.fork(parent, child)
+        self.model.fork(parent, child)
+        self.rows[child] = (list(self.rows[parent][0]), list(self.rows[parent][1]))
+
+    def truncate(self, sid, n):
+        self.bm.truncate(sid, n)
+        self.model.truncate(sid, n)
+        self.rows[sid] = (self.rows[sid][0][:n], self.rows[sid][1][:n])
+
+    def tables(self, ids):
+        B = self.B
+        maxb = max(-(-len(self.rows[s][0]) // B) for s in ids)
+        t, l = self.bm.block_tables(ids, maxb)
+        mt, ml = self.model.block_tables(ids, maxb)
+        assert np.array_equal(t, np.array(mt, np.int32)) and list(l) == ml
+        return t, l
+
+    def check_pools(self):
+        torch.cuda.synchronize()
+        assert np.array_equal(self.kc.cpu().view(self.tt).numpy(), self.k_or)
+        assert np.array_equal(self.vc.cpu().view(self.tt).numpy(), self.v_or)
+
+    def logical(self, sid):
+        return np.stack(self.rows[sid][0]), np.stack(self.rows[sid][1])
+
+
+def decode_and_check(m, ids, Hq, what):
+    lib = m.lib
+    t, l = m.tables(ids)
+    for i, sid in enumerate(ids):
+        assert l[i] == len(m.rows[sid][0])
+    q = torch.randn((len(ids), Hq, m.D), generator=m.gen).to(TORCH_DT[m.dtype]).cuda()
+    out = torch.empty_like(q)
+    max_ctx = int(l.max())
+    ws = torch.empty(max(16, lib.pa_decode_workspace_size(len(ids), Hq, m.D, max_ctx, 0)),
+                     dtype=torch.uint8, device="cuda")
+    lib.pa_decode(out, q, m.kc, m.vc, torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(),
+                  max_ctx, m.D ** -0.5, 0, ws)
+    m.check_pools()
+    got, qf = f64(out), f64(q)
+    for i, sid in enumerate(ids):
+        K, V = m.logical(sid)
+        want = att.dense_decode(qf[i], K, V, m.D ** -0.5)
+        check(got[i], want, m.dtype, f"{what}: seq {sid} (n={K.shape[0]})")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 32, 8, 128), ("f32", 4, 4, 64)])
+def test_rollback_then_append_and_decode(gpu, dtype, Hq, Hkv, D):
+    print(f"[gpu] rollback {dtype} Hq/Hkv={Hq}/{Hkv} D={D}", flush=True)
+    B = 16
+    m = Mirror(NB=96, B=B, Hkv=Hkv, D=D, dtype=dtype, seed=31)
+    A, Bq, Cq, FA, FB = 0, 1, 2, 10, 11
+    m.add(A, 90)       # last block holds 80..89
+    m.add(Bq, 70)      # last block holds 64..69
+    m.add(Cq, 40)
+    m.fork(A, FA)      # FA shares A's partial last block
+    # speculation: 20 tokens each; A's first write copies the shared block (A gets the copy)
+    pairs = m.append([A, Bq, Cq], 20)
+    assert len(pairs) == 1
+    m.fork(Bq, FB)     # FB shares every block of B, speculative tokens included
+    decode_and_check(m, [A, Bq, Cq, FA, FB], Hq, "after speculation")
+    # verification rejects most of it
+    m.truncate(A, 95)  # kept block (private copy) holds 80..95; 95 is a rejected token
+    m.truncate(Bq, 72)  # kept block 64..79 is shared with FB; 72..79 rejected for B only
+    m.truncate(Cq, 48)  # a block boundary: the block of 48..59 goes back to the pool
+    decode_and_check(m, [A, Bq, Cq, FA, FB], Hq, "after rollback")
+    # real tokens: A overwrites its rejected slot in place; B copies the shared kept block;
+    # C starts a fresh block; FA and FB write into blocks no longer shared
+    pairs = m.append([A, Bq, Cq, FA, FB], 3)
+    assert len(pairs) == 1
+    decode_and_check(m, [A, Bq, Cq, FA, FB], Hq, "after the next append")
+    # a second round: roll back to one token and to exactly one block, then decode steps
+    m.truncate(FA, 1)
+    m.truncate(FB, 16)
+    for step in range(3):
+        m.append([A, Bq, Cq, FA, FB], 1)
+    decode_and_check(m, [A, Bq, Cq, FA, FB], Hq, "after a second rollback")
+
+
+@pytest.mark.parametrize("B", [16, 32])
+def test_radix_prefill_of_the_suffix_only(gpu, B):
+    print(f"[gpu] radix suffix prefill B={B}", flush=True)
+    Hq, Hkv, D, P = 64, 8, 128, 300
+    m = Mirror(NB=160, B=B, Hkv=Hkv, D=D, dtype="bf16", seed=47)
+    lib = m.lib
+    prompt = list(range(500, 500 + P))
+    pk, pv = m.values(P)  # the prompt's K/V: the same tokens give the same keys and values
+    suffix = {0: 25, 1: 40, 2: 40, 3: 40, 4: 7}
+    tokens = {r: prompt + [10 ** 5 + 1000 * r + i for i in range(n)] for r, n in suffix.items()}
+    scale = D ** -0.5
+
+    def admit(r):
+        toks = tokens[r]
+        slots, n_cached = m.bm.add_seq_cached(r, toks)
+        ms, mn = m.model.add_seq_cached(r, toks)
+        assert list(slots) == ms and n_cached == mn
+        sk, sv = m.values(suffix[r])
+        k, v = torch.cat([pk, sk]), torch.cat([pv, sv])
+        m.store(k[n_cached:], v[n_cached:], slots[n_cached:], [])
+        m.rows[r] = (list(f64(k)), list(f64(v)))
+        return n_cached
+
+    def prefill(reqs, C):
+        t, l = m.tables(reqs)
+        q = torch.randn((len(reqs), C, Hq, D), generator=m.gen).to(torch.bfloat16).cuda()
+        out = torch.empty_like(q)
+        lib.pa_chunk_attend(out, q, m.kc, m.vc, torch.from_numpy(t).cuda(),
+                            torch.from_numpy(l).cuda(), scale)
+        m.check_pools()
+        got, qf = f64(out), f64(q)
+        for i, r in enumerate(reqs):
+            K, V = m.logical(r)
+            check(got[i], att.chunk_attend(qf[i], K, V, scale), "bf16", f"request {r}")
+        return q, out
+
+    # request 0 finds nothing cached: a prefill of all its tokens, then its blocks are cached
+    assert admit(0) == 0
+    prefill([0], P + suffix[0])
+    m.bm.cache_insert(0, tokens[0])
+    m.model.cache_insert(0, tokens[0])
+    # requests 1-3 reuse the prompt's full blocks and prefill only the rest, in one call
+    cached = (P // B) * B
+    assert [admit(r) for r in (1, 2, 3)] == [cached] * 3
+    C = P - cached + suffix[1]
+    q, out_cached = prefill([1, 2, 3], C)
+    # request 4: a shorter suffix
+    assert admit(4) == cached
+    prefill([4], P - cached + suffix[4])
+    st = m.bm.stats()
+    assert st["cache_hit_blocks"] == 4 * (P // B)
+    # the first table entries of requests 1-4 are request 0's blocks
+    t, _ = m.tables([0, 1, 2, 3, 4])
+    assert (t[1:, :P // B] == t[0, :P // B]).all()
+    # the same three requests stored privately (every position written): bit-identical
+    mp = Mirror(NB=160, B=B, Hkv=Hkv, D=D, dtype="bf16", seed=48)
+    ids = [1, 2, 3]
+    for r in ids:
+        k, v = (torch.from_numpy(np.stack(x)).to(torch.bfloat16) for x in m.rows[r])
+        slots = mp.bm.add_seq(r, len(tokens[r]))
+        mp.model.add_seq(r, len(tokens[r]))
+        mp.store(k, v, slots, [])
+        mp.rows[r] = m.rows[r]
+    tp, lp = mp.tables(ids)
+    out_private = torch.empty_like(out_cached)
+    lib.pa_chunk_attend(out_private, q, mp.kc, mp.vc, torch.from_numpy(tp).cuda(),
+                        torch.from_numpy(lp).cuda(), scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out_cached.view(torch.int16), out_private.view(torch.int16))

@@ -362,6 +362,30 @@ pa_status pa_decode_step(void* out, const void* q, const void* key, const void* 
                          int32_t dtype, int32_t partition_tokens, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Bytes of device scratch pa_decode_step_noalloc holds on each GPU it runs on, in MiB. */
+#define PA_NOALLOC_SCRATCH_MIB 96
+
+/* pa_decode_step without the workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The decode's scratch (queue, work list, merge counters, partial results) is a file-scope
+ * device array of PA_NOALLOC_SCRATCH_MIB MiB inside the library; each GPU the library runs on
+ * holds its own copy until the process ends.  This call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine); the caller still owns every input and output.
+ * Arguments, results and errors are those of pa_decode_step, plus PA_ERR_WORKSPACE (before
+ * any device work) when the batch needs more scratch than the array holds -- the size
+ * pa_decode_workspace_size(S, Hq, D, max_ctx_len, partition_tokens) reports; e.g. 256
+ * sequences of 64 query heads, D = 128, fit up to max_ctx_len = 11,264 with automatic
+ * partitions.  Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents (each call initialises what it reads): calls that overlap on one GPU (two
+ * streams or two threads) race and must be serialised by the caller. */
+pa_status pa_decode_step_noalloc(void* out, const void* q, const void* key, const void* value,
+                                 void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                 int32_t* block_tables, int32_t* ctx_lens,
+                                 const int32_t* new_ctx_lens, int32_t S, int32_t Hq, int32_t Hkv,
+                                 int32_t D, int32_t B, int32_t num_blocks, int32_t max_blocks,
+                                 int32_t max_ctx_len, float scale, int32_t dtype,
+                                 int32_t partition_tokens, void* stream);
+
 /* Whole-block copies between the pools and host memory, for swapping a paused request's
  * KV-cache to CPU RAM and back ([TT] "Infrastructure Scale"; pa_bm_swap_out / pa_bm_swap_in
  * give the block lists).

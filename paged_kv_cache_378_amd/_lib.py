@@ -118,6 +118,8 @@ _SIGS = {
                    _f32, _i32, _i32, _vp, _sz, _vp], _i32),
     "pa_decode_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                         _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "pa_decode_step_noalloc": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp], _i32),
     "pa_swap_blocks": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "pa_chunk_attend": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _vp], _i32),
@@ -482,11 +484,10 @@ def _step_input(t, what: str):
     return t.data_ptr()
 
 
-def pa_decode_step(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
-                   max_ctx_len: int, scale: float, partition_tokens: int = 0, workspace=None,
-                   stream=None, new_ctx_lens=None) -> None:
-    """slot_mapping and new_ctx_lens may be device tensors or pinned host tensors; with
-    new_ctx_lens given, the step copies them into ctx_lens (a device tensor) before decoding."""
+def _step_args(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
+               new_ctx_lens):
+    """Checks and pointers shared by pa_decode_step and pa_decode_step_noalloc (every argument
+    up to partition_tokens, in the C order)."""
     torch = _torch()
     NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
     S, Hq, Dq = q.shape
@@ -501,16 +502,39 @@ def pa_decode_step(out, q, key, value, k_cache, v_cache, slot_mapping, block_tab
         raise PaError(PA_ERR_INVALID_ARG, "block_tables must be [S, max_blocks], ctx_lens [S]")
     if new_ctx_lens is not None and tuple(new_ctx_lens.shape) != (S,):
         raise PaError(PA_ERR_INVALID_ARG, "new_ctx_lens must be [S]")
+    new_ptr = None if new_ctx_lens is None else _step_input(new_ctx_lens, "new_ctx_lens")
+    return (_dev(out, "out"), _dev(q, "q"), _dev(key, "key"), _dev(value, "value"),
+            _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _step_input(slot_mapping, "slot_mapping"),
+            _dev(block_tables, "block_tables", torch.int32),
+            _dev(ctx_lens, "ctx_lens", torch.int32), new_ptr, S, Hq, Hkv, D, B, NB,
+            block_tables.shape[1])
+
+
+def pa_decode_step(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
+                   max_ctx_len: int, scale: float, partition_tokens: int = 0, workspace=None,
+                   stream=None, new_ctx_lens=None) -> None:
+    """slot_mapping and new_ctx_lens may be device tensors or pinned host tensors; with
+    new_ctx_lens given, the step copies them into ctx_lens (a device tensor) before decoding."""
+    args = _step_args(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
+                      new_ctx_lens)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (_dev(workspace, "workspace"),
                                                             workspace.numel() * workspace.element_size())
-    new_ptr = None if new_ctx_lens is None else _step_input(new_ctx_lens, "new_ctx_lens")
-    _check(_lib.pa_decode_step(_dev(out, "out"), _dev(q, "q"), _dev(key, "key"), _dev(value, "value"),
-                               _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                               _step_input(slot_mapping, "slot_mapping"),
-                               _dev(block_tables, "block_tables", torch.int32),
-                               _dev(ctx_lens, "ctx_lens", torch.int32), new_ptr, S, Hq, Hkv, D, B,
-                               NB, block_tables.shape[1], max_ctx_len, float(scale),
-                               _dtype_code(q), partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
+    _check(_lib.pa_decode_step(*args, max_ctx_len, float(scale), _dtype_code(q), partition_tokens,
+                               ws_ptr, ws_bytes, _stream(stream)))
+
+
+PA_NOALLOC_SCRATCH_BYTES = 96 << 20  # PA_NOALLOC_SCRATCH_MIB of include/pa.h
+
+
+def pa_decode_step_noalloc(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables,
+                           ctx_lens, max_ctx_len: int, scale: float, partition_tokens: int = 0,
+                           stream=None, new_ctx_lens=None) -> None:
+    """pa_decode_step on the library's static scratch (no workspace argument)."""
+    args = _step_args(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
+                      new_ctx_lens)
+    _check(_lib.pa_decode_step_noalloc(*args, max_ctx_len, float(scale), _dtype_code(q),
+                                       partition_tokens, _stream(stream)))
 
 
 def pa_swap_blocks(k_cache, v_cache, host, blocks, to_host: bool, stream=None) -> None:

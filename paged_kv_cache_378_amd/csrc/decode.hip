@@ -1179,3 +1179,76 @@ extern "C" pa_status pa_decode_step(void* out, const void* q, const void* key, c
   return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, &wr,
                   new_ctx_lens ? ctx_lens : nullptr);
 }
+
+// ---------------------------------------------------------------------------------------
+// pa_decode_step without a caller workspace, for callers that cannot allocate device memory
+// (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+// The decode's scratch -- queue header, work list, merge counters, partial results -- lives
+// in one file-scope device array of a fixed size; each GPU the library runs on holds its own
+// copy until the process ends.  The plan kernel initialises everything the decode reads from
+// it (the header, the list, and the merge counters when partitions are merged), so nothing
+// has to be cleared between calls.  Every call on one GPU uses the same array: calls that
+// overlap on one GPU (two streams, two threads) race on it.
+// ---------------------------------------------------------------------------------------
+namespace pa {
+constexpr size_t kNoAllocScratchBytes = size_t(PA_NOALLOC_SCRATCH_MIB) << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace pa
+
+static __device__ __align__(256) unsigned char scratch[pa::kNoAllocScratchBytes];
+
+namespace pa {
+
+// Device address of `scratch` on the current device, taken once per device with
+// hipGetSymbolAddress (in host code the array's name is only a host-side stand-in, never a
+// device address).  No allocation: a fixed table indexed by device.
+static pa_status noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_HIP, "pa_decode_step_noalloc: no current device below %d", kMaxDevices);
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_HIP, "pa_decode_step_noalloc: hipGetSymbolAddress(scratch) failed: %s",
+                  hipGetErrorString(e));
+    }
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return ok();
+}
+
+}  // namespace pa
+
+extern "C" pa_status pa_decode_step_noalloc(void* out, const void* q, const void* key,
+                                            const void* value, void* k_cache, void* v_cache,
+                                            const int32_t* slot_mapping, int32_t* block_tables,
+                                            int32_t* ctx_lens, const int32_t* new_ctx_lens,
+                                            int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                            int32_t B, int32_t num_blocks, int32_t max_blocks,
+                                            int32_t max_ctx_len, float scale, int32_t dtype,
+                                            int32_t partition_tokens, void* stream) {
+  // The scratch this call needs (the size pa_decode_workspace_size reports), checked against
+  // the array before any HIP call.
+  size_t need = 0;
+  if (pa_status st = pa_decode_workspace_size(S, Hq, D, max_ctx_len, partition_tokens, &need))
+    return st;
+  if (need > kNoAllocScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_decode_step_noalloc: this batch needs %zu bytes of scratch, the static scratch "
+                "holds %zu (PA_NOALLOC_SCRATCH_MIB); use pa_decode_step with a workspace",
+                need, kNoAllocScratchBytes);
+  if (S == 0) return ok();
+  void* ws = nullptr;
+  if (pa_status st = noalloc_scratch(&ws)) return st;
+  return pa_decode_step(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
+                        new_ctx_lens, S, Hq, Hkv, D, B, num_blocks, max_blocks, max_ctx_len, scale,
+                        dtype, partition_tokens, ws, kNoAllocScratchBytes, stream);
+}

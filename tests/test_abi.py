@@ -94,3 +94,19 @@ def test_workspace_size(libpa):
     assert libpa.pa_decode_workspace_size(4, 4, 64, 1000, 0) > 0        # automatic choice
     with pytest.raises(libpa.PaError):
         libpa.pa_decode_workspace_size(4, 4, 64, 100, 40)
+
+
+def test_noalloc_step_rejects_oversize_batches_before_any_device_call(libpa):
+    # The scratch check comes first, so this runs without a GPU (pointers never dereferenced).
+    lib = _raw(libpa)
+    fake = C.c_void_p(0x1000)
+    S, Hq, D, max_ctx = 2048, 64, 128, 8192
+    assert libpa.pa_decode_workspace_size(S, Hq, D, max_ctx, 0) > libpa.PA_NOALLOC_SCRATCH_BYTES
+    st = lib.pa_decode_step_noalloc(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, S,
+                                    Hq, 8, D, 16, 1 << 20, max_ctx // 16, max_ctx, 0.1,
+                                    libpa.PA_DTYPE_BF16, 0, None)
+    assert st == libpa.PA_ERR_WORKSPACE and b"static scratch" in lib.pa_last_error()
+    # the binding's constant is the header's
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    mib = int(re.search(r"#define PA_NOALLOC_SCRATCH_MIB (\d+)", text).group(1))
+    assert libpa.PA_NOALLOC_SCRATCH_BYTES == mib << 20

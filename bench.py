@@ -7,8 +7,8 @@ head_dim 128, bf16, block size 16, log-normal context lengths (median 1,024, cli
 values (N(0,1) rounded to bf16).
 
 One step = the whole hot path for one batch:
-  host  : pa_bm_append_slots (one token per sequence, copy-on-write decisions) and
-          pa_bm_seq_lens into pinned host buffers (2 KB);
+  host  : pa_bm_append_step (one token per sequence: slots, copy-on-write decisions and the
+          new lengths in one pass) into pinned host buffers (2 KB);
   device: pa_copy_blocks (if any pairs) -> pa_decode_step: one launch that reads the pinned
           slots and lengths directly and does the cache write + the block-table entries the
           step created (on the device-resident tables) together with the decode planning,
@@ -297,6 +297,11 @@ def run_decode(args, w, st, t_setup):
     RING, MARK = 16, 8
     pin_slots = [torch.empty(S, dtype=torch.int32).pin_memory() for _ in range(RING)]
     pin_lens = [torch.empty(S, dtype=torch.int32).pin_memory() for _ in range(RING)]
+    pairs_h = np.empty((S, 2), np.int32)
+    # the host half of the step: one pa_bm_append_step call (slots, copy-on-write pairs and the
+    # new lengths in one pass) straight into the pinned buffers, its arguments marshalled once
+    append_step = st.bm.prepare_append_step(ids, 1, [t.numpy() for t in pin_slots],
+                                            [t.numpy() for t in pin_lens], pairs_h)
     marks = [torch.cuda.Event() for _ in range(4)]
     stream = torch.cuda.current_stream()
     host_s, step_lens, n_pairs = [], [], []
@@ -309,15 +314,13 @@ def run_decode(args, w, st, t_setup):
             marks[((i - RING) // MARK) % len(marks)].synchronize()
         slots_h, lens_h = pin_slots[r], pin_lens[r]
         h0 = time.perf_counter()
-        slots, pairs = st.bm.append_slots(ids, 1)
-        slots_h.numpy()[:] = slots
-        st.bm.seq_lens(ids, lens_h.numpy())
-        n_pairs.append(len(pairs))
+        np_ = append_step(r)
         if timed:
             host_s.append(time.perf_counter() - h0)
             step_lens.append(lens_h.numpy().copy())
-        if len(pairs):
-            _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs).to(dev))
+        n_pairs.append(np_)
+        if np_:
+            _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs_h[:np_]).to(dev))
         _lib.pa_decode_step(out, st.vals["q"], st.vals["k_step"], st.vals["v_step"], st.k_cache,
                             st.v_cache, slots_h, tables_d, lens_d, max_ctx, w.scale,
                             args.partition, ws, new_ctx_lens=lens_h)

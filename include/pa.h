@@ -142,6 +142,16 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
                              int32_t tokens_each, int32_t* slots_out, int32_t* copy_pairs_out,
                              int32_t pairs_cap, int32_t* n_copies_out);
 
+/* pa_bm_append_slots that also writes lens_out[i] (host array of n_seqs ints), the length of
+ * seq_ids[i] after the call, in the same pass: the host half of one serving step (slots,
+ * copy-on-write pairs and the new context lengths) in one call.  The host cost of block
+ * management is one of the overheads [VP] "3. Production Failure Modes" says to watch; once
+ * the handle's scratch has grown to the batch size, a step allocates no host memory.  Errors
+ * and failure atomicity as pa_bm_append_slots (lens_out is not written on error). */
+pa_status pa_bm_append_step(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
+                            int32_t tokens_each, int32_t* slots_out, int32_t* lens_out,
+                            int32_t* copy_pairs_out, int32_t pairs_cap, int32_t* n_copies_out);
+
 /* Zero-copy fork ([VP] "Zero-Copy Forking & Parallel Sampling"): child receives the parent's
  * table and length; every block's count goes up by one.  No device work. */
 pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id);

@@ -93,6 +93,7 @@ _SIGS = {
     "pa_bm_destroy": ([_vp], _i32),
     "pa_bm_add_seq": ([_vp, _i64, _i32, _pi32], _i32),
     "pa_bm_append_slots": ([_vp, _pi64, _i32, _i32, _pi32, _pi32, _i32, _pi32], _i32),
+    "pa_bm_append_step": ([_vp, _pi64, _i32, _i32, _pi32, _pi32, _pi32, _i32, _pi32], _i32),
     "pa_bm_fork": ([_vp, _i64, _i64], _i32),
     "pa_bm_free_seq": ([_vp, _i64], _i32),
     "pa_bm_block_tables": ([_vp, _pi64, _i32, _i32, _pi32, _pi32], _i32),
@@ -179,6 +180,55 @@ def pa_bm_append_slots(h, seq_ids, tokens_each: int, pairs_cap: int | None = Non
     _check(_lib.pa_bm_append_slots(h, ids.ctypes.data_as(_pi64), len(ids), tokens_each,
                                    _ptr32(slots), _ptr32(pairs), cap, C.byref(n)))
     return slots, pairs[: n.value].copy()
+
+
+def pa_bm_append_step(h, seq_ids, tokens_each: int, slots_out=None, lens_out=None,
+                      pairs_out=None):
+    """(slots, lengths after the step, copy pairs).  seq_ids must be a contiguous int64 array;
+    the optional output arrays (int32, C-contiguous; pairs_out [cap, 2]) are filled in place,
+    so a serving loop can hand in pinned buffers and reuse them."""
+    ids = seq_ids if isinstance(seq_ids, np.ndarray) and seq_ids.dtype == np.int64 and \
+        seq_ids.flags.c_contiguous else np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+    n = len(ids)
+    slots = np.empty(n * tokens_each, np.int32) if slots_out is None else slots_out
+    lens = np.empty(n, np.int32) if lens_out is None else lens_out
+    pairs = np.empty((max(n, 1), 2), np.int32) if pairs_out is None else pairs_out
+    assert slots.dtype == np.int32 and slots.flags.c_contiguous and slots.size >= n * tokens_each
+    assert lens.dtype == np.int32 and lens.flags.c_contiguous and lens.size >= n
+    assert pairs.dtype == np.int32 and pairs.flags.c_contiguous and pairs.ndim == 2
+    nc = _i32()
+    _check(_lib.pa_bm_append_step(h, ids.ctypes.data_as(_pi64), n, tokens_each, _ptr32(slots),
+                                  _ptr32(lens), _ptr32(pairs), pairs.shape[0], C.byref(nc)))
+    return slots, lens, pairs[:nc.value]
+
+
+class PreparedAppendStep:
+    """pa_bm_append_step with its arguments marshalled once, for a serving loop that appends to
+    the same batch every step: the batch ids and a ring of output buffers (int32 numpy arrays,
+    e.g. views of pinned host memory the device reads) are fixed, so a call passes only the
+    ring index.  call(r) fills slots_bufs[r], lens_bufs[r] and pairs_buf and returns the number
+    of copy-on-write pairs (the first rows of pairs_buf)."""
+
+    def __init__(self, h, seq_ids, tokens_each: int, slots_bufs, lens_bufs, pairs_buf):
+        self._keep = (np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64)), list(slots_bufs),
+                      list(lens_bufs), pairs_buf)
+        ids = self._keep[0]
+        n = len(ids)
+        for sb, lb in zip(slots_bufs, lens_bufs):
+            assert sb.dtype == np.int32 and sb.flags.c_contiguous and sb.size >= n * tokens_each
+            assert lb.dtype == np.int32 and lb.flags.c_contiguous and lb.size >= n
+        assert pairs_buf.dtype == np.int32 and pairs_buf.flags.c_contiguous and pairs_buf.ndim == 2
+        self._nc = _i32()
+        pids, pp, nref = ids.ctypes.data_as(_pi64), _ptr32(pairs_buf), C.byref(self._nc)
+        self._args = [(h, pids, n, tokens_each, _ptr32(sb), _ptr32(lb), pp, pairs_buf.shape[0], nref)
+                      for sb, lb in zip(slots_bufs, lens_bufs)]
+        self._fn = _lib.pa_bm_append_step
+
+    def __call__(self, r: int) -> int:
+        st = self._fn(*self._args[r])
+        if st != PA_OK:
+            _check(st)
+        return self._nc.value
 
 
 def pa_bm_fork(h, parent: int, child: int) -> None:
@@ -306,6 +356,12 @@ class BlockManager:
 
     def append_slots(self, seq_ids, tokens_each, pairs_cap=None):
         return pa_bm_append_slots(self.h, seq_ids, tokens_each, pairs_cap)
+
+    def append_step(self, seq_ids, tokens_each, slots_out=None, lens_out=None, pairs_out=None):
+        return pa_bm_append_step(self.h, seq_ids, tokens_each, slots_out, lens_out, pairs_out)
+
+    def prepare_append_step(self, seq_ids, tokens_each, slots_bufs, lens_bufs, pairs_buf):
+        return PreparedAppendStep(self.h, seq_ids, tokens_each, slots_bufs, lens_bufs, pairs_buf)
 
     def fork(self, parent, child):
         pa_bm_fork(self.h, parent, child)

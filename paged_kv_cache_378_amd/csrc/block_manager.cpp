@@ -34,6 +34,7 @@ namespace {
 struct Seq {
   std::vector<int32_t> blocks;  // physical ids in logical order
   int32_t n = 0;                // tokens held
+  uint64_t stamp = 0;           // the append call that last named it (repeat detection)
 };
 
 // Prefix-cache tree node: one full block of B tokens, keyed by those token ids under its
@@ -73,6 +74,19 @@ struct pa_bm {
   std::priority_queue<std::pair<int64_t, int64_t>, std::vector<std::pair<int64_t, int64_t>>,
                       std::greater<std::pair<int64_t, int64_t>>> cand;
   int64_t tick = 0;
+  // Per-call scratch of the append calls, kept so a decode step allocates nothing once the
+  // vectors have grown to the batch size.
+  uint64_t epoch = 0;
+  std::vector<Seq*> batch;
+  // The ids `batch` was resolved from, valid while no sequence has been erased since (erasing
+  // is the only way an element's address in `seqs` changes): a serving loop names the same
+  // batch step after step, and then no id is looked up again.
+  std::vector<int64_t> batch_ids;
+  bool batch_valid = false;
+  uint64_t seq_erasures = 0;
+  uint64_t batch_erasures = 0;
+  std::vector<char> cow;
+  std::unordered_map<int32_t, int32_t> dec;  // shared block -> copies already made from it
   int32_t cached = 0;                     // live nodes
   int64_t cache_hit_blocks = 0;
   int64_t cache_evictions = 0;
@@ -155,6 +169,8 @@ struct pa_bm {
       offer(node_of_block[b]);  // now held by the tree alone?
     }
   }
+  // n % B, by a mask when B is a power of two (the usual 16, 32, 64).
+  int32_t offset_of(int32_t n) const { return (B & (B - 1)) == 0 ? (n & (B - 1)) : n % B; }
   // New blocks a sequence of n tokens needs to grow by k tokens (block boundaries crossed).
   bool is_swapped(int64_t id) const { return swapped.count(id) != 0; }
   int64_t boundary_blocks(int32_t n, int32_t k) const {
@@ -241,100 +257,149 @@ pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id, int32_t n_tokens, int32_t* sl
   return ok();
 }
 
-pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
-                             int32_t tokens_each, int32_t* slots_out, int32_t* copy_pairs_out,
-                             int32_t pairs_cap, int32_t* n_copies_out) {
-  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: NULL handle");
+}  // extern "C"
+
+namespace {
+
+// One append call: tokens_each tokens for each of n_seqs sequences, in batch order; slots,
+// copy-on-write pairs and (lens_out != nullptr) the lengths after the call.  Resolves every id
+// and counts blocks and copies in a dry run first, so a failing call changes nothing.
+pa_status append_batch(pa_bm* bm, const char* who, const int64_t* seq_ids, int32_t n_seqs,
+                       int32_t tokens_each, int32_t* slots_out, int32_t* lens_out,
+                       int32_t* copy_pairs_out, int32_t pairs_cap, int32_t* n_copies_out) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "%s: NULL handle", who);
   if (n_seqs < 0 || tokens_each < 0 || pairs_cap < 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: negative count");
-  if (n_seqs > 0 && !seq_ids) return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: seq_ids NULL");
+    return fail(PA_ERR_INVALID_ARG, "%s: negative count", who);
+  if (n_seqs > 0 && !seq_ids) return fail(PA_ERR_INVALID_ARG, "%s: seq_ids NULL", who);
   if (n_seqs > 0 && tokens_each > 0 && !slots_out)
-    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: slots_out NULL");
+    return fail(PA_ERR_INVALID_ARG, "%s: slots_out NULL", who);
   if (pairs_cap > 0 && !copy_pairs_out)
-    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: copy_pairs_out NULL");
+    return fail(PA_ERR_INVALID_ARG, "%s: copy_pairs_out NULL", who);
   if (n_copies_out) *n_copies_out = 0;
   const int32_t B = bm->B;
 
-  // Dry run: resolve ids, reject repeats, count blocks and copies in batch order.
-  std::vector<Seq*> batch(n_seqs);
-  std::vector<char> cow(n_seqs, 0);
+  // Dry run: resolve ids (or reuse the last call's resolution of the same ids), reject repeats
+  // (a sequence named twice carries this call's stamp), count new blocks and copies in batch
+  // order.  Only a shared last block can be copied, so only shared blocks are tracked.
   int64_t need = 0, copies = 0;
   try {
-    std::unordered_set<int64_t> seen;
-    seen.reserve(static_cast<size_t>(n_seqs) * 2);
-    std::unordered_map<int32_t, int32_t> dec;  // block -> copies already made from it
-    for (int32_t i = 0; i < n_seqs; ++i) {
-      auto it = bm->seqs.find(seq_ids[i]);
-      if (it == bm->seqs.end())
-        return bm->is_swapped(seq_ids[i])
-                   ? fail(PA_ERR_SWAPPED, "pa_bm_append_slots: sequence %lld is swapped out",
-                          (long long)seq_ids[i])
-                   : fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_append_slots: unknown sequence %lld",
-                          (long long)seq_ids[i]);
-      if (!seen.insert(seq_ids[i]).second)
-        return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: sequence %lld repeats in the batch",
-                    (long long)seq_ids[i]);
-      Seq* s = &it->second;
-      batch[i] = s;
-      if (tokens_each == 0) continue;
-      if (s->n % B != 0) {
+    const bool same = bm->batch_valid && bm->batch_erasures == bm->seq_erasures &&
+                      bm->batch_ids.size() == static_cast<size_t>(n_seqs) &&
+                      (n_seqs == 0 || std::memcmp(bm->batch_ids.data(), seq_ids,
+                                                  sizeof(int64_t) * n_seqs) == 0);
+    if (!same) {
+      bm->batch_valid = false;
+      bm->batch.resize(static_cast<size_t>(n_seqs));
+      const uint64_t stamp = ++bm->epoch;
+      for (int32_t i = 0; i < n_seqs; ++i) {
+        auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end())
+          return bm->is_swapped(seq_ids[i])
+                     ? fail(PA_ERR_SWAPPED, "%s: sequence %lld is swapped out", who,
+                            (long long)seq_ids[i])
+                     : fail(PA_ERR_UNKNOWN_SEQ, "%s: unknown sequence %lld", who,
+                            (long long)seq_ids[i]);
+        Seq* s = &it->second;
+        if (s->stamp == stamp)
+          return fail(PA_ERR_INVALID_ARG, "%s: sequence %lld repeats in the batch", who,
+                      (long long)seq_ids[i]);
+        s->stamp = stamp;
+        bm->batch[i] = s;
+      }
+      bm->batch_ids.assign(seq_ids, seq_ids + n_seqs);
+      bm->batch_erasures = bm->seq_erasures;
+      bm->batch_valid = true;
+    }
+    bm->cow.assign(static_cast<size_t>(n_seqs), 0);
+    bm->dec.clear();
+    for (int32_t i = 0; i < n_seqs && tokens_each > 0; ++i) {
+      Seq* s = bm->batch[i];
+      const int32_t off = bm->offset_of(s->n);
+      if (off != 0) {
         const int32_t last = s->blocks.back();
-        int32_t& d = dec[last];
-        if (bm->ref[last] - d > 1) {
-          cow[i] = 1;
-          ++d;
-          ++copies;
-          ++need;
+        if (bm->ref[last] > 1) {
+          int32_t& d = bm->dec[last];
+          if (bm->ref[last] - d > 1) {
+            bm->cow[i] = 1;
+            ++d;
+            ++copies;
+            ++need;
+          }
         }
       }
       if (static_cast<int64_t>(s->n) + tokens_each > INT32_MAX)
-        return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: sequence length overflows int32");
-      const int64_t grow = bm->boundary_blocks(s->n, tokens_each);
+        return fail(PA_ERR_INVALID_ARG, "%s: sequence length overflows int32", who);
+      const int64_t grow = tokens_each == 1 ? (off == 0) : bm->boundary_blocks(s->n, tokens_each);
       need += grow;
-      // Capacity now, so the commit below cannot throw half-way.
-      s->blocks.reserve(s->blocks.size() + static_cast<size_t>(grow));
+      // Capacity now (growing geometrically), so the commit below cannot throw half-way.
+      const size_t want = s->blocks.size() + static_cast<size_t>(grow);
+      if (s->blocks.capacity() < want) s->blocks.reserve(std::max(want, 2 * s->blocks.capacity()));
     }
   } catch (...) {
-    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: out of host memory");
+    bm->batch_valid = false;
+    return fail(PA_ERR_INVALID_ARG, "%s: out of host memory", who);
   }
   if (copies > pairs_cap)
-    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: %lld copy pairs needed, capacity %d",
+    return fail(PA_ERR_INVALID_ARG, "%s: %lld copy pairs needed, capacity %d", who,
                 (long long)copies, pairs_cap);
   if (!bm->make_room(need))
-    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_bm_append_slots: needs %lld blocks, %d free",
-                (long long)need, bm->nfree);
+    return fail(PA_ERR_OUT_OF_BLOCKS, "%s: needs %lld blocks, %d free", who, (long long)need,
+                bm->nfree);
 
-  // Commit.
+  // Commit.  The dry run reserved every table it grows; only the eviction heap (a block of
+  // the prefix cache left referenced by the tree alone) can still allocate.
+  int32_t np = 0;
+  int64_t o = 0;
   try {
-    int32_t np = 0;
-    int64_t o = 0;
     for (int32_t i = 0; i < n_seqs; ++i) {
-      Seq* s = batch[i];
-      if (tokens_each == 0) continue;
-      if (cow[i]) {
-        const int32_t last = s->blocks.back();
-        const int32_t fresh = bm->take();
-        --bm->ref[last];  // stays >= 1: the dry run saw a count above one
-        if (bm->ref[last] == 1) bm->offer(bm->node_of_block[last]);
-        s->blocks.back() = fresh;
-        copy_pairs_out[2 * np] = last;
-        copy_pairs_out[2 * np + 1] = fresh;
-        ++np;
-        ++bm->cow_copies;
+      Seq* s = bm->batch[i];
+      if (tokens_each > 0) {
+        if (bm->cow[i]) {
+          const int32_t last = s->blocks.back();
+          const int32_t fresh = bm->take();
+          --bm->ref[last];  // stays >= 1: the dry run saw a count above one
+          if (bm->ref[last] == 1) bm->offer(bm->node_of_block[last]);
+          s->blocks.back() = fresh;
+          copy_pairs_out[2 * np] = last;
+          copy_pairs_out[2 * np + 1] = fresh;
+          ++np;
+          ++bm->cow_copies;
+        }
+        // position n sits in the last block at offset n % B (a new block when that is 0)
+        int32_t off = bm->offset_of(s->n);
+        for (int32_t t = 0; t < tokens_each; ++t) {
+          if (off == 0) s->blocks.push_back(bm->take());
+          slots_out[o++] = s->blocks.back() * B + off;
+          off = off + 1 == B ? 0 : off + 1;
+        }
+        s->n += tokens_each;
       }
-      for (int32_t t = 0; t < tokens_each; ++t) {
-        const int32_t pos = s->n;
-        if (pos % B == 0) s->blocks.push_back(bm->take());
-        slots_out[o++] = s->blocks[pos / B] * B + pos % B;
-        s->n = pos + 1;
-      }
+      if (lens_out) lens_out[i] = s->n;
     }
-    if (n_copies_out) *n_copies_out = np;
   } catch (...) {
-    // Unreachable: the dry run reserved every vector the commit grows.
-    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slots: out of host memory during commit");
+    return fail(PA_ERR_INVALID_ARG, "%s: out of host memory during commit", who);
   }
+  if (n_copies_out) *n_copies_out = np;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
+                             int32_t tokens_each, int32_t* slots_out, int32_t* copy_pairs_out,
+                             int32_t pairs_cap, int32_t* n_copies_out) {
+  return append_batch(bm, "pa_bm_append_slots", seq_ids, n_seqs, tokens_each, slots_out, nullptr,
+                      copy_pairs_out, pairs_cap, n_copies_out);
+}
+
+pa_status pa_bm_append_step(pa_bm* bm, const int64_t* seq_ids, int32_t n_seqs,
+                            int32_t tokens_each, int32_t* slots_out, int32_t* lens_out,
+                            int32_t* copy_pairs_out, int32_t pairs_cap, int32_t* n_copies_out) {
+  if (n_seqs > 0 && !lens_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_append_step: lens_out NULL");
+  return append_batch(bm, "pa_bm_append_step", seq_ids, n_seqs, tokens_each, slots_out, lens_out,
+                      copy_pairs_out, pairs_cap, n_copies_out);
 }
 
 pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
@@ -366,6 +431,7 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
   }
   for (int32_t b : it->second.blocks) bm->release(b);
   bm->seqs.erase(it);
+  ++bm->seq_erasures;
   return ok();
 }
 
@@ -508,6 +574,7 @@ pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq_id, int32_t* blocks_out, int32_t
   for (int32_t i = 0; i < k; ++i) blocks_out[i] = blocks[i];
   for (int32_t b : blocks) bm->release(b);
   bm->seqs.erase(it);
+  ++bm->seq_erasures;
   ++bm->swap_outs;
   return ok();
 }

@@ -219,3 +219,115 @@ def test_seq_lens_errors(libpa):
     assert list(bm.seq_lens([])) == []
     with pytest.raises(libpa.UnknownSeq):
         bm.seq_lens([5, 6])
+
+
+def test_append_step_bit_exact_with_repeated_batches(libpa):
+    # pa_bm_append_step = append_slots + the lengths after the call, in one pass.  Serving loops
+    # name the same batch step after step (the library then reuses its resolution of the ids);
+    # frees, swap-outs, re-admissions under an old id, forks and truncations in between must
+    # all be seen exactly as the model sees them.
+    rng = random.Random(99)
+    for B in (1, 16, 32):
+        NB = 160
+        order = rng.sample(range(NB), NB)
+        lib_bm = libpa.BlockManager(NB, B, order)
+        model = BlockManagerModel(NB, B, order)
+        next_id = 0
+        batch = []
+        for step in range(1200):
+            live = sorted(model.seqs)
+            op = rng.random()
+            if op < 0.1 or not live:
+                sid = rng.choice([next_id, *(s for s in batch if s not in model.seqs
+                                             and s not in model.swapped)])
+                n = rng.randrange(0, 2 * B + 3)
+                try:
+                    want = model.add_seq(sid, n)
+                except ModelOOB:
+                    with pytest.raises(libpa.OutOfBlocks):
+                        lib_bm.add_seq(sid, n)
+                else:
+                    assert list(lib_bm.add_seq(sid, n)) == want
+                next_id = max(next_id, sid + 1)
+            elif op < 0.16:
+                p = rng.choice(live)
+                model.fork(p, next_id)
+                lib_bm.fork(p, next_id)
+                next_id += 1
+            elif op < 0.22:
+                s = rng.choice(live)
+                model.free_seq(s)
+                lib_bm.free_seq(s)
+            elif op < 0.26:
+                s = rng.choice(live)
+                model.swap_out(s)
+                lib_bm.swap_out(s)
+            elif op < 0.30 and model.swapped:
+                s = rng.choice(sorted(model.swapped))
+                try:
+                    model.swap_in(s)
+                except ModelOOB:
+                    with pytest.raises(libpa.OutOfBlocks):
+                        lib_bm.swap_in(s)
+                else:
+                    lib_bm.swap_in(s)
+            elif op < 0.34:
+                s = rng.choice(live)
+                k = rng.randint(0, model.seq_len(s))
+                model.truncate(s, k)
+                lib_bm.truncate(s, k)
+            else:
+                if not batch or rng.random() < 0.15:
+                    batch = rng.sample(live, rng.randint(1, len(live)))
+                k = rng.choice([1, 1, 1, 0, 2, B + 1])
+                gone = [s for s in batch if s not in model.seqs]
+                if gone:
+                    err = libpa.Swapped if gone[0] in model.swapped else libpa.UnknownSeq
+                    with pytest.raises(err):
+                        lib_bm.append_step(batch, k)
+                    continue
+                try:
+                    want_slots, want_pairs = model.append_slots(batch, k)
+                except ModelOOB:
+                    with pytest.raises(libpa.OutOfBlocks):
+                        lib_bm.append_step(batch, k)
+                else:
+                    slots, lens, pairs = lib_bm.append_step(batch, k)
+                    assert list(slots) == want_slots
+                    assert [tuple(p) for p in pairs] == want_pairs
+                    assert list(lens) == [model.seq_len(s) for s in batch]
+            if step % 100 == 0:
+                same_state(lib_bm, model, sorted(model.seqs))
+        same_state(lib_bm, model, sorted(model.seqs))
+
+
+def test_append_step_batch_reuse_edge_cases(libpa):
+    bm = libpa.BlockManager(64, 4)
+    model = BlockManagerModel(64, 4)
+    for s in (1, 2, 3):
+        assert list(bm.add_seq(s, 5)) == model.add_seq(s, 5)
+    for _ in range(3):  # the same batch: resolved once, reused
+        slots, lens, _ = bm.append_step([1, 2, 3], 1)
+        assert list(slots) == model.append_slots([1, 2, 3], 1)[0]
+    # a freed member: refused, nothing changes
+    bm.free_seq(2)
+    model.free_seq(2)
+    with pytest.raises(libpa.UnknownSeq):
+        bm.append_step([1, 2, 3], 1)
+    same_state(bm, model, [1, 3])
+    # re-admitted under the same id: the new sequence is the one appended to
+    assert list(bm.add_seq(2, 9)) == model.add_seq(2, 9)
+    slots, lens, _ = bm.append_step([1, 2, 3], 1)
+    assert list(slots) == model.append_slots([1, 2, 3], 1)[0]
+    assert list(lens) == [model.seq_len(s) for s in (1, 2, 3)]
+    # a repeat inside the batch is refused even right after the batch was resolved
+    with pytest.raises(libpa.PaError):
+        bm.append_step([1, 1, 3], 1)
+    slots, _, _ = bm.append_step([1, 2, 3], 1)
+    assert list(slots) == model.append_slots([1, 2, 3], 1)[0]
+    # swapped out: refused as swapped
+    bm.swap_out(3)
+    model.swap_out(3)
+    with pytest.raises(libpa.Swapped):
+        bm.append_step([1, 2, 3], 1)
+    same_state(bm, model, [1, 2])

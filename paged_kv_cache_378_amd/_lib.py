@@ -19,6 +19,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
+# Test hook: PA_HOST_LIB names a host-only build of the block manager (the sanitizer build of
+# build_san.py); only the host entry points are bound then, and the device ones raise.
+HOST_ONLY = bool(os.environ.get("PA_HOST_LIB"))
+if HOST_ONLY:
+    LIB_PATH = os.environ["PA_HOST_LIB"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -125,7 +130,20 @@ _SIGS = {
     "pa_chunk_attend": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _vp], _i32),
 }
+class _HostOnly:
+    """Stand-in for a device entry point in the host-only build: calling it fails loudly."""
+
+    def __init__(self, name):
+        self.name = name
+
+    def __call__(self, *a):
+        raise RuntimeError(f"{self.name} is a device entry point; {LIB_PATH} is a host-only build")
+
+
 for _name, (_args, _res) in _SIGS.items():
+    if HOST_ONLY and not hasattr(_lib, _name):
+        setattr(_lib, _name, _HostOnly(_name))
+        continue
     _fn = getattr(_lib, _name)
     _fn.argtypes = _args
     _fn.restype = _res

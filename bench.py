@@ -93,6 +93,11 @@ WORKLOADS = {
              "D=128, B=32, causal inside the chunk",
     "swap": "preemption by swapping: every 8th sequence of the llama3-70b-shaped batch (32 of "
             "256) swapped out to pinned host memory and back in",
+    "ceilings": "HBM read ceilings: a streaming read of 4 GiB and a gather of 4 GiB as 4 KiB chunks "
+                "in shuffled and in sequential order, swept over launch shapes",
+    "paging_cost": "paging cost at small batch: the long-context decode step (32,768 tokens, "
+                   "64/8 heads, D=128, B=32) over a scattered pool vs physically consecutive "
+                   "blocks, alternating",
 }
 PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
@@ -155,6 +160,12 @@ def main() -> int:
     ap.add_argument("--batch", type=int, default=0,
                     help="llama70b / long32k: number of sequences (0 = the workload's own: 256 / "
                          "32); e.g. 1 for the batch-1 paging-overhead comparison with --pool")
+    ap.add_argument("--flush", action="store_true",
+                    help="decode workloads: write a 1 GiB buffer before every step and time each "
+                         "call by its own HIP events (no byte of the step's data left in any cache)")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="processes of the all-core CPU oracle leg (at most os.cpu_count(); 0 = "
+                         "skip that leg)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the timed steps, run one device-to-device copy of this many MiB "
                          "(a plain copy of known size that calibrates the HBM byte counters)")
@@ -172,11 +183,16 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.workload in ("ceilings", "paging_cost"):
+        line = (run_ceilings if args.workload == "ceilings" else run_paging_cost)(args, dev)
+        print(json.dumps(line), flush=True)
+        return 0 if "error" not in line else 1
     if args.block_size != 16 and args.workload not in ("llama70b", "swap"):
         print(json.dumps({"error": "--block-size applies to the llama70b and swap workloads"}))
         return 2
-    if args.batch and args.workload not in ("llama70b", "long32k"):
-        print(json.dumps({"error": "--batch applies to the llama70b and long32k workloads"}))
+    if args.batch and args.workload not in ("llama70b", "long32k", "paging_cost"):
+        print(json.dumps({"error": "--batch applies to the llama70b, long32k and paging_cost "
+                                   "workloads"}))
         return 2
     w = make_workload(wl, args.workload, args.pool, args.block_size, args.batch)
     t_setup = time.perf_counter()
@@ -196,7 +212,7 @@ def main() -> int:
     return 0 if "error" not in line else 1
 
 
-SPREAD_BLOCKS = 5  # blocks of steps timed after the main region, for the per-step spread
+SPREAD_BLOCKS = 20  # blocks of steps timed after the main region, for the per-step spread
 
 
 def timed_loop(args, step, spread=False, on_timed_end=None):
@@ -250,7 +266,8 @@ def timed_loop(args, step, spread=False, on_timed_end=None):
 
 
 def spread_steps(args):
-    return max(1, args.steps // SPREAD_BLOCKS)
+    # a few steps per block: an event pair around every step would add its own gap to each
+    return max(1, args.steps // 5)
 
 
 def spread_summary(blocks):
@@ -279,12 +296,13 @@ def run_decode(args, w, st, t_setup):
     dev = st.device
     S, B = w.num_seqs, w.block_size
     total = args.warmup + args.steps + SPREAD_BLOCKS * spread_steps(args)
-    max_ctx = st.max_ctx + total
+    ids = np.asarray(w.step_ids, np.int64)
+    # the longest context the steps reach (from the current lengths: a state may have run steps)
+    max_ctx = max(st.max_ctx - 1, int(st.bm.seq_lens(ids).max())) + total
     max_blocks = (max_ctx + B - 1) // B
     nbytes = _lib.pa_decode_workspace_size(S, w.hq, w.head_dim, max_ctx, args.partition)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     out = st.new_out()
-    ids = np.asarray(w.step_ids, np.int64)
 
     # Block tables and lengths live on the device.  Each step's slots and lengths (2 KB) are
     # written into a ring of pinned host buffers that pa_decode_step's first kernel reads
@@ -304,7 +322,13 @@ def run_decode(args, w, st, t_setup):
                                             [t.numpy() for t in pin_lens], pairs_h)
     marks = [torch.cuda.Event() for _ in range(4)]
     stream = torch.cuda.current_stream()
-    host_s, step_lens, n_pairs = [], [], []
+    host_s, step_lens, n_pairs, all_lens = [], [], [], []
+    # --flush: a 1 GiB write before every step, outside per-call events, so no byte of the
+    # step's K/V can still sit in the 256 MB Infinity Cache or the L2s
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+    call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] if args.flush else []
+    timed_calls = []
 
     def step(i, timed):
         r = i % RING
@@ -319,11 +343,20 @@ def run_decode(args, w, st, t_setup):
             host_s.append(time.perf_counter() - h0)
             step_lens.append(lens_h.numpy().copy())
         n_pairs.append(np_)
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xFF)
+            if timed:
+                e0, e1 = call_ev[len(timed_calls)]
+                e0.record(stream)
         if np_:
             _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs_h[:np_]).to(dev))
         _lib.pa_decode_step(out, st.vals["q"], st.vals["k_step"], st.vals["v_step"], st.k_cache,
                             st.v_cache, slots_h, tables_d, lens_d, max_ctx, w.scale,
                             args.partition, ws, new_ctx_lens=lens_h)
+        if flush_buf is not None and timed:
+            e1.record(stream)
+            timed_calls.append((e0, e1))
+        all_lens.append(lens_h.numpy().copy())
         if i % MARK == MARK - 1:
             marks[(i // MARK) % len(marks)].record(stream)
 
@@ -345,8 +378,19 @@ def run_decode(args, w, st, t_setup):
     ms_step = 1e3 * elapsed / args.steps
     # Each step puts one pa_decode_step call on the stream (plus pa_copy_blocks where a step
     # has copy-on-write pairs), so the event time of the region over the steps is the call's
-    # average duration, launch gaps between calls included.
+    # average duration, launch gaps between calls included.  With --flush the region also holds
+    # the flushes: the call's duration is then the mean of its own event pairs.
     dec_avg_ms = region_ms / args.steps
+    flushed = None
+    if flush_buf is not None:
+        per_call = np.array([a.elapsed_time(b) for a, b in timed_calls])
+        dec_avg_ms = float(per_call.mean())
+        flushed = {"flush_bytes": flush_buf.numel(), "call_ms_mean": round(dec_avg_ms, 4),
+                   "call_ms_p10": round(float(np.percentile(per_call, 10)), 4),
+                   "call_ms_median": round(float(np.median(per_call)), 4),
+                   "call_ms_p90": round(float(np.percentile(per_call, 90)), 4),
+                   "note": "a 1 GiB device write before every step; the call (copy-on-write "
+                           "copies if any + pa_decode_step) timed by its own HIP event pair"}
     dec_bytes, write_bytes = zip(*[algorithmic_bytes(l, w, S) for l in step_lens])
     # the timed call is pa_decode_step: decode bytes plus the new tokens' cache write
     dec_bytes_avg = float(np.mean(dec_bytes)) + float(np.mean(write_bytes))
@@ -367,10 +411,14 @@ def run_decode(args, w, st, t_setup):
         step_bytes_avg = step_bytes_avg - logical_kv + uniq
     achieved = dec_bytes_avg / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes_avg / (ms_step * 1e-3) / 1e9
-    headline = args.workload == "llama70b" and not args.batch
+    if flushed is not None:  # the wall clock holds the flushes: the call time is the step
+        value = achieved
+        ms_step = dec_avg_ms
+    all_bytes = [sum(algorithmic_bytes(l, w, S)) for l in all_lens]
+    headline = args.workload == "llama70b" and not args.batch and flushed is None
     cpu = None
     if args.cpu_seqs > 0 and headline:
-        cpu = cpu_baseline(w, st, args.cpu_seqs, args.cpu_seconds)
+        cpu = cpu_baseline(w, st, args.cpu_seqs, args.cpu_seconds, args.cpu_workers)
     line = {"metric": "paged decode attention: HBM GB/s (% of peak) + decode tokens/s at batch 256",
             "value": round(value, 1), "unit": "GB/s"}
     line.update(base_line(args, w, ms_step))
@@ -389,6 +437,10 @@ def run_decode(args, w, st, t_setup):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic()
                      if headline and args.pool == "churned" and w.block_size == 16 else None,
+                     "traffic_source": "profiles/pa_decode_step_llama70b_b256.md: FETCH_SIZE + "
+                                       "WRITE_SIZE per call from rocprofv3 counter runs of the "
+                                       "same kernel sources (null once the sources differ); not "
+                                       "measured in this run",
                      "kernel": "pa_decode_step (cache write + plan, persistent split-K decode, "
                                "merge); avg_ms = HIP-event time of the timed region / steps",
                      "avg_ms": round(dec_avg_ms, 4), "algorithmic_bytes": int(dec_bytes_avg)},
@@ -397,10 +449,130 @@ def run_decode(args, w, st, t_setup):
                                note="per-step time of %d further blocks of steps after the "
                                     "timed region, each between its own HIP events"
                                     % SPREAD_BLOCKS),
+        "calls": {"count": len(all_bytes),
+                  "algorithmic_bytes_mean": int(np.mean(all_bytes)),
+                  "note": "every pa_decode_step call of this run (warm-up, timed, spread "
+                          "blocks): a counter run of this command divides its per-dispatch "
+                          "bytes by this mean"},
         "setup_s": round(t_setup, 1),
     })
+    if flushed is not None:
+        line["flushed"] = flushed
     line.update(extra)
     return line
+
+
+def run_ceilings(args, dev):
+    """Achievable HBM read rates on this GPU (libpa_probe.so): the best streaming read and the
+    best gather of shuffled (and of sequential) 4 KiB chunks over a sweep of launch shapes, each
+    shape timed over 10 launches after 2 warm-ups."""
+    import ctypes as C
+
+    import torch
+
+    lib = C.CDLL(os.path.join(ROOT, "paged_kv_cache_378_amd", "libpa_probe.so"))
+    lib.pa_probe_read_stream.argtypes = [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_void_p,
+                                         C.POINTER(C.c_size_t), C.c_void_p]
+    lib.pa_probe_read_gather.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                         C.c_void_p, C.c_void_p]
+    nbytes = 4 << 30
+    nchunks = nbytes // 4096
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    grids = (256, 384, 512, 768, 1024, 2048)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device=dev)
+    g = torch.Generator().manual_seed(7)
+    orders = {"shuffled": torch.randperm(nchunks, generator=g).to(torch.int32).to(dev),
+              "sequential": torch.arange(nchunks, dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream()
+    s_ptr = stream.cuda_stream
+
+    def timed(launch, reps=10):
+        for _ in range(2):
+            launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    stream_rows, gather_rows = [], []
+    for wg in grids:
+        for loads in (1, 2, 4, 8):
+            got = C.c_size_t()
+            st = lib.pa_probe_read_stream(buf.data_ptr(), nbytes, wg, loads, sink.data_ptr(),
+                                          C.byref(got), s_ptr)
+            if st:
+                return {"error": f"pa_probe_read_stream({wg}, {loads}) returned {st}"}
+            ms = timed(lambda: lib.pa_probe_read_stream(buf.data_ptr(), nbytes, wg, loads,
+                                                        sink.data_ptr(), C.byref(got), s_ptr))
+            stream_rows.append({"workgroups": wg, "loads_in_flight": loads,
+                                "GBps": round(got.value / (ms * 1e-3) / 1e9, 1)})
+    for name, order in orders.items():
+        for wg in grids[:5]:
+            for per_wave in (1, 2, 4):
+                ms = timed(lambda: lib.pa_probe_read_gather(buf.data_ptr(), order.data_ptr(),
+                                                            nchunks, per_wave, wg,
+                                                            sink.data_ptr(), s_ptr))
+                gather_rows.append({"order": name, "workgroups": wg, "chunks_per_wave": per_wave,
+                                    "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+    best_stream = max(stream_rows, key=lambda r: r["GBps"])
+    best = {n: max((r for r in gather_rows if r["order"] == n), key=lambda r: r["GBps"])
+            for n in orders}
+    line = {"metric": "HBM read ceiling (best streaming read)", "value": best_stream["GBps"],
+            "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 2, "higher_is_better": True,
+            "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": WORKLOADS["ceilings"], "parallelism": "none (1 GPU)"},
+            "pct_of_hbm_peak": round(100 * best_stream["GBps"] / HBM_PEAK_GBS, 2),
+            "best_stream": best_stream, "best_gather_shuffled": best["shuffled"],
+            "best_gather_sequential": best["sequential"],
+            "gather_shuffled_pct_of_hbm_peak": round(100 * best["shuffled"]["GBps"] / HBM_PEAK_GBS, 2),
+            "stream_sweep": stream_rows, "gather_sweep": gather_rows}
+    return line
+
+
+def run_paging_cost(args, dev):
+    """The contiguous-vs-paged comparison at small batch ("Taming the Tail", "Deep-Dive
+    Curiosity: The Performance Trade-off": a contiguous kernel is 1-2% faster at batch 1): the
+    same long-context decode step (args.batch sequences, default 1, of 32,768 tokens) over the
+    workload's scattered pool and over physically consecutive blocks, run as decode-step
+    benchmarks in alternation (four of each) so drift hits both the same."""
+    from paged_kv_cache_378_amd import workloads as wl
+    from paged_kv_cache_378_amd.runner import PagedState
+
+    S = args.batch or 1
+    states = {}
+    for pool in ("churned", "contiguous"):
+        w = wl.long_context(S=S)
+        if pool == "contiguous":
+            w.free_order = np.arange(w.num_blocks, dtype=np.int32)
+        states[pool] = (w, PagedState(w, dev, poison=True))
+    runs = {"churned": [], "contiguous": []}
+    sub = argparse.Namespace(**vars(args))
+    sub.cpu_seqs = 0
+    sub.flush = False
+    for _ in range(4):
+        for pool in ("churned", "contiguous"):
+            w, st = states[pool]
+            r = run_decode(sub, w, st, 0.0)
+            if "error" in r:
+                return r
+            runs[pool].append(r)
+    med = {p: float(np.median([r["ms_per_step"] for r in rs])) for p, rs in runs.items()}
+    call = {p: float(np.median([r["roofline"]["avg_ms"] for r in rs])) for p, rs in runs.items()}
+    ratio = med["churned"] / med["contiguous"]
+    return {"metric": "paging cost: decode step time over a scattered pool / over physically "
+                      "consecutive blocks", "value": round(ratio, 4), "unit": "ratio",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": False, "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": WORKLOADS["paging_cost"], "global_batch": S,
+                       "seq_len": 32768, "parallelism": "none (1 GPU)"},
+            "step_ms_median": {p: round(v, 4) for p, v in med.items()},
+            "call_ms_median": {p: round(v, 4) for p, v in call.items()},
+            "step_ms_runs": {p: [r["ms_per_step"] for r in rs] for p, rs in runs.items()},
+            "paging_overhead_pct": round(100 * (ratio - 1), 2),
+            "page_claim": "a contiguous kernel is 1-2% faster at batch 1"}
 
 
 def chunk_flops(lens, C, w):
@@ -570,45 +742,91 @@ def run_swap(args, w, st, t_setup):
     return line
 
 
-def cpu_baseline(w, st, n_seqs, min_seconds):
-    """The fp64 oracle on the first n_seqs sequences of the batch, one thread, repeated until it
-    has run for min_seconds (the batch's K/V are copied to the host once, outside the timing)."""
-    import torch
+def _oracle_batch_loop(batch, scale, min_seconds):
+    """The oracle's decode over `batch` [(q, K, V) in fp64] on this thread, repeated until it
+    has run for min_seconds; returns (sequence-steps done, their context tokens, seconds of
+    oracle time)."""
+    from oracle import attention as att
+    busy, done, ctx = 0.0, 0, 0
+    while busy < min_seconds:
+        for qi, K, V in batch:
+            t0 = time.perf_counter()
+            att.dense_decode(qi, K, V, scale)
+            busy += time.perf_counter() - t0
+            done += 1
+            ctx += K.shape[0]
+    return done, ctx, busy
+
+
+def _oracle_worker(job):
+    """One process of the all-core leg: bf16 bit patterns in, the oracle at one thread."""
+    bits, scale, min_seconds = job
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as att
+    batch = [tuple(att.bf16_bits_to_f64(x) for x in seq) for seq in bits]
+    with threadpool_limits(limits=1):
+        return _oracle_batch_loop(batch, scale, min_seconds)
+
+
+def cpu_baseline(w, st, n_seqs, min_seconds, workers=16):
+    """The fp64 oracle, unchanged, on the first n_seqs sequences of the batch (their K/V copied to
+    the host once, outside the timing), in two legs, each in fresh interpreters (spawned
+    processes: no GPU or torch thread state; in this process, after torch has run, one-thread
+    BLAS measured ~40% slower):
+      * all cores: min(workers, os.cpu_count()) processes, each running its share of the
+        sequences on one thread for at least min_seconds; the rate is the processes' summed
+        context tokens per second of their own oracle time over the batch's mean context;
+      * one thread: one process running every sequence for at least min_seconds.
+    A decode step produces one token per sequence, so sequence-steps per second are tokens/s."""
+    import multiprocessing as mp
+
+    import torch
+
     from paged_kv_cache_378_amd import workloads as wl
 
     n_seqs = min(n_seqs, w.num_seqs)
     q = st.vals["q"]
-    batch = []
-    tokens = 0
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    seq_bits, tokens = [], 0
     for i in range(n_seqs):
         ks, vs = wl.logical_kv(w, w.step_ids[i], st.vals)
-        K = torch.cat(ks).to("cpu", torch.float64).numpy()
-        V = torch.cat(vs).to("cpu", torch.float64).numpy()
-        batch.append((q[i].to("cpu", torch.float64).numpy(), K, V))
-        tokens += K.shape[0]
-    busy = 0.0
-    done = 0
-    with threadpool_limits(limits=1):
-        torch_threads = torch.get_num_threads()
-        torch.set_num_threads(1)
-        try:
-            while busy < min_seconds:
-                for qi, K, V in batch:
-                    t0 = time.perf_counter()
-                    att.dense_decode(qi, K, V, w.scale)
-                    busy += time.perf_counter() - t0
-                    done += 1
-        finally:
-            torch.set_num_threads(torch_threads)
-    return {"value": round(done / busy, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the first {n_seqs} of {w.num_seqs} sequences of one decode step "
-                      f"({tokens} context tokens, all {w.hq} heads), numpy fp64, 1 thread, run "
-                      f"{done // n_seqs}x ({done} sequence-steps in {busy:.1f} s of oracle time; "
+        seq_bits.append((bits(q[i]), bits(torch.cat(ks)), bits(torch.cat(vs))))
+        tokens += seq_bits[-1][1].shape[0]
+    ncpu = os.cpu_count() or 1
+    what = (f"the first {n_seqs} of {w.num_seqs} sequences of one decode step ({tokens} context "
+            f"tokens, all {w.hq} heads), numpy fp64")
+    ctx = mp.get_context("spawn")  # fresh interpreters, no GPU state
+    with ctx.Pool(1) as pool:
+        d1, _, b1 = pool.apply(_oracle_worker, ((seq_bits, w.scale, min_seconds),))
+    one = {"value": round(d1 / b1, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "os_cpu_count": ncpu,
+           "sample": f"{what}, 1 process of 1 thread, run {d1 // n_seqs}x ({d1} sequence-steps "
+                     f"in {b1:.1f} s of oracle time; the host copy of K/V is not timed)",
+           "oracle_s": round(b1, 2)}
+    nproc = min(workers, ncpu, n_seqs)
+    if nproc <= 1:
+        return one
+    jobs = [(seq_bits[k::nproc], w.scale, min_seconds) for k in range(nproc)]
+    t0 = time.perf_counter()
+    with ctx.Pool(nproc) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    wall = time.perf_counter() - t0
+    done = sum(d for d, _, _ in res)
+    # The processes' shares differ in length mix, so their rates are summed in context tokens
+    # per second and converted back at the batch's mean context (a sum of sequence rates would
+    # favour shares of short sequences).
+    rate = sum(c / b for _, c, b in res) / (tokens / n_seqs)
+    return {"value": round(rate, 1), "unit": "tokens/s", "cores": nproc, "os_cpu_count": ncpu,
+            "kind": "oracle",
+            "sample": f"{what}, {nproc} processes of 1 thread each, each on every {nproc}-th "
+                      f"sequence for >= {min_seconds:.0f} s ({done} sequence-steps in all; rate = the "
+                      f"processes' summed context tokens per second / the batch's mean context; "
                       f"the host copy of K/V is not timed)",
-            "oracle_s": round(busy, 2)}
+            "wall_s_with_startup": round(wall, 1), "one_thread": one}
 
 
 if __name__ == "__main__":

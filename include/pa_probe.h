@@ -1,0 +1,45 @@
+/*
+ * pa_probe.h -- HBM read-bandwidth probes for MI355X (libpa_probe.so).
+ *
+ * Measurement aids, not part of the paged-attention method: they give the achievable read
+ * rates that the decode kernel's bandwidth is compared with (the 8 TB/s figure is the vendor's
+ * peak; what a kernel can stream is lower).  Two access patterns:
+ *   - a streaming read of one contiguous buffer;
+ *   - a gather of 4 KiB chunks in a caller-given order: a shuffled order is the pattern of a
+ *     decode over a pool whose blocks are scattered ([TT] "How the Architecture Works": logical
+ *     blocks map to physical blocks anywhere in the pool; at B = 16, D = 128, bf16 a
+ *     (block, kv-head) K or V tile is 4 KiB).
+ * Both only enqueue one kernel on `stream` (a hipStream_t, NULL = null stream); the caller owns
+ * every buffer and times the launch.  Loads are 16-byte non-temporal loads; each thread folds
+ * what it read into one word of `sink` so no load can be removed.  Return: 0, or -1 for an
+ * argument outside what the kernels support, -7 for a launch error (as pa.h's codes).
+ */
+#ifndef PA_PROBE_H_
+#define PA_PROBE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads the first floor(nbytes / (16 * workgroups * 256 * loads)) * (16 * workgroups * 256 *
+ * loads) bytes of buf (device, 16-byte aligned) once; *read_bytes receives that count.
+ * workgroups in [1, 65536] of 256 threads; loads in {1, 2, 4, 8}: 16-byte loads each lane keeps
+ * in flight.  sink: device, workgroups * 256 uint32. */
+int32_t pa_probe_read_stream(const void* buf, size_t nbytes, int32_t workgroups, int32_t loads,
+                             uint32_t* sink, size_t* read_bytes, void* stream);
+
+/* Reads chunks order[0..nchunks) of 4 KiB each from buf (device, nchunks * 4 KiB, 16-byte
+ * aligned), every chunk once; order (device int32) holds chunk ids in [0, nchunks) (others are
+ * clamped into range).  A wave reads `per_wave` chunks per iteration (in {1, 2, 4}), each as
+ * four 1 KiB contiguous loads.  workgroups of 256 threads; sink as above. */
+int32_t pa_probe_read_gather(const void* buf, const int32_t* order, int32_t nchunks,
+                             int32_t per_wave, int32_t workgroups, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_PROBE_H_ */

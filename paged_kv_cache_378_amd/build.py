@@ -16,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
+PROBE = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,11 +33,10 @@ def _sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".cpp", ".hip")))
 
 
-def _compile(src: str) -> str:
-    path = os.path.join(CSRC, src)
-    obj = os.path.join(OBJ, src + ".o")
+def _compile(path: str) -> str:
+    obj = os.path.join(OBJ, os.path.basename(path) + ".o")
     cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
-    if src.endswith(".hip"):
+    if path.endswith(".hip"):
         cmd[1:1] = ["-x", "hip", *DEVICE]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -47,19 +48,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = _sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """libpa.so (the library) and libpa_probe.so (the bandwidth probes bench.py measures the
+    achievable read rates with)."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = [os.path.join(CSRC, f) for f in _sources()]
+    probes = sorted(os.path.join(PROBE, f) for f in os.listdir(PROBE) if f.endswith(".hip"))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probes))) as ex:
+        objs = list(ex.map(_compile, srcs + probes))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources and {PROBE_LIB}")
     return LIB
 
 

@@ -161,8 +161,9 @@ def main() -> int:
                     help="llama70b / long32k: number of sequences (0 = the workload's own: 256 / "
                          "32); e.g. 1 for the batch-1 paging-overhead comparison with --pool")
     ap.add_argument("--flush", action="store_true",
-                    help="decode workloads: write a 1 GiB buffer before every step and time each "
-                         "call by its own HIP events (no byte of the step's data left in any cache)")
+                    help="decode workloads: write 1 GiB and read another 1 GiB before every step "
+                         "and time each call by its own HIP events (no byte of the step's data "
+                         "left in any cache, no dirty line to write back)")
     ap.add_argument("--cpu-workers", type=int, default=16,
                     help="processes of the all-core CPU oracle leg (at most os.cpu_count(); 0 = "
                          "skip that leg)")
@@ -323,9 +324,12 @@ def run_decode(args, w, st, t_setup):
     marks = [torch.cuda.Event() for _ in range(4)]
     stream = torch.cuda.current_stream()
     host_s, step_lens, n_pairs, all_lens = [], [], [], []
-    # --flush: a 1 GiB write before every step, outside per-call events, so no byte of the
-    # step's K/V can still sit in the 256 MB Infinity Cache or the L2s
+    # --flush: before every step, outside per-call events, a 1 GiB write and then an ordinary
+    # read of another 1 GiB, so no byte of the step's data is left in the 256 MB Infinity Cache
+    # or the L2s, and no dirty line either (a write alone would leave up to 256 MB of them for
+    # the step to write back)
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+    flush_rd = torch.ones(1 << 28, dtype=torch.int32, device=dev) if args.flush else None
     call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)] if args.flush else []
     timed_calls = []
@@ -345,6 +349,7 @@ def run_decode(args, w, st, t_setup):
         n_pairs.append(np_)
         if flush_buf is not None:
             flush_buf.fill_(i & 0xFF)
+            flush_rd.amax()
             if timed:
                 e0, e1 = call_ev[len(timed_calls)]
                 e0.record(stream)
@@ -385,12 +390,14 @@ def run_decode(args, w, st, t_setup):
     if flush_buf is not None:
         per_call = np.array([a.elapsed_time(b) for a, b in timed_calls])
         dec_avg_ms = float(per_call.mean())
-        flushed = {"flush_bytes": flush_buf.numel(), "call_ms_mean": round(dec_avg_ms, 4),
+        flushed = {"flush_bytes_written": flush_buf.numel(),
+                   "flush_bytes_read": flush_rd.numel() * 4, "call_ms_mean": round(dec_avg_ms, 4),
                    "call_ms_p10": round(float(np.percentile(per_call, 10)), 4),
                    "call_ms_median": round(float(np.median(per_call)), 4),
                    "call_ms_p90": round(float(np.percentile(per_call, 90)), 4),
-                   "note": "a 1 GiB device write before every step; the call (copy-on-write "
-                           "copies if any + pa_decode_step) timed by its own HIP event pair"}
+                   "note": "a 1 GiB device write and a 1 GiB read of another buffer before "
+                           "every step; the call (copy-on-write copies if any + "
+                           "pa_decode_step) timed by its own HIP event pair"}
     dec_bytes, write_bytes = zip(*[algorithmic_bytes(l, w, S) for l in step_lens])
     # the timed call is pa_decode_step: decode bytes plus the new tokens' cache write
     dec_bytes_avg = float(np.mean(dec_bytes)) + float(np.mean(write_bytes))

@@ -160,6 +160,10 @@ def main() -> int:
     ap.add_argument("--batch", type=int, default=0,
                     help="llama70b / long32k: number of sequences (0 = the workload's own: 256 / "
                          "32); e.g. 1 for the batch-1 paging-overhead comparison with --pool")
+    ap.add_argument("--no-share-groups", action="store_true",
+                    help="shared16 / shared32: decode without share groups (by default the "
+                         "batch's groups from pa_bm_share_groups, taken once before the steps, are "
+                         "passed to pa_decode_step_shared)")
     ap.add_argument("--flush", action="store_true",
                     help="decode workloads: write 1 GiB and read another 1 GiB before every step "
                          "and time each call by its own HIP events (no byte of the step's data "
@@ -324,6 +328,24 @@ def run_decode(args, w, st, t_setup):
     marks = [torch.cuda.Event() for _ in range(4)]
     stream = torch.cuda.current_stream()
     host_s, step_lens, n_pairs, all_lens = [], [], [], []
+    # Share groups (shared-prefix workloads): the host helper's groups, taken once from the
+    # batch's tables before the steps; they stay valid through the steps' copy-on-write (the
+    # copies hold the same K/V at the shared positions)
+    groups_d, share = None, None
+    if args.workload.startswith("shared") and not args.no_share_groups:
+        g = w.hq // w.hkv
+        groups = st.bm.share_groups(ids, max(2, min(4, 16 // g)), 32)
+        groups_d = torch.from_numpy(groups).to(dev)
+        lens_now = st.bm.seq_lens(ids)
+        gm = min(4, 16 // g)
+        reads = int(lens_now.sum()) - sum(
+            (int((r[1:] >= 0).sum()) - -(-int((r[1:] >= 0).sum()) // gm)) * (int(r[0]) // 32 * 32)
+            for r in groups)
+        share = {"groups": int(len(groups)),
+                 "sequences_in_groups": int(sum((r[1:] >= 0).sum() for r in groups)),
+                 "tokens_read_per_step": reads, "tokens_logical": int(lens_now.sum()),
+                 "note": "pa_bm_share_groups once before the steps; each group's shared tokens "
+                         "(rounded down to 32) are read once per item of %d members" % gm}
     # --flush: before every step, outside per-call events, a 1 GiB write and then an ordinary
     # read of another 1 GiB, so no byte of the step's data is left in the 256 MB Infinity Cache
     # or the L2s, and no dirty line either (a write alone would leave up to 256 MB of them for
@@ -355,9 +377,15 @@ def run_decode(args, w, st, t_setup):
                 e0.record(stream)
         if np_:
             _lib.pa_copy_blocks(st.k_cache, st.v_cache, torch.from_numpy(pairs_h[:np_]).to(dev))
-        _lib.pa_decode_step(out, st.vals["q"], st.vals["k_step"], st.vals["v_step"], st.k_cache,
-                            st.v_cache, slots_h, tables_d, lens_d, max_ctx, w.scale,
-                            args.partition, ws, new_ctx_lens=lens_h)
+        if groups_d is None:
+            _lib.pa_decode_step(out, st.vals["q"], st.vals["k_step"], st.vals["v_step"],
+                                st.k_cache, st.v_cache, slots_h, tables_d, lens_d, max_ctx,
+                                w.scale, args.partition, ws, new_ctx_lens=lens_h)
+        else:
+            _lib.pa_decode_step_shared(out, st.vals["q"], st.vals["k_step"], st.vals["v_step"],
+                                       st.k_cache, st.v_cache, slots_h, tables_d, lens_d, max_ctx,
+                                       w.scale, groups_d, args.partition, ws,
+                                       new_ctx_lens=lens_h)
         if flush_buf is not None and timed:
             e1.record(stream)
             timed_calls.append((e0, e1))
@@ -465,6 +493,8 @@ def run_decode(args, w, st, t_setup):
     })
     if flushed is not None:
         line["flushed"] = flushed
+    if share is not None:
+        line["share_groups"] = share
     line.update(extra)
     return line
 

@@ -245,6 +245,24 @@ pa_status pa_bm_cache_evict(pa_bm* bm, int32_t n_blocks, int32_t* n_evicted_out)
  * slots past the new length are simply never read. */
 pa_status pa_bm_truncate(pa_bm* bm, int64_t seq_id, int32_t n_keep);
 
+/* Share groups of a batch for pa_decode_shared / pa_decode_step_shared ([TT] "Complex Memory
+ * Sharing": sequences forked from one prompt, or admitted through the prefix cache, read the
+ * same physical blocks for their shared part).  Sequences of seq_ids whose tables start with
+ * the same physical blocks are grouped, at most max_members (2..4) per group: the tables are
+ * ordered so that common physical prefixes are adjacent, and the tree of those prefixes is
+ * walked from its deepest nodes up -- at each node the sequences not yet grouped form groups
+ * of max_members sharing that node's tokens; a smaller remainder is grouped there when that
+ * saves at least the reads it could save one level up (a group of k saves (k - 1) * L
+ * reads), else left to the parent.  Groups sharing fewer than min_tokens tokens are left
+ * out.  groups_out: host [cap, 5] ints, one row per group: the
+ * number of tokens L every member holds in the same physical blocks (positions below every
+ * member's length), then the members as indices into seq_ids, ascending, -1 padded.
+ * *n_groups_out receives the number of groups (rows ordered by their first member);
+ * PA_ERR_INVALID_ARG if it exceeds cap (at most n / 2 are ever needed).  Host only. */
+pa_status pa_bm_share_groups(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_members,
+                             int32_t min_tokens, int32_t* groups_out, int32_t cap,
+                             int32_t* n_groups_out);
+
 /* ---- host utilities ---------------------------------------------------------------- */
 
 typedef struct {
@@ -346,6 +364,30 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t max_ctx_len, float scale, int32_t dtype, int32_t partition_tokens,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode with share groups ([TT] "Complex Memory Sharing": requests that share a prompt read
+ * its blocks from one physical copy).  groups: device int32 [n_groups, 5], rows as
+ * pa_bm_share_groups writes them: L, then up to 4 member sequences (indices in [0, S), -1
+ * padded); 0 <= n_groups <= S.  The caller promises that every member holds the same keys and
+ * values as its group's first member at positions [0, L) -- true for blocks a fork or the
+ * prefix cache shares, and it stays true after copy-on-write (the copies are bit copies) as
+ * long as no member is truncated below L.  Each group's range is then read once for several
+ * members: on the matrix cores (bf16, 3 to 8 query heads per kv-head) one work item serves
+ * 16 / (Hq/Hkv) members (at most 4), their heads side by side in the same 16-column operand, and
+ * each member merges that result with its own tokens [L, n) like any other partition.  The
+ * result is the same attention (it differs from pa_decode's only by the order of its fp32
+ * sums).  The device plan checks each group: a member index out of range, an invalid length,
+ * or a sequence already taken by an earlier group drops that member; L is cut to the members'
+ * shortest length and rounded down to a multiple of 32; a group left with fewer than two
+ * members or L < 32 is ignored.  Other shapes and dtypes ignore the groups.  A wrong promise
+ * gives wrong outputs for that group's members, never an access outside the buffers.  The
+ * workspace is the one pa_decode_workspace_size reports. */
+pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* ctx_lens, int32_t S,
+                           int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+                           int32_t max_blocks, int32_t max_ctx_len, float scale, int32_t dtype,
+                           int32_t partition_tokens, const int32_t* groups, int32_t n_groups,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* One decode step of a serving loop on the device, fused: the cache write and block-table patch
  * of pa_cache_append for one new token per sequence (tokens_each = 1), then pa_decode over the
  * updated tables.  The decode's planning work runs in the same launch as the cache write (the
@@ -372,6 +414,17 @@ pa_status pa_decode_step(void* out, const void* q, const void* key, const void* 
                          int32_t dtype, int32_t partition_tokens, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* pa_decode_step with share groups (as in pa_decode_shared). */
+pa_status pa_decode_step_shared(void* out, const void* q, const void* key, const void* value,
+                                void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                int32_t* block_tables, int32_t* ctx_lens,
+                                const int32_t* new_ctx_lens, int32_t S, int32_t Hq, int32_t Hkv,
+                                int32_t D, int32_t B, int32_t num_blocks, int32_t max_blocks,
+                                int32_t max_ctx_len, float scale, int32_t dtype,
+                                int32_t partition_tokens, const int32_t* groups,
+                                int32_t n_groups, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Bytes of device scratch pa_decode_step_noalloc holds on each GPU it runs on, in MiB. */
 #define PA_NOALLOC_SCRATCH_MIB 96
 
@@ -384,7 +437,7 @@ pa_status pa_decode_step(void* out, const void* q, const void* key, const void* 
  * Arguments, results and errors are those of pa_decode_step, plus PA_ERR_WORKSPACE (before
  * any device work) when the batch needs more scratch than the array holds -- the size
  * pa_decode_workspace_size(S, Hq, D, max_ctx_len, partition_tokens) reports; e.g. 256
- * sequences of 64 query heads, D = 128, fit up to max_ctx_len = 11,264 with automatic
+ * sequences of 64 query heads, D = 128, fit up to max_ctx_len = 10,240 with automatic
  * partitions.  Every call on one GPU shares that GPU's array, and the array keeps the last
  * call's contents (each call initialises what it reads): calls that overlap on one GPU (two
  * streams or two threads) race and must be serialised by the caller. */

@@ -105,6 +105,7 @@ _SIGS = {
     "pa_bm_seq_len": ([_vp, _i64, _pi32], _i32),
     "pa_bm_seq_lens": ([_vp, _pi64, _i32, _pi32], _i32),
     "pa_bm_refcount": ([_vp, _i32, _pi32], _i32),
+    "pa_bm_share_groups": ([_vp, _pi64, _i32, _i32, _i32, _pi32, _i32, _pi32], _i32),
     "pa_bm_free_list": ([_vp, _pi32, _i32, _pi32], _i32),
     "pa_bm_stats": ([_vp, C.POINTER(pa_bm_stats_t)], _i32),
     "pa_bm_swap_out": ([_vp, _i64, _pi32, _i32, _pi32], _i32),
@@ -122,6 +123,11 @@ _SIGS = {
     "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)], _i32),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                    _f32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "pa_decode_shared": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                          _i32, _f32, _i32, _i32, _vp, _i32, _vp, _sz, _vp], _i32),
+    "pa_decode_step_shared": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                               _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _i32, _vp, _sz,
+                               _vp], _i32),
     "pa_decode_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                         _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp], _i32),
     "pa_decode_step_noalloc": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
@@ -282,6 +288,17 @@ def pa_bm_seq_lens(h, seq_ids, lens_out=None) -> np.ndarray:
     return lens
 
 
+def pa_bm_share_groups(h, seq_ids, max_members: int = 4, min_tokens: int = 32) -> np.ndarray:
+    """[n_groups, 5] int32 rows (shared tokens L, member batch indices, -1 padded)."""
+    ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+    cap = max(len(ids) // 2, 1)
+    out = np.empty((cap, 5), np.int32)
+    n = _i32()
+    _check(_lib.pa_bm_share_groups(h, ids.ctypes.data_as(_pi64), len(ids), max_members,
+                                   min_tokens, _ptr32(out), cap, C.byref(n)))
+    return out[:n.value].copy()
+
+
 def pa_bm_refcount(h, block: int) -> int:
     n = _i32()
     _check(_lib.pa_bm_refcount(h, block, C.byref(n)))
@@ -398,6 +415,9 @@ class BlockManager:
 
     def refcount(self, block):
         return pa_bm_refcount(self.h, block)
+
+    def share_groups(self, seq_ids, max_members=4, min_tokens=32):
+        return pa_bm_share_groups(self.h, seq_ids, max_members, min_tokens)
 
     def free_list(self):
         return pa_bm_free_list(self.h)
@@ -546,6 +566,37 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, ctx_lens, max_ctx_len: int
                           partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
 
 
+def _groups_arg(groups):
+    """(device pointer, rows) of share groups: None or an int32 device tensor [n, 5]."""
+    torch = _torch()
+    if groups is None:
+        return None, 0
+    if groups.dim() != 2 or groups.shape[1] != 5:
+        raise PaError(PA_ERR_INVALID_ARG, "groups must be [n_groups, 5]")
+    return (_dev(groups, "groups", torch.int32) if groups.shape[0] else None), groups.shape[0]
+
+
+def pa_decode_shared(out, q, k_cache, v_cache, block_tables, ctx_lens, max_ctx_len: int,
+                     scale: float, groups=None, partition_tokens: int = 0, workspace=None,
+                     stream=None) -> None:
+    torch = _torch()
+    NB, Hkv, B, D = _pool_shape(k_cache, v_cache)
+    S, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise PaError(PA_ERR_INVALID_ARG, "q/out must be [S, Hq, D] of the pools' dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(ctx_lens.shape) != (S,):
+        raise PaError(PA_ERR_INVALID_ARG, "block_tables must be [S, max_blocks], ctx_lens [S]")
+    g_ptr, ng = _groups_arg(groups)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                            workspace.numel() * workspace.element_size())
+    _check(_lib.pa_decode_shared(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                 _dev(v_cache, "v_cache"),
+                                 _dev(block_tables, "block_tables", torch.int32),
+                                 _dev(ctx_lens, "ctx_lens", torch.int32), S, Hq, Hkv, D, B, NB,
+                                 block_tables.shape[1], max_ctx_len, float(scale), _dtype_code(q),
+                                 partition_tokens, g_ptr, ng, ws_ptr, ws_bytes, _stream(stream)))
+
+
 def _step_input(t, what: str):
     """Device tensor, or a pinned host tensor (the library reads page-locked memory directly)."""
     torch = _torch()
@@ -596,6 +647,21 @@ def pa_decode_step(out, q, key, value, k_cache, v_cache, slot_mapping, block_tab
                                                             workspace.numel() * workspace.element_size())
     _check(_lib.pa_decode_step(*args, max_ctx_len, float(scale), _dtype_code(q), partition_tokens,
                                ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_decode_step_shared(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables,
+                          ctx_lens, max_ctx_len: int, scale: float, groups=None,
+                          partition_tokens: int = 0, workspace=None, stream=None,
+                          new_ctx_lens=None) -> None:
+    """pa_decode_step with share groups (an int32 device tensor [n_groups, 5], or None)."""
+    args = _step_args(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, ctx_lens,
+                      new_ctx_lens)
+    g_ptr, ng = _groups_arg(groups)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                            workspace.numel() * workspace.element_size())
+    _check(_lib.pa_decode_step_shared(*args, max_ctx_len, float(scale), _dtype_code(q),
+                                      partition_tokens, g_ptr, ng, ws_ptr, ws_bytes,
+                                      _stream(stream)))
 
 
 PA_NOALLOC_SCRATCH_BYTES = 96 << 20  # PA_NOALLOC_SCRATCH_MIB of include/pa.h

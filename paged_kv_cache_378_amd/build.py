@@ -33,14 +33,23 @@ def _sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".cpp", ".hip")))
 
 
+RESOURCES = os.path.join(OBJ, "kernel_resources.txt")
+
+
 def _compile(path: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(path) + ".o")
     cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
     if path.endswith(".hip"):
-        cmd[1:1] = ["-x", "hip", *DEVICE]
+        # the compiler's per-kernel resource report (registers, scratch, occupancy, LDS) is kept
+        # beside the objects; tests/test_kernel_resources.py reads it
+        cmd[1:1] = ["-x", "hip", *DEVICE, "-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    remark = "[-Rpass-analysis=kernel-resource-usage]"
+    if path.endswith(".hip"):
+        with open(os.path.join(OBJ, os.path.basename(path) + ".resources.txt"), "w") as f:
+            f.write("\n".join(l for l in res.stderr.splitlines() if remark in l) + "\n")
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l and remark not in l)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{err}")
     if err.strip():

@@ -498,6 +498,101 @@ pa_status pa_bm_seq_lens(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* 
   return ok();
 }
 
+pa_status pa_bm_share_groups(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t max_members,
+                             int32_t min_tokens, int32_t* groups_out, int32_t cap,
+                             int32_t* n_groups_out) {
+  if (!bm || !n_groups_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_share_groups: NULL argument");
+  *n_groups_out = 0;
+  if (n < 0 || cap < 0 || max_members < 2 || max_members > 4 || min_tokens < 1)
+    return fail(PA_ERR_INVALID_ARG,
+                "pa_bm_share_groups: n %d, cap %d, max_members %d (2..4), min_tokens %d (>= 1)", n,
+                cap, max_members, min_tokens);
+  if (n > 0 && !seq_ids) return fail(PA_ERR_INVALID_ARG, "pa_bm_share_groups: seq_ids NULL");
+  if (cap > 0 && !groups_out) return fail(PA_ERR_INVALID_ARG, "pa_bm_share_groups: groups_out NULL");
+  try {
+    std::vector<const Seq*> seq(static_cast<size_t>(n));
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = bm->seqs.find(seq_ids[i]);
+      if (it == bm->seqs.end())
+        return bm->is_swapped(seq_ids[i])
+                   ? fail(PA_ERR_SWAPPED, "pa_bm_share_groups: sequence %lld is swapped out",
+                          (long long)seq_ids[i])
+                   : fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_share_groups: unknown sequence %lld",
+                          (long long)seq_ids[i]);
+      seq[i] = &it->second;
+    }
+    // Tables in lexicographic order of their physical blocks: sequences with the longest
+    // common physical prefix end up next to each other.
+    std::vector<int32_t> ord(static_cast<size_t>(n));
+    for (int32_t i = 0; i < n; ++i) ord[i] = i;
+    std::sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) {
+      return std::lexicographical_compare(seq[x]->blocks.begin(), seq[x]->blocks.end(),
+                                          seq[y]->blocks.begin(), seq[y]->blocks.end()) ||
+             (seq[x]->blocks == seq[y]->blocks && x < y);
+    });
+    // Tokens two sequences hold in the same physical blocks (positions below both lengths).
+    auto shared = [&](int32_t x, int32_t y) -> int64_t {
+      const auto& a = seq[x]->blocks;
+      const auto& b = seq[y]->blocks;
+      size_t k = 0;
+      while (k < a.size() && k < b.size() && a[k] == b[k]) ++k;
+      return std::min<int64_t>({static_cast<int64_t>(k) * bm->B, seq[x]->n, seq[y]->n});
+    };
+    std::vector<int64_t> adj(n > 0 ? static_cast<size_t>(n - 1) : 0);
+    for (int32_t i = 0; i + 1 < n; ++i) adj[i] = shared(ord[i], ord[i + 1]);
+    // The sorted order is the leaf order of the tree of common prefixes: a range whose adjacent
+    // shared counts are all >= m is a node whose sequences share m tokens.  Walk it bottom-up:
+    // at each node (m = the range's smallest adjacent count) group the sequences its subtrees
+    // left over, max_members at a time; a remainder of r >= 2 is grouped here too when that
+    // saves at least what its members could save one level up ((r - 1) m >= r m_parent),
+    // otherwise it is left to the parent.  A group of k saves (k - 1) L reads.
+    std::vector<std::pair<int64_t, std::vector<int32_t>>> groups;
+    std::function<std::vector<int32_t>(int32_t, int32_t, int64_t)> walk =
+        [&](int32_t lo, int32_t hi, int64_t m_parent) -> std::vector<int32_t> {
+      if (hi - lo == 1) return {ord[lo]};
+      int64_t m = INT64_MAX;
+      for (int32_t i = lo; i + 1 < hi; ++i) m = std::min(m, adj[i]);
+      std::vector<int32_t> left;
+      int32_t start = lo;
+      for (int32_t i = lo; i + 1 < hi; ++i)
+        if (adj[i] == m) {
+          auto sub = walk(start, i + 1, m);
+          left.insert(left.end(), sub.begin(), sub.end());
+          start = i + 1;
+        }
+      auto sub = walk(start, hi, m);
+      left.insert(left.end(), sub.begin(), sub.end());
+      if (m < min_tokens) return left;
+      size_t k = 0;
+      for (; left.size() - k >= static_cast<size_t>(max_members); k += max_members)
+        groups.emplace_back(m, std::vector<int32_t>(left.begin() + k, left.begin() + k + max_members));
+      const int64_t r = static_cast<int64_t>(left.size() - k);
+      if (r >= 2 && (r - 1) * m >= r * m_parent) {
+        groups.emplace_back(m, std::vector<int32_t>(left.begin() + k, left.end()));
+        k = left.size();
+      }
+      return std::vector<int32_t>(left.begin() + k, left.end());
+    };
+    if (n > 1) (void)walk(0, n, 0);
+    for (auto& g : groups) std::sort(g.second.begin(), g.second.end());
+    std::sort(groups.begin(), groups.end(),
+              [](const auto& x, const auto& y) { return x.second[0] < y.second[0]; });
+    *n_groups_out = static_cast<int32_t>(groups.size());
+    if (static_cast<int32_t>(groups.size()) > cap)
+      return fail(PA_ERR_INVALID_ARG, "pa_bm_share_groups: %zu groups, capacity %d",
+                  groups.size(), cap);
+    for (size_t g = 0; g < groups.size(); ++g) {
+      int32_t* row = groups_out + g * 5;
+      row[0] = static_cast<int32_t>(std::min<int64_t>(groups[g].first, INT32_MAX));
+      for (int k = 0; k < 4; ++k)
+        row[1 + k] = k < static_cast<int>(groups[g].second.size()) ? groups[g].second[k] : -1;
+    }
+  } catch (...) {
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_share_groups: out of host memory");
+  }
+  return ok();
+}
+
 pa_status pa_bm_refcount(pa_bm* bm, int32_t block, int32_t* out) {
   if (!bm || !out) return fail(PA_ERR_INVALID_ARG, "pa_bm_refcount: NULL argument");
   if (block < 0 || block >= bm->num_blocks)

@@ -44,6 +44,7 @@
 // clamped in-range address and their score is set to -inf and their V elements to zero, so
 // values past the end (even NaN) cannot reach the output.
 
+#include <climits>
 #include <cmath>
 #include <map>
 #include <mutex>
@@ -63,6 +64,10 @@ constexpr int kMinAutoPT = 1024;  // smallest partition the automatic choice use
                                   // 32,768 tokens at batch 1 take 0.065 ms at 256, 0.040 at 1,024)
 constexpr int kMaxAutoPT = 4096;  // largest partition the automatic choice uses
 constexpr int kPtSlot = 11;       // queue[kPtSlot]: the partition length the plan used
+constexpr int kPmaxSlot = 12;     // queue[kPmaxSlot]: partial-result slots per (sequence, head)
+constexpr int kGroupMembers = 4;  // sequences a share group may name
+constexpr int kGroupRec = 1 + kGroupMembers;  // caller's record: tokens, members
+constexpr int kVGroupRec = 2 + kGroupMembers;  // validated record: tokens, members, count
 constexpr int kPlanThreads = 256;
 constexpr int kMaxBuckets = kMaxPT / 32 + 1;  // partial partitions bucketed by 32-token tiles
 constexpr int kPlanKeep = 2048;  // sequences whose lengths the plan keeps in LDS between passes
@@ -71,6 +76,9 @@ constexpr int kShareSlots = 1 << kShareBits;
 constexpr int kShareProbes = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// A work-list entry is two int4: (sequence s, or -1 - group for a share-group item; partial
+// slot; first token; end token) and the member sequences ((s, -1, -1, -1) for a sequence's own
+// item).  Each entry stands for Hkv items, one per kv-head.
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -80,9 +88,14 @@ struct DecodeArgs {
   const int32_t* ctx_lens;
   float* part_o;    // [S, Hq, Pmax, D]  partition outputs (normalised)
   float2* part_ml;  // [S, Hq, Pmax]     (max in log2 units, sum)
-  int2* items;      // work list: (sequence, partition) entries, longest first; Hkv items each
+  int4* items;      // work list: entries (see above), longest first
   int* queue;       // [0] number of items, [2 + x] next unclaimed slot of XCD x
   int* done;        // [S, Hkv] partitions finished (split sequences), zeroed by the plan
+  int* nparts;      // [S] partial results of each sequence (written by the plan)
+  const int32_t* groups;  // caller's share groups [ngroups][kGroupRec] (device), or null
+  int* vgroups;     // [ngroups][kVGroupRec] the groups as the plan accepted them
+  int ngroups;      // groups given
+  int gmem;         // sequences one group item serves (16 / G on the matrix cores; 0: no groups)
   int S, Hq, Hkv, G, max_blocks, num_blocks, PT, Pmax;
   int len_cap;      // min(max_blocks * B, max_ctx_len): longest context the call may see
   float scale_log2;
@@ -95,25 +108,36 @@ __device__ __forceinline__ int eff_len(int n, int cap, bool& bad) {
   return n < 0 ? 0 : (n > cap ? cap : n);
 }
 
+// Element k of a 4-entry array by selects on constant indices: a runtime index into a local
+// array makes the compiler keep the array in scratch memory (a 12% slower decode, measured).
+__device__ __forceinline__ int pick4(const int (&v)[kGroupMembers], int k) {
+  return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
+}
+
 // ---------------------------------------------------------------------------------------
 // Shared epilogue: merge the NW wave states held in LDS and store.
-// s_ml[w][h] = (m, l); s_o[w][h][d] = unnormalised output of wave w relative to its own m.
+// s_ml[w][c] = (m, l); s_o[w][c][d] = unnormalised output of wave w relative to its own m, for
+// the ncols columns of the item: column c is head c % G of member c / G.  A member with one
+// partition gets its final output, the others a partial result in slot `slot`.
 // ---------------------------------------------------------------------------------------
 template <typename T, int D, int HMAX>
-__device__ void finish_partition(const DecodeArgs& a, int s, int kvh, int part, int nparts,
+__device__ void finish_partition(const DecodeArgs& a, const int (&mem)[kGroupMembers],
+                                 const int (&np)[kGroupMembers], int ncols, int kvh, int slot,
                                  bool bad, float (*s_ml)[HMAX][2], float (*s_o)[HMAX][D]) {
   const int G = a.G;
-  for (int idx = threadIdx.x; idx < G * D; idx += kNW * kWave) {
-    const int h = idx / D, d = idx - h * D;
+  for (int idx = threadIdx.x; idx < ncols * D; idx += kNW * kWave) {
+    const int c = idx / D, d = idx - c * D;
+    const int j = c / G, h = c - j * G;
+    const int s = pick4(mem, j), nparts = pick4(np, j);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_ml[w][h][0]);
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_ml[w][c][0]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) {
-      const float sc = exp2f(s_ml[w][h][0] - M);
-      L += s_ml[w][h][1] * sc;
-      O += s_o[w][h][d] * sc;
+      const float sc = exp2f(s_ml[w][c][0] - M);
+      L += s_ml[w][c][1] * sc;
+      O += s_o[w][c][d] * sc;
     }
     const int hq = kvh * G + h;
     const float r = bad ? NAN : O / L;
@@ -122,7 +146,7 @@ __device__ void finish_partition(const DecodeArgs& a, int s, int kvh, int part, 
     } else {
       // partials are written through to memory (agent scope): the workgroup that merges them
       // may run on another XCD, behind another L2
-      const size_t row = (static_cast<size_t>(s) * a.Hq + hq) * a.Pmax + part;
+      const size_t row = (static_cast<size_t>(s) * a.Hq + hq) * a.Pmax + slot;
       st_agent(a.part_o + row * D + d, r);
       if (d == 0) {
         float* ml = reinterpret_cast<float*>(a.part_ml + row);
@@ -246,38 +270,50 @@ __device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
   }
 }
 
-// Start of a work item: read the context length and stage the partition's slice of the
-// block table in LDS.  The table loads do not depend on the length (the slice is cut at
-// max_blocks), so both are in flight together.  Entries the partition uses that lie outside
-// the pool are replaced by block 0 (every load stays inside the pool) and flag the item as
-// bad; entries past the context end are ignored.
+// Start of a work item: its token range [t0, t1), partial slot and members come with the
+// entry; read each member's number of partial results, the context length (for the bad-length
+// check of a sequence's own item) and stage the slice of the block table the range needs in
+// LDS.  The loads do not depend on each other, so they are in flight together.  A share-group
+// item reads its first member's table: over the group's range the members hold the same K/V.
+// Entries the range uses that lie outside the pool are replaced by block 0 (every load stays
+// inside the pool) and flag the item as bad.
 struct ItemRange {
-  int n, nparts, t0, t1, b0;
+  int t0, t1, b0, slot, nmem;
+  int mem[kGroupMembers], np[kGroupMembers];
   bool bad;
 };
 
 template <int B>
-__device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, int s, int part, int* s_tbl,
-                                                int* s_bad) {
-  constexpr int kPer = (kMaxPT / B + kNW * kWave - 1) / (kNW * kWave);
-  const int raw_n = a.ctx_lens[s];
-  const int b0 = part * (a.PT / B);
-  const int nb_max = min(a.PT / B, a.max_blocks - b0);
-  const int32_t* row = a.tables + static_cast<size_t>(s) * a.max_blocks + b0;
+__device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, const int4 e0, const int4 e1,
+                                                int* s_tbl, int* s_bad) {
+  constexpr int kTbl = kMaxPT / B + 1;  // a range may start inside a block
+  constexpr int kPer = (kTbl + kNW * kWave - 1) / (kNW * kWave);
+  ItemRange it;
+  it.t0 = e0.z;
+  it.t1 = e0.w;
+  it.slot = e0.y;
+  it.mem[0] = e1.x;
+  it.mem[1] = e1.y;
+  it.mem[2] = e1.z;
+  it.mem[3] = e1.w;
+  it.nmem = 1 + (e1.y >= 0) + (e1.z >= 0) + (e1.w >= 0);
+  const int s = e1.x;
+  const bool own = e0.x >= 0;
+  const int raw_n = own ? a.ctx_lens[s] : 1;
+  it.b0 = it.t0 / B;
+  int nb = it.t1 > it.t0 ? (it.t1 - 1) / B - it.b0 + 1 : 0;
+  nb = min(nb, a.max_blocks - it.b0);
+  const int32_t* row = a.tables + static_cast<size_t>(s) * a.max_blocks + it.b0;
   int ent[kPer];
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int i = threadIdx.x + r * kNW * kWave;
-    ent[r] = i < nb_max ? row[i] : 0;
+    ent[r] = i < nb ? row[i] : 0;
   }
-  ItemRange it;
-  bool bad_len;
-  it.n = eff_len(raw_n, a.len_cap, bad_len);
-  it.nparts = it.n > 0 ? (it.n + a.PT - 1) / a.PT : 1;
-  it.t0 = part * a.PT;
-  it.t1 = min(it.n, it.t0 + a.PT);
-  it.b0 = b0;
-  const int nb = it.t1 > it.t0 ? (it.t1 + B - 1) / B - b0 : 0;
+#pragma unroll
+  for (int k = 0; k < kGroupMembers; ++k) it.np[k] = it.mem[k] >= 0 ? a.nparts[it.mem[k]] : 0;
+  bool bad_len = false;
+  if (own) (void)eff_len(raw_n, a.len_cap, bad_len);
   if (threadIdx.x == 0) *s_bad = 0;
   __syncthreads();
   bool bad_ent = false;
@@ -328,8 +364,9 @@ __device__ __forceinline__ void for_each_item(const DecodeArgs& a, int* s_next, 
         claimed = true;
       }
     };
-    const int2 it = a.items[i / a.Hkv];
-    body(it.x, i % a.Hkv, it.y, claim);
+    const int e = i / a.Hkv;
+    const int4 e0 = a.items[2 * e], e1 = a.items[2 * e + 1];
+    body(e0, e1, i % a.Hkv, claim);
     claim();  // a body that had no tile for wave 0
     if (threadIdx.x == 0) *s_next = nxt;
     __syncthreads();
@@ -366,8 +403,8 @@ struct MfmaV {
 // KEEP: K/V loaded without the non-temporal hint (the plan saw blocks shared by several
 // sequences; their lines are read again by other items).
 template <int D, int B, bool KEEP, typename Claim>
-__device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, int part,
-                                          int* s_tbl, int* s_bad, float (*s_ml)[16][2],
+__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, const int4 e1,
+                                          int kvh, int* s_tbl, int* s_bad, float (*s_ml)[16][2],
                                           float (*s_o)[16][D], Claim&& claim) {
   constexpr int NST = D / 32, NNT = D / 16;
   const int lane = threadIdx.x & (kWave - 1), w = wave_id();
@@ -375,21 +412,24 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, i
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
   const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
 
-  // Q^T operand: column = head r16 (zero for padded heads), k = 8 dims per step.
+  // Q^T operand: column r16 = head r16 % G of member r16 / G (zero past the item's members),
+  // k = 8 dims per step.  A sequence's own item has one member; a share-group item up to 16 / G.
   bf16x8 qop[NST];
   {
-    const int h = r16 < a.G ? r16 : 0;
+    const int j = r16 / a.G, h = r16 - j * a.G;
+    const int mj = j == 0 ? e1.x : j == 1 ? e1.y : j == 2 ? e1.z : j == 3 ? e1.w : -1;
+    const bool live = mj >= 0;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<size_t>(s) * a.Hq + kvh * a.G + h) * D;
+                         (static_cast<size_t>(live ? mj : e1.x) * a.Hq + kvh * a.G + (live ? h : 0)) * D;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (4 * st + gp));
-      if (r16 >= a.G) u = make_uint4(0, 0, 0, 0);
+      if (!live) u = make_uint4(0, 0, 0, 0);
       qop[st] = __builtin_bit_cast(bf16x8, u);
     }
   }
 
-  const ItemRange rg = begin_item<B>(a, s, part, s_tbl, s_bad);
+  const ItemRange rg = begin_item<B>(a, e0, e1, s_tbl, s_bad);
   const int t0 = rg.t0, t1 = rg.t1, b0 = rg.b0;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -540,30 +580,33 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int kvh, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_o[w][r16][16 * ni + 4 * gp + i] = o[ni][i];
   __syncthreads();
-  finish_partition<uint16_t, D, 16>(a, s, kvh, part, rg.nparts, rg.bad, s_ml, s_o);
-  merge_if_last<uint16_t, D>(a, s, kvh, rg.nparts);
+  finish_partition<uint16_t, D, 16>(a, rg.mem, rg.np, rg.nmem * a.G, kvh, rg.slot, rg.bad, s_ml, s_o);
+  for (int k = 0; k < rg.nmem; ++k)
+    merge_if_last<uint16_t, D>(a, pick4(rg.mem, k), kvh, pick4(rg.np, k));
 }
 
 template <int D, int B>
 __global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(kMfmaWaves)))
 void decode_mfma_kernel(DecodeArgs a) {
-  a.PT = a.queue[kPtSlot];                        // the plan's choice
-  a.Pmax = (a.len_cap + a.PT - 1) / a.PT;  // partial results packed for it
-  __shared__ int s_tbl[kMaxPT / B];
+  a.PT = a.queue[kPtSlot];      // the plan's choice
+  a.Pmax = a.queue[kPmaxSlot];  // partial results packed for it
+  // s_o doubles as each wave's K staging slot, read and written in 16-byte vectors: keep it
+  // (and the rest) 16-byte aligned whatever the table slice's size
+  __shared__ __attribute__((aligned(16))) int s_tbl[kMaxPT / B + 1];
   __shared__ int s_bad, s_next;
-  __shared__ float s_ml[kNW][16][2];
-  __shared__ float s_o[kNW][16][D];
+  __shared__ __attribute__((aligned(16))) float s_ml[kNW][16][2];
+  __shared__ __attribute__((aligned(16))) float s_o[kNW][16][D];
   // A batch whose sequences share prefix blocks (the plan's sharing test, which also picks
   // the per-XCD queues) keeps K/V lines in cache: each shared line is read by many items of
   // the same kv-head on one XCD, and a non-temporal load marks it to leave first.  Shared-
   // prefix batches: 0.1975 -> 0.183 ms (B = 16), 0.205 -> 0.190 ms (B = 32); on a batch with
   // no sharing the hint is worth 11% (Llama-3-70B-shaped batch 0.296 vs 0.33 ms without it).
   const bool keep = a.queue[1] != 0;
-  for_each_item(a, &s_next, [&](int s, int kvh, int part, auto&& claim) {
+  for_each_item(a, &s_next, [&](const int4 e0, const int4 e1, int kvh, auto&& claim) {
     if (keep)
-      mfma_item<D, B, true>(a, s, kvh, part, s_tbl, &s_bad, s_ml, s_o, claim);
+      mfma_item<D, B, true>(a, e0, e1, kvh, s_tbl, &s_bad, s_ml, s_o, claim);
     else
-      mfma_item<D, B, false>(a, s, kvh, part, s_tbl, &s_bad, s_ml, s_o, claim);
+      mfma_item<D, B, false>(a, e0, e1, kvh, s_tbl, &s_bad, s_ml, s_o, claim);
   });
 }
 
@@ -577,9 +620,10 @@ void decode_mfma_kernel(DecodeArgs a) {
 // are broadcast through a per-wave LDS slot.
 // ---------------------------------------------------------------------------------------
 template <typename T, int D, int B, int G, int LPT, int TPR>
-__device__ __forceinline__ void valu_item(const DecodeArgs& a, int s, int kvh, int part,
-                                          int* s_tbl, int* s_bad, float (*s_ml)[G][2],
+__device__ __forceinline__ void valu_item(const DecodeArgs& a, const int4 e0, const int4 e1,
+                                          int kvh, int* s_tbl, int* s_bad, float (*s_ml)[G][2],
                                           float (*s_o)[G][D], float (*s_p)[G][TPR]) {
+  const int s = e1.x;  // no share groups on this kernel: always the sequence's own item
   constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte load
   constexpr int CPL = D / LPT / VEC;    // 16-byte chunks of a key row per lane
   constexpr int DPL = CPL * VEC;        // dims per lane in QK
@@ -611,7 +655,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, int s, int kvh, i
       }
   }
 
-  const ItemRange rg = begin_item<B>(a, s, part, s_tbl, s_bad);
+  const ItemRange rg = begin_item<B>(a, e0, e1, s_tbl, s_bad);
   const int t0 = rg.t0, t1 = rg.t1, b0 = rg.b0;
 
   float m_run[G], l_run[G], acc[G][DV];
@@ -721,23 +765,23 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, int s, int kvh, i
     for (int e = 0; e < DV; ++e) s_o[w][h][lane + kWave * e] = acc[h][e];
   }
   __syncthreads();
-  finish_partition<T, D, G>(a, s, kvh, part, rg.nparts, rg.bad, s_ml, s_o);
-  merge_if_last<T, D>(a, s, kvh, rg.nparts);
+  finish_partition<T, D, G>(a, rg.mem, rg.np, G, kvh, rg.slot, rg.bad, s_ml, s_o);
+  merge_if_last<T, D>(a, s, kvh, rg.np[0]);
 }
 
 template <typename T, int D, int B, int G, int LPT>
 __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) {
-  a.PT = a.queue[kPtSlot];                        // the plan's choice
-  a.Pmax = (a.len_cap + a.PT - 1) / a.PT;  // partial results packed for it
+  a.PT = a.queue[kPtSlot];      // the plan's choice
+  a.Pmax = a.queue[kPmaxSlot];  // partial results packed for it
   constexpr int TPR = kWave / LPT;      // tokens per round
-  __shared__ int s_tbl[kMaxPT / B];
+  __shared__ __attribute__((aligned(16))) int s_tbl[kMaxPT / B + 1];
   __shared__ int s_bad, s_next;
-  __shared__ float s_ml[kNW][G][2];
-  __shared__ float s_o[kNW][G][D];
+  __shared__ __attribute__((aligned(16))) float s_ml[kNW][G][2];
+  __shared__ __attribute__((aligned(16))) float s_o[kNW][G][D];
   __shared__ __attribute__((aligned(16))) float s_p[kNW][G][TPR];  // weights of the round
-  for_each_item(a, &s_next, [&](int s, int kvh, int part, auto&& claim) {
+  for_each_item(a, &s_next, [&](const int4 e0, const int4 e1, int kvh, auto&& claim) {
     claim();  // at the start: these items are short
-    valu_item<T, D, B, G, LPT, TPR>(a, s, kvh, part, s_tbl, &s_bad, s_ml, s_o, s_p);
+    valu_item<T, D, B, G, LPT, TPR>(a, e0, e1, kvh, s_tbl, &s_bad, s_ml, s_o, s_p);
   });
 }
 
@@ -767,6 +811,15 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 
 // lens_src: the lengths to plan with (system-scope loads when `sys`: page-locked host memory);
 // lens_out: when not null, receives a copy of them for the decode kernel (a.ctx_lens).
+//
+// Share groups (a.gmem > 0, a.ngroups > 0, S <= kPlanKeep): group g names up to kGroupMembers
+// sequences that hold the same K/V at positions [0, L).  The plan accepts a member only if its
+// index is in range, its length is valid and no earlier group took it (first come, by an LDS
+// claim); a group keeps L' = min(L, its members' lengths) rounded down to a multiple of 32, and
+// is dropped (its members then plan alone) with fewer than two members or L' < 32.  Each
+// accepted group's range is split into partitions of PT tokens, and each partition into items
+// of a.gmem members; a member's own items cover [L', n) in partitions of PT from L'.  Its
+// partial results are the group's partitions first (slots 0 .. ceil(L'/PT) - 1), then its own.
 __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src,
                           int32_t* lens_out, bool sys) {
   constexpr int kPlanWaves = kPlanThreads / kWave;
@@ -774,33 +827,33 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   __shared__ int s_base[kMaxBuckets];  // first entry of each bucket (then a cursor)
   __shared__ int s_wave[kPlanWaves];
   __shared__ int s_full;               // full partitions counted so far
-  __shared__ int s_len[kPlanKeep];     // pass 1's lengths of the first kPlanKeep sequences
+  __shared__ int s_len[kPlanKeep];     // pass 0's lengths of the first kPlanKeep sequences
+  __shared__ int s_grp[kPlanKeep];     // group that took the sequence (claims), then its L'
   __shared__ int s_first[kShareSlots];  // open-addressing set of first blocks seen
   __shared__ int s_dups;                // sequences whose first block another one also has
-  __shared__ unsigned long long s_total;  // sum of the context lengths
-  __shared__ int s_pt;
+  __shared__ unsigned long long s_total;  // tokens the items will read
+  __shared__ int s_pt, s_pmax;
+  const bool groups_on = a.gmem > 0 && a.ngroups > 0 && a.S <= kPlanKeep;
+  const int ngroups = groups_on ? a.ngroups : 0;
   for (int i = threadIdx.x; i < kShareSlots; i += kPlanThreads) s_first[i] = -1;
+  for (int i = threadIdx.x; i < kPlanKeep; i += kPlanThreads) s_grp[i] = -1;
   if (threadIdx.x == 0) {
     s_full = 0;
     s_dups = 0;
     s_total = 0;
   }
-  if (a.Pmax > 1)
-    for (int i = threadIdx.x; i < a.S * a.Hkv; i += kPlanThreads) a.done[i] = 0;
+  for (int i = threadIdx.x; i < a.S * a.Hkv; i += kPlanThreads) a.done[i] = 0;
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   __syncthreads();
-  // Pass 0, one sequence per thread per round: lengths (kept in LDS, copied to lens_out), the
-  // sharing test and the total.
-  unsigned long long my_total = 0;
+  // Pass 0, one sequence per thread per round: lengths (kept in LDS, copied to lens_out) and
+  // the sharing test.
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
-    bool bad;
     // The table entry is requested first: it then travels with the length, which may have to
     // come over the bus.
     const int blk = a.tables[static_cast<size_t>(s) * a.max_blocks];
     const int raw = ld_step(lens_src + s, sys);
     if (lens_out) lens_out[s] = raw;
     if (s < kPlanKeep) s_len[s] = raw;
-    my_total += static_cast<unsigned long long>(eff_len(raw, a.len_cap, bad));
     // Prefix sharing shows as one physical first block in several tables.  A set in LDS
     // (bounded probing, so a full set only undercounts) counts the repeats.
     if (blk >= 0) {
@@ -815,6 +868,58 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
         h = (h + 1) & (kShareSlots - 1);
       }
     }
+  }
+  __syncthreads();
+  // Share groups: claim members, then record each group as accepted (L' = 0: dropped).
+  for (int g = threadIdx.x; g < ngroups; g += kPlanThreads) {
+    const int32_t* rec = a.groups + static_cast<size_t>(g) * kGroupRec;
+    const int L = rec[0];
+    // accepted members, compacted (scalars: a runtime index into a local array would put it
+    // in scratch memory)
+    int m0 = -1, m1 = -1, m2 = -1, m3 = -1, nm = 0, nmin = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < kGroupMembers; ++k) {
+      const int m = rec[1 + k];
+      if (m < 0 || m >= a.S) continue;
+      bool bad;
+      const int n = eff_len(s_len[m], a.len_cap, bad);
+      if (bad || atomicCAS(&s_grp[m], -1, g) != -1) continue;
+      if (nm == 0) m0 = m;
+      else if (nm == 1) m1 = m;
+      else if (nm == 2) m2 = m;
+      else m3 = m;
+      ++nm;
+      nmin = min(nmin, n);
+    }
+    int Lg = nm >= 2 && L > 0 ? (min(L, nmin) & ~31) : 0;
+    int* v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
+    v[0] = Lg;
+    v[1] = m0;
+    v[2] = m1;
+    v[3] = m2;
+    v[4] = m3;
+    v[1 + kGroupMembers] = nm;
+  }
+  __syncthreads();
+  // Each claimed sequence's range base: its group's L' (0 for a dropped group); the total of
+  // tokens the items read (a group's range once per item of gmem members).
+  unsigned long long my_total = 0;
+  for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
+    bool bad;
+    const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
+    const int n = eff_len(raw, a.len_cap, bad);
+    int base = 0;
+    if (groups_on) {
+      const int g = s_grp[s];
+      base = g >= 0 ? a.vgroups[static_cast<size_t>(g) * kVGroupRec] : 0;
+      s_grp[s] = base;
+    }
+    my_total += static_cast<unsigned long long>(bad ? 0 : n - base);
+  }
+  for (int g = threadIdx.x; g < ngroups; g += kPlanThreads) {
+    const int* v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
+    const int chunks = (v[1 + kGroupMembers] + a.gmem - 1) / a.gmem;
+    my_total += static_cast<unsigned long long>(v[0]) * static_cast<unsigned long long>(chunks);
   }
   if (my_total) atomicAdd(&s_total, my_total);
   __syncthreads();
@@ -835,6 +940,9 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
         }
     }
     s_pt = pt;
+    // a member's group partitions and own partitions together are at most one more than an
+    // unsplit range's
+    s_pmax = (a.len_cap + pt - 1) / pt + (groups_on ? 1 : 0);
   }
   __syncthreads();
   const int PT = s_pt;
@@ -842,24 +950,58 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
   __syncthreads();
   // Pass 1: full partitions get consecutive entries from a block-wide prefix sum; partial ones
-  // are counted per bucket.
-  for (int s0 = 0; s0 < a.S; s0 += kPlanThreads) {
-    const int s = s0 + threadIdx.x;
-    int n = 0;
+  // are counted per bucket.  Round r: thread t takes sequence r * kPlanThreads + t and group
+  // r * kPlanThreads + t.
+  const int rounds = (max(a.S, ngroups) + kPlanThreads - 1) / kPlanThreads;
+  for (int r = 0; r < rounds; ++r) {
+    const int s = r * kPlanThreads + threadIdx.x, g = s;
+    int full_s = 0, full_g = 0, chunks = 0, n = 0, base = 0, npre = 0, nm = 0, Lg = 0;
+    bool bad = false;
     if (s < a.S) {
-      bool bad;
       const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
       n = eff_len(raw, a.len_cap, bad);
+      base = groups_on ? s_grp[s] : 0;
+      npre = (base + PT - 1) / PT;
+      if (!bad) full_s = (n - base) / PT;
+      const int rem = bad ? 0 : n - base - full_s * PT;
+      a.nparts[s] = bad ? 1 : npre + full_s + (rem > 0);
+      if (bad || rem > 0) atomicAdd(&s_cnt[(rem + 31) / 32], 1);
     }
-    const int full = s < a.S ? n / PT : 0, rem = n - full * PT;
-    const int incl = wave_inclusive_sum(full);
+    const int* v = nullptr;
+    if (g < ngroups) {
+      v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
+      Lg = v[0];
+      nm = v[1 + kGroupMembers];
+      if (Lg > 0) {
+        chunks = (nm + a.gmem - 1) / a.gmem;
+        full_g = Lg / PT;
+        const int rem = Lg - full_g * PT;
+        if (rem > 0) atomicAdd(&s_cnt[(rem + 31) / 32], chunks);
+      }
+    }
+    const int mine = full_s + chunks * full_g;
+    const int incl = wave_inclusive_sum(mine);
     if (lane == kWave - 1) s_wave[w] = incl;
-    if (s < a.S && (rem > 0 || n == 0)) atomicAdd(&s_cnt[(rem + 31) / 32], 1);
     __syncthreads();
     int before = s_full;
-    for (int v = 0; v < w; ++v) before += s_wave[v];
-    const int f0 = before + incl - full;
-    for (int p = 0; p < full; ++p) a.items[f0 + p] = make_int2(s, p);
+    for (int u = 0; u < w; ++u) before += s_wave[u];
+    int e = before + incl - mine;
+    for (int q = 0; q < full_s; ++q, ++e) {
+      a.items[2 * e] = make_int4(s, npre + q, base + q * PT, base + (q + 1) * PT);
+      a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
+    }
+    for (int c = 0; c < chunks; ++c) {
+      int mm[kGroupMembers];
+#pragma unroll
+      for (int k = 0; k < kGroupMembers; ++k) {
+        const int j = c * a.gmem + k;
+        mm[k] = k < a.gmem && j < nm ? v[1 + j] : -1;
+      }
+      for (int p = 0; p < full_g; ++p, ++e) {
+        a.items[2 * e] = make_int4(-1 - g, p, p * PT, (p + 1) * PT);
+        a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
+      }
+    }
     __syncthreads();
     if (threadIdx.x == kPlanThreads - 1) s_full = before + incl;
     __syncthreads();
@@ -877,16 +1019,42 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       for (int x = 0; x < kXcd; ++x) a.queue[2 + x] = (grid - x + kXcd - 1) / kXcd;
       a.queue[2 + kXcd] = grid;
       a.queue[kPtSlot] = PT;
+      a.queue[kPmaxSlot] = s_pmax;
     }
   }
   __syncthreads();
-  // Pass 2: the partial partitions (each thread revisits the sequences it read in pass 1).
+  // Pass 2: the partial partitions (each thread revisits the sequences and groups of pass 1).
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
     bool bad;
     const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
     const int n = eff_len(raw, a.len_cap, bad);
-    const int full = n / PT, rem = n - full * PT;
-    if (rem > 0 || n == 0) a.items[atomicAdd(&s_base[(rem + 31) / 32], 1)] = make_int2(s, full);
+    const int base = groups_on ? s_grp[s] : 0;
+    const int full = bad ? 0 : (n - base) / PT, rem = bad ? 0 : n - base - full * PT;
+    if (bad || rem > 0) {
+      const int e = atomicAdd(&s_base[(rem + 31) / 32], 1);
+      const int t0 = bad ? 0 : base + full * PT;
+      a.items[2 * e] = make_int4(s, bad ? 0 : (base + PT - 1) / PT + full, t0, bad ? 0 : n);
+      a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
+    }
+  }
+  for (int g = threadIdx.x; g < ngroups; g += kPlanThreads) {
+    const int* v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
+    const int Lg = v[0], nm = v[1 + kGroupMembers];
+    if (Lg <= 0) continue;
+    const int full = Lg / PT, rem = Lg - full * PT;
+    if (rem == 0) continue;
+    const int chunks = (nm + a.gmem - 1) / a.gmem;
+    for (int c = 0; c < chunks; ++c) {
+      int mm[kGroupMembers];
+#pragma unroll
+      for (int k = 0; k < kGroupMembers; ++k) {
+        const int j = c * a.gmem + k;
+        mm[k] = k < a.gmem && j < nm ? v[1 + j] : -1;
+      }
+      const int e = atomicAdd(&s_base[(rem + 31) / 32], 1);
+      a.items[2 * e] = make_int4(-1 - g, full, full * PT, Lg);
+      a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
+    }
   }
 }
 
@@ -916,10 +1084,12 @@ __global__ __launch_bounds__(kPlanThreads) void step_prologue_kernel(CacheWriteA
 // Host side.
 // ---------------------------------------------------------------------------------------
 
-// Workspace: [queue header | work list | partition (m, l) | partition outputs].  The work
-// list is sized for Hq heads (an upper bound of Hkv) so that the size query needs no Hkv.
+// Workspace: [queue header | work list | merge counters | partial-result counts | accepted
+// share groups | partition (m, l) | partition outputs].  Counters are sized for Hq heads (an
+// upper bound of Hkv), so the size query needs no Hkv.  Pmax is the number of partial-result
+// slots per (sequence, head): one more than an unsplit context needs, for the share groups.
 struct WsLayout {
-  size_t items, done, ml, o, total;
+  size_t items, done, nparts, vgroups, ml, o, total;
 };
 
 static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -927,20 +1097,26 @@ static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 static WsLayout ws_layout(int S, int Hq, int D, int Pmax) {
   WsLayout L{};
   size_t off = 256;
-  L.items = off;
-  off += round256(static_cast<size_t>(S) * Pmax * Hq * sizeof(int2));
-  if (Pmax > 1) {
-    const size_t rows = static_cast<size_t>(S) * Hq * Pmax;
-    L.done = off;
-    off += round256(static_cast<size_t>(S) * Hq * sizeof(int));
-    L.ml = off;
-    off += round256(rows * sizeof(float2));
-    L.o = off;
-    off += rows * D * sizeof(float);
-  }
+  L.items = off;  // at most S * Pmax entries of two int4
+  off += round256(static_cast<size_t>(S) * Pmax * 2 * sizeof(int4));
+  L.done = off;
+  off += round256(static_cast<size_t>(S) * Hq * sizeof(int));
+  L.nparts = off;
+  off += round256(static_cast<size_t>(S) * sizeof(int));
+  L.vgroups = off;
+  off += round256(static_cast<size_t>(S) * kVGroupRec * sizeof(int));
+  const size_t rows = static_cast<size_t>(S) * Hq * Pmax;
+  L.ml = off;
+  off += round256(rows * sizeof(float2));
+  L.o = off;
+  off += rows * D * sizeof(float);
   L.total = off;
   return L;
 }
+
+// Partial-result slots per (sequence, head) the workspace holds for contexts of at most
+// max_ctx tokens in partitions of at least pt tokens (see WsLayout).
+static int ws_pmax(int max_ctx, int pt) { return (max_ctx > 0 ? (max_ctx + pt - 1) / pt : 1) + 1; }
 
 // Workgroups of kernel k that fit on the device at once (the persistent grid size).
 static int resident_grid(const void* k, int threads, size_t lds_dynamic) {
@@ -1000,22 +1176,26 @@ static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void*
                 "(bf16: 1..16, f32: 1, 2, 4, 8)", a.G, dtype);
   const int cap = resident_grid(reinterpret_cast<const void*>(k), kNW * kWave, 0);
   if (cap <= 0) return fail(PA_ERR_HIP, "pa_decode: cannot query the device's compute units");
+  // Share groups run on the matrix-core kernel only: a group item puts 16 / G sequences' heads
+  // in the 16 columns of the Q^T operand (at most kGroupMembers).
+  a.gmem = (k == decode_mfma_kernel<D, B>) ? min(kGroupMembers, 16 / a.G) : 0;
+  if (a.gmem <= 1) a.gmem = 0;
   // partition_tokens = 0: the plan picks the length from the batch (at least kMinAutoPT, which
   // bounds the partitions per sequence; the size query assumed the same).
   a.PT = partition_tokens;
   const int pt_min = partition_tokens ? partition_tokens : kMinAutoPT;
-  a.Pmax = (a.len_cap + pt_min - 1) / pt_min;
+  a.Pmax = ws_pmax(a.len_cap, pt_min);
   if (static_cast<int64_t>(a.S) * a.Pmax * a.Hq >= (int64_t(1) << 31))
     return fail(PA_ERR_INVALID_ARG, "pa_decode: S * partitions * Hq too large");
   const WsLayout L = ws_layout(a.S, a.Hq, D, a.Pmax);  // fits: PT >= the size query's choice
   char* ws = static_cast<char*>(workspace);
   a.queue = reinterpret_cast<int*>(ws);
-  a.items = reinterpret_cast<int2*>(ws + L.items);
-  if (a.Pmax > 1) {
-    a.done = reinterpret_cast<int*>(ws + L.done);
-    a.part_ml = reinterpret_cast<float2*>(ws + L.ml);
-    a.part_o = reinterpret_cast<float*>(ws + L.o);
-  }
+  a.items = reinterpret_cast<int4*>(ws + L.items);
+  a.done = reinterpret_cast<int*>(ws + L.done);
+  a.nparts = reinterpret_cast<int*>(ws + L.nparts);
+  a.vgroups = reinterpret_cast<int*>(ws + L.vgroups);
+  a.part_ml = reinterpret_cast<float2*>(ws + L.ml);
+  a.part_o = reinterpret_cast<float*>(ws + L.o);
 
   const int64_t max_items = static_cast<int64_t>(a.S) * a.Pmax * a.Hkv;
   const int grid = static_cast<int>(max_items < cap ? max_items : cap);
@@ -1048,7 +1228,7 @@ extern "C" pa_status pa_decode_workspace_size(int32_t S, int32_t Hq, int32_t D, 
   if (partition_tokens != 0 && (partition_tokens % 32 || partition_tokens < 32 || partition_tokens > kMaxPT))
     return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_size: partition_tokens %d", partition_tokens);
   const int pt = partition_tokens ? partition_tokens : kMinAutoPT;
-  const int Pmax = max_ctx_len > 0 ? (max_ctx_len + pt - 1) / pt : 1;
+  const int Pmax = ws_pmax(max_ctx_len, pt);
   if (static_cast<int64_t>(S) * Pmax * Hq >= (int64_t(1) << 31))
     return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_size: S * partitions * Hq too large");
   *bytes = ws_layout(S, Hq, D, Pmax).total;
@@ -1090,7 +1270,7 @@ static pa_status decode_setup(const char* who, void* out, const void* q, const v
   // The workspace must hold the layout for the shortest partition this call may pick (the
   // size pa_decode_workspace_size reports), checked before anything touches the device.
   const int pt_min = partition_tokens ? partition_tokens : kMinAutoPT;
-  const int pmax_min = (max_ctx_len + pt_min - 1) / pt_min;
+  const int pmax_min = ws_pmax(max_ctx_len, pt_min);
   if (static_cast<int64_t>(S) * pmax_min * Hq >= (int64_t(1) << 31))
     return fail(PA_ERR_INVALID_ARG, "%s: S * partitions * Hq too large", who);
   const size_t need = ws_layout(S, Hq, D, pmax_min).total;
@@ -1118,9 +1298,8 @@ static pa_status decode_setup(const char* who, void* out, const void* q, const v
   return ok();
 }
 
-static pa_status dispatch(const DecodeArgs& a, int D, int B, int32_t dtype, int pt, void* w,
-                          size_t wb, void* stream, const CacheWriteArgs* wr,
-                          int32_t* lens_out = nullptr) {
+static pa_status dispatch(DecodeArgs a, int D, int B, int32_t dtype, int pt, void* w, size_t wb,
+                          void* stream, const CacheWriteArgs* wr, int32_t* lens_out = nullptr) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 64)
     return B == 16 ? launch<64, 16>(a, dtype, pt, w, wb, st, wr, lens_out)
@@ -1131,19 +1310,94 @@ static pa_status dispatch(const DecodeArgs& a, int D, int B, int32_t dtype, int 
                  : launch<128, 64>(a, dtype, pt, w, wb, st, wr, lens_out);
 }
 
+// Checks the share groups of pa_decode_shared / pa_decode_step_shared visible on the host and
+// adds them to the arguments.
+static pa_status set_groups(const char* who, DecodeArgs* a, const int32_t* groups,
+                            int32_t n_groups) {
+  if (n_groups < 0 || n_groups > a->S)
+    return fail(PA_ERR_INVALID_ARG, "%s: n_groups %d outside [0, S = %d]", who, n_groups, a->S);
+  if (n_groups == 0) return ok();
+  if (!groups) return fail(PA_ERR_INVALID_ARG, "%s: groups is NULL", who);
+  bool host = false;
+  if (pa_status st = memory_kind(who, "groups", groups, &host)) return st;
+  if (host) return fail(PA_ERR_INVALID_ARG, "%s: groups must be device memory", who);
+  a->groups = groups;
+  a->ngroups = n_groups;
+  return ok();
+}
+
+static pa_status decode_call(const char* who, void* out, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables,
+                             const int32_t* ctx_lens, int32_t S, int32_t Hq, int32_t Hkv,
+                             int32_t D, int32_t B, int32_t num_blocks, int32_t max_blocks,
+                             int32_t max_ctx_len, float scale, int32_t dtype,
+                             int32_t partition_tokens, const int32_t* groups, int32_t n_groups,
+                             void* workspace, size_t workspace_bytes_in, void* stream) {
+  DecodeArgs a;
+  if (pa_status st = decode_setup(who, out, q, k_cache, v_cache, block_tables, ctx_lens, S, Hq,
+                                  Hkv, D, B, num_blocks, max_blocks, max_ctx_len, scale, dtype,
+                                  partition_tokens, workspace, workspace_bytes_in, &a))
+    return st;
+  if (S == 0) return ok();
+  if (pa_status st = set_groups(who, &a, groups, n_groups)) return st;
+  return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, nullptr);
+}
+
+static pa_status step_call(const char* who, void* out, const void* q, const void* key,
+                           const void* value, void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int32_t* block_tables, int32_t* ctx_lens,
+                           const int32_t* new_ctx_lens, int32_t S, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t B, int32_t num_blocks, int32_t max_blocks,
+                           int32_t max_ctx_len, float scale, int32_t dtype,
+                           int32_t partition_tokens, const int32_t* groups, int32_t n_groups,
+                           void* workspace, size_t workspace_bytes_in, void* stream) {
+  DecodeArgs a;
+  if (pa_status st = decode_setup(who, out, q, k_cache, v_cache, block_tables, ctx_lens, S, Hq,
+                                  Hkv, D, B, num_blocks, max_blocks, max_ctx_len, scale, dtype,
+                                  partition_tokens, workspace, workspace_bytes_in, &a))
+    return st;
+  if (S == 0) return ok();
+  if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned16(key) || !aligned16(value))
+    return fail(PA_ERR_INVALID_ARG, "%s: key and value must be 16-byte aligned", who);
+  if (pa_status st = set_groups(who, &a, groups, n_groups)) return st;
+  if (new_ctx_lens == ctx_lens) new_ctx_lens = nullptr;
+  bool host_slots = false, host_lens = false;
+  if (pa_status st = memory_kind(who, "slot_mapping", slot_mapping, &host_slots)) return st;
+  if (new_ctx_lens)
+    if (pa_status st = memory_kind(who, "new_ctx_lens", new_ctx_lens, &host_lens)) return st;
+  // The write's table patch and the plan read the step's lengths from their source; the decode
+  // kernel reads the device copy the plan leaves in ctx_lens.
+  CacheWriteArgs wr = make_cache_write_args(
+      key, value, k_cache, v_cache, slot_mapping, S, Hkv, D, B, num_blocks, dtype,
+      TablePatch{block_tables, new_ctx_lens ? new_ctx_lens : ctx_lens, 1, max_blocks});
+  wr.sys = host_slots || host_lens;
+  return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, &wr,
+                  new_ctx_lens ? ctx_lens : nullptr);
+}
+
 extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* ctx_lens, int32_t S,
                                int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
                                int32_t max_blocks, int32_t max_ctx_len, float scale, int32_t dtype,
                                int32_t partition_tokens, void* workspace, size_t workspace_bytes_in,
                                void* stream) {
-  DecodeArgs a;
-  if (pa_status st = decode_setup("pa_decode", out, q, k_cache, v_cache, block_tables, ctx_lens, S,
-                                  Hq, Hkv, D, B, num_blocks, max_blocks, max_ctx_len, scale, dtype,
-                                  partition_tokens, workspace, workspace_bytes_in, &a))
-    return st;
-  if (S == 0) return ok();
-  return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, nullptr);
+  return decode_call("pa_decode", out, q, k_cache, v_cache, block_tables, ctx_lens, S, Hq, Hkv, D,
+                     B, num_blocks, max_blocks, max_ctx_len, scale, dtype, partition_tokens,
+                     nullptr, 0, workspace, workspace_bytes_in, stream);
+}
+
+extern "C" pa_status pa_decode_shared(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* ctx_lens, int32_t S, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t B, int32_t num_blocks, int32_t max_blocks,
+                                      int32_t max_ctx_len, float scale, int32_t dtype,
+                                      int32_t partition_tokens, const int32_t* groups,
+                                      int32_t n_groups, void* workspace,
+                                      size_t workspace_bytes_in, void* stream) {
+  return decode_call("pa_decode_shared", out, q, k_cache, v_cache, block_tables, ctx_lens, S, Hq,
+                     Hkv, D, B, num_blocks, max_blocks, max_ctx_len, scale, dtype,
+                     partition_tokens, groups, n_groups, workspace, workspace_bytes_in, stream);
 }
 
 extern "C" pa_status pa_decode_step(void* out, const void* q, const void* key, const void* value,
@@ -1154,30 +1408,26 @@ extern "C" pa_status pa_decode_step(void* out, const void* q, const void* key, c
                                     int32_t max_blocks, int32_t max_ctx_len, float scale,
                                     int32_t dtype, int32_t partition_tokens, void* workspace,
                                     size_t workspace_bytes_in, void* stream) {
-  DecodeArgs a;
-  if (pa_status st = decode_setup("pa_decode_step", out, q, k_cache, v_cache, block_tables, ctx_lens,
-                                  S, Hq, Hkv, D, B, num_blocks, max_blocks, max_ctx_len, scale,
-                                  dtype, partition_tokens, workspace, workspace_bytes_in, &a))
-    return st;
-  if (S == 0) return ok();
-  if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "pa_decode_step: NULL pointer");
-  if (!aligned16(key) || !aligned16(value))
-    return fail(PA_ERR_INVALID_ARG, "pa_decode_step: key and value must be 16-byte aligned");
-  if (new_ctx_lens == ctx_lens) new_ctx_lens = nullptr;
-  bool host_slots = false, host_lens = false;
-  if (pa_status st = memory_kind("pa_decode_step", "slot_mapping", slot_mapping, &host_slots))
-    return st;
-  if (new_ctx_lens)
-    if (pa_status st = memory_kind("pa_decode_step", "new_ctx_lens", new_ctx_lens, &host_lens))
-      return st;
-  // The write's table patch and the plan read the step's lengths from their source; the decode
-  // kernel reads the device copy the plan leaves in ctx_lens.
-  CacheWriteArgs wr = make_cache_write_args(
-      key, value, k_cache, v_cache, slot_mapping, S, Hkv, D, B, num_blocks, dtype,
-      TablePatch{block_tables, new_ctx_lens ? new_ctx_lens : ctx_lens, 1, max_blocks});
-  wr.sys = host_slots || host_lens;
-  return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, &wr,
-                  new_ctx_lens ? ctx_lens : nullptr);
+  return step_call("pa_decode_step", out, q, key, value, k_cache, v_cache, slot_mapping,
+                   block_tables, ctx_lens, new_ctx_lens, S, Hq, Hkv, D, B, num_blocks, max_blocks,
+                   max_ctx_len, scale, dtype, partition_tokens, nullptr, 0, workspace,
+                   workspace_bytes_in, stream);
+}
+
+extern "C" pa_status pa_decode_step_shared(void* out, const void* q, const void* key,
+                                           const void* value, void* k_cache, void* v_cache,
+                                           const int32_t* slot_mapping, int32_t* block_tables,
+                                           int32_t* ctx_lens, const int32_t* new_ctx_lens,
+                                           int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                           int32_t B, int32_t num_blocks, int32_t max_blocks,
+                                           int32_t max_ctx_len, float scale, int32_t dtype,
+                                           int32_t partition_tokens, const int32_t* groups,
+                                           int32_t n_groups, void* workspace,
+                                           size_t workspace_bytes_in, void* stream) {
+  return step_call("pa_decode_step_shared", out, q, key, value, k_cache, v_cache, slot_mapping,
+                   block_tables, ctx_lens, new_ctx_lens, S, Hq, Hkv, D, B, num_blocks, max_blocks,
+                   max_ctx_len, scale, dtype, partition_tokens, groups, n_groups, workspace,
+                   workspace_bytes_in, stream);
 }
 
 // ---------------------------------------------------------------------------------------

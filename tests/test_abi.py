@@ -86,11 +86,13 @@ def test_device_calls_reject_bad_arguments_before_launch(libpa):
 
 
 def test_workspace_size(libpa):
-    one = libpa.pa_decode_workspace_size(4, 4, 64, 100, 128)            # one partition: work list
-    four = libpa.pa_decode_workspace_size(4, 4, 64, 100, 32)            # 4 partitions: + partials
+    # partial-result slots per (sequence, head): ceil(max_ctx / partition) + 1 (the extra slot is
+    # a share group's partition); each slot holds 64 outputs + max + sum in fp32
+    one = libpa.pa_decode_workspace_size(4, 4, 64, 100, 128)            # 1 + 1 slots
+    four = libpa.pa_decode_workspace_size(4, 4, 64, 100, 32)            # 4 + 1 slots
     assert 0 < one < four
-    # partials: 4 seqs x 4 heads x 4 partitions x (64 outputs + max + sum) fp32
-    assert four - one >= 4 * 4 * 4 * (64 + 2) * 4
+    assert one >= 4 * 4 * 2 * (64 + 2) * 4
+    assert four - one >= 4 * 4 * 3 * (64 + 2) * 4
     assert libpa.pa_decode_workspace_size(4, 4, 64, 1000, 0) > 0        # automatic choice
     with pytest.raises(libpa.PaError):
         libpa.pa_decode_workspace_size(4, 4, 64, 100, 40)

@@ -118,7 +118,9 @@ class Mirror:
         return np.stack(self.rows[sid][0]), np.stack(self.rows[sid][1])
 
 
-def decode_and_check(m, ids, Hq, what):
+def decode_and_check(m, ids, Hq, what, groups=None):
+    """Decode the batch (pa_decode, or pa_decode_shared with the given share groups) and check
+    every sequence against the oracle on its logical rows, and the pools bit for bit."""
     lib = m.lib
     t, l = m.tables(ids)
     for i, sid in enumerate(ids):
@@ -128,8 +130,12 @@ def decode_and_check(m, ids, Hq, what):
     max_ctx = int(l.max())
     ws = torch.empty(max(16, lib.pa_decode_workspace_size(len(ids), Hq, m.D, max_ctx, 0)),
                      dtype=torch.uint8, device="cuda")
-    lib.pa_decode(out, q, m.kc, m.vc, torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(),
-                  max_ctx, m.D ** -0.5, 0, ws)
+    td, ld = torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda()
+    if groups is None:
+        lib.pa_decode(out, q, m.kc, m.vc, td, ld, max_ctx, m.D ** -0.5, 0, ws)
+    else:
+        lib.pa_decode_shared(out, q, m.kc, m.vc, td, ld, max_ctx, m.D ** -0.5,
+                             torch.from_numpy(np.ascontiguousarray(groups, np.int32)).cuda(), 0, ws)
     m.check_pools()
     got, qf = f64(out), f64(q)
     for i, sid in enumerate(ids):

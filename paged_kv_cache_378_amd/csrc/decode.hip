@@ -68,6 +68,9 @@ constexpr int kPmaxSlot = 12;     // queue[kPmaxSlot]: partial-result slots per 
 constexpr int kGroupMembers = 4;  // sequences a share group may name
 constexpr int kGroupRec = 1 + kGroupMembers;  // caller's record: tokens, members
 constexpr int kVGroupRec = 2 + kGroupMembers;  // validated record: tokens, members, count
+constexpr int kFuseTail = 256;    // a group member's own tokens past the group's range, up to
+                                  // this many, are read by the group's last item (no item of
+                                  // their own, no merge when the range is one partition)
 constexpr int kPlanThreads = 256;
 constexpr int kMaxBuckets = kMaxPT / 32 + 1;  // partial partitions bucketed by 32-token tiles
 constexpr int kPlanKeep = 2048;  // sequences whose lengths the plan keeps in LDS between passes
@@ -280,24 +283,32 @@ __device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
 struct ItemRange {
   int t0, t1, b0, slot, nmem;
   int mem[kGroupMembers], np[kGroupMembers];
+  int tail[kGroupMembers];  // fused tail of each member: its tokens [t1, t1 + tail)
   bool bad;
 };
 
+// Table entries staged for one member's fused tail (tokens t1 .. t1 + kFuseTail - 1).
+template <int B>
+constexpr int kTailTbl = kFuseTail / B + 1;
+
 template <int B>
 __device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, const int4 e0, const int4 e1,
-                                                int* s_tbl, int* s_bad) {
+                                                int* s_tbl, int* s_bad, int* s_tail) {
   constexpr int kTbl = kMaxPT / B + 1;  // a range may start inside a block
   constexpr int kPer = (kTbl + kNW * kWave - 1) / (kNW * kWave);
   ItemRange it;
   it.t0 = e0.z;
   it.t1 = e0.w;
   it.slot = e0.y;
-  it.mem[0] = e1.x;
-  it.mem[1] = e1.y;
-  it.mem[2] = e1.z;
-  it.mem[3] = e1.w;
+  // a member slot: the sequence in the low 16 bits, its fused tail length above (-1: none)
+  const int c4[kGroupMembers] = {e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+  for (int k = 0; k < kGroupMembers; ++k) {
+    it.mem[k] = c4[k] < 0 ? -1 : (c4[k] & 0xFFFF);
+    it.tail[k] = c4[k] < 0 ? 0 : (c4[k] >> 16);
+  }
   it.nmem = 1 + (e1.y >= 0) + (e1.z >= 0) + (e1.w >= 0);
-  const int s = e1.x;
+  const int s = it.mem[0];
   const bool own = e0.x >= 0;
   const int raw_n = own ? a.ctx_lens[s] : 1;
   it.b0 = it.t0 / B;
@@ -312,6 +323,18 @@ __device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, const int4 
   }
 #pragma unroll
   for (int k = 0; k < kGroupMembers; ++k) it.np[k] = it.mem[k] >= 0 ? a.nparts[it.mem[k]] : 0;
+  // fused tails: thread (j, i) loads entry i of member j's blocks from t1 on
+  constexpr int kTT = kTailTbl<B>;
+  const int tj = static_cast<int>(threadIdx.x) / kTT, ti = static_cast<int>(threadIdx.x) - tj * kTT;
+  int tent = -1;  // an entry the tail needs past the table row stays -1: block 0, output NaN
+  bool tneed = false;
+  if (s_tail && tj < kGroupMembers) {
+    const int tl = pick4(it.tail, tj);
+    const int cnt = tl > 0 ? (it.t1 + tl - 1) / B - it.t1 / B + 1 : 0;
+    tneed = ti < cnt;
+    if (tneed && it.t1 / B + ti < a.max_blocks)
+      tent = a.tables[static_cast<size_t>(pick4(it.mem, tj)) * a.max_blocks + it.t1 / B + ti];
+  }
   bool bad_len = false;
   if (own) (void)eff_len(raw_n, a.len_cap, bad_len);
   if (threadIdx.x == 0) *s_bad = 0;
@@ -328,6 +351,13 @@ __device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, const int4 
       }
       s_tbl[i] = p;
     }
+  }
+  if (tneed) {
+    if (tent < 0 || tent >= a.num_blocks) {
+      bad_ent = true;
+      tent = 0;
+    }
+    s_tail[tj * kTT + ti] = tent;
   }
   if (bad_ent) *s_bad = 1;
   __syncthreads();
@@ -404,8 +434,9 @@ struct MfmaV {
 // sequences; their lines are read again by other items).
 template <int D, int B, bool KEEP, typename Claim>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, const int4 e1,
-                                          int kvh, int* s_tbl, int* s_bad, float (*s_ml)[16][2],
-                                          float (*s_o)[16][D], Claim&& claim) {
+                                          int kvh, int* s_tbl, int* s_bad, int* s_tail,
+                                          float (*s_ml)[16][2], float (*s_o)[16][D],
+                                          Claim&& claim) {
   constexpr int NST = D / 32, NNT = D / 16;
   const int lane = threadIdx.x & (kWave - 1), w = wave_id();
   const int r16 = lane & 15, gp = lane >> 4;
@@ -417,10 +448,11 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
   bf16x8 qop[NST];
   {
     const int j = r16 / a.G, h = r16 - j * a.G;
-    const int mj = j == 0 ? e1.x : j == 1 ? e1.y : j == 2 ? e1.z : j == 3 ? e1.w : -1;
-    const bool live = mj >= 0;
+    const int cj = j == 0 ? e1.x : j == 1 ? e1.y : j == 2 ? e1.z : j == 3 ? e1.w : -1;
+    const bool live = cj >= 0;
+    const int mj = live ? (cj & 0xFFFF) : (e1.x & 0xFFFF);  // low 16 bits: the sequence
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<size_t>(live ? mj : e1.x) * a.Hq + kvh * a.G + (live ? h : 0)) * D;
+                         (static_cast<size_t>(mj) * a.Hq + kvh * a.G + (live ? h : 0)) * D;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (4 * st + gp));
@@ -429,8 +461,15 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
     }
   }
 
-  const ItemRange rg = begin_item<B>(a, e0, e1, s_tbl, s_bad);
+  const ItemRange rg = begin_item<B>(a, e0, e1, s_tbl, s_bad, s_tail);
   const int t0 = rg.t0, t1 = rg.t1, b0 = rg.b0;
+  // A segment of tokens [t0, t1) read through table entries tbl[] of logical blocks from b0 on:
+  // the item's range, or one member's fused tail.
+  struct Seg {
+    int t0, t1, b0;
+    const int* tbl;
+  };
+  const Seg main_seg{t0, t1, b0, s_tbl};
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[NNT];
@@ -447,12 +486,12 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
   using KT = MfmaK<D>;
   unsigned char* kstage = reinterpret_cast<unsigned char*>(&s_o[w][0][0]);
   static_assert(sizeof(s_o[0]) >= 32 * D * 2, "the wave's output slot holds a K tile");
-  auto load_k = [&](KT& kt, int tile) {
-    const int tt = t0 + 32 * tile;
+  auto load_k = [&](KT& kt, const Seg& sg, int tile) {
+    const int tt = sg.t0 + 32 * tile;
 #pragma unroll
     for (int i = 0; i < KT::NI; ++i) {
-      const int tok = min(tt + KT::TPI * i + lane / KT::CH, t1 - 1);
-      const int p = s_tbl[tok / B - b0];
+      const int tok = min(tt + KT::TPI * i + lane / KT::CH, sg.t1 - 1);
+      const int p = sg.tbl[tok / B - sg.b0];
       const uint16_t* kp = kc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride +
                            static_cast<size_t>(tok % B) * D;
       kt.raw[i] = KEEP ? ld_kv16_keep(kp + 8 * (lane % KT::CH)) : ld_kv16(kp + 8 * (lane % KT::CH));
@@ -478,9 +517,9 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
   };
   // V^T rows: lane (gp, r16) reads dim 16*ni + r16 at tokens 8*gp .. 8*gp+7 of the tile
   // (16 contiguous bytes of the transposed block).
-  auto load_v = [&](MfmaV<D>& vt, int tile) {
-    const int tv = min(t0 + 32 * tile + 8 * gp, (t1 - 1) & ~7);
-    const int p = s_tbl[tv / B - b0];
+  auto load_v = [&](MfmaV<D>& vt, const Seg& sg, int tile) {
+    const int tv = min(sg.t0 + 32 * tile + 8 * gp, (sg.t1 - 1) & ~7);
+    const int p = sg.tbl[tv / B - sg.b0];
     const uint16_t* vp = vc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride + (tv % B);
     // At B = 64 a V^T row is 128 bytes and a 32-token tile reads half of it; the other half is
     // another wave's tile, read at about the same time.  A non-temporal load lets the line go
@@ -493,12 +532,14 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
                                    : ld_kv16(vp + (16 * ni + r16) * B);
   };
 
-  // One tile: QK^T on kt, refill kt with tile `pf`, softmax, PV on vt, refill vt with `pf`.
-  auto step = [&](MfmaK<D>& kt, MfmaV<D>& vt, int tile, int pf) {
-    const int tt = t0 + 32 * tile;
-    const bool more = pf < ntiles;
+  // One tile of segment sg: QK^T on kt, refill kt with tile `pf` of segment nsg (when `more`),
+  // softmax, PV on vt, refill vt.  col_ok: this lane's column takes part (false for the other
+  // members' columns while a member's fused tail is read).
+  auto step = [&](MfmaK<D>& kt, MfmaV<D>& vt, const Seg& sg, int tile, bool col_ok,
+                  const Seg& nsg, int pf, bool more) {
+    const int tt = sg.t0 + 32 * tile;
     stage_k(kt);
-    if (more) load_k(kt, pf);  // the raw registers are free once staged
+    if (more) load_k(kt, nsg, pf);  // the raw registers are free once staged
     f32x4 sacc[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -511,26 +552,29 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
     }
 
     // lane (gp, r16): scores of head r16 for tokens tt + 8*gp + j, j = 4*m + i
-    const int valid = t1 - (tt + 8 * gp);  // tokens of this lane's group that exist
+    const int valid = sg.t1 - (tt + 8 * gp);  // tokens of this lane's group that exist
     float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float v = sacc[j >> 2][j & 3] * a.scale_log2;
-      x[j] = j < valid ? v : -INFINITY;
+      x[j] = j < valid && col_ok ? v : -INFINITY;
     }
     float mx = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
+    // A masked column may have seen no score yet (m = -inf): its reference max stays 0 so
+    // no -inf - -inf arises (on the item's own range every column has a score: folded away).
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    const float m_ref = col_ok || m_new != -INFINITY ? m_new : 0.f;
+    const float alpha = exp2f(m_run - m_ref);
     m_run = m_new;
     bf16x8 pop;
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const __bf16 pb = static_cast<__bf16>(exp2f(x[j] - m_new));
+      const __bf16 pb = static_cast<__bf16>(exp2f(x[j] - m_ref));
       pop[j] = pb;
       psum += static_cast<float>(pb);
     }
@@ -551,7 +595,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
       o[ni] *= alpha;
       o[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt.v[ni], pop, o[ni], 0, 0, 0);
     }
-    if (more) load_v(vt, pf);
+    if (more) load_v(vt, nsg, pf);
   };
 
   // The wave's tiles are w, w + NW, ...  (A second register set, two tiles in flight at two
@@ -559,9 +603,42 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
   if (w < ntiles) {
     MfmaK<D> kt;
     MfmaV<D> vt;
-    load_k(kt, w);
-    load_v(vt, w);
-    for (int tile = w; tile < ntiles; tile += kNW) step(kt, vt, tile, tile + kNW);
+    load_k(kt, main_seg, w);
+    load_v(vt, main_seg, w);
+    for (int tile = w; tile < ntiles; tile += kNW)
+      step(kt, vt, main_seg, tile, true, main_seg, tile + kNW, tile + kNW < ntiles);
+  }
+
+  // Fused tails (a share-group item that ends its range): member j's own tokens [t1, t1 +
+  // tail_j), read through its staged table entries, with only member j's columns live.  The
+  // tail tiles of all members are numbered member after member; wave w takes g = w, w + NW, ...
+  const int nt0 = (rg.tail[0] + 31) / 32, nt1 = (rg.tail[1] + 31) / 32;
+  const int nt2 = (rg.tail[2] + 31) / 32, nt3 = (rg.tail[3] + 31) / 32;
+  const int ntail = nt0 + nt1 + nt2 + nt3;  // uniform: 0 on every other item
+  if (w < ntail) {
+    constexpr int kTT = kTailTbl<B>;
+    auto seg_of = [&](int g, Seg& sg, int& k, int& j) {
+      j = g < nt0 ? 0 : g < nt0 + nt1 ? 1 : g < nt0 + nt1 + nt2 ? 2 : 3;
+      k = g - (j == 0 ? 0 : j == 1 ? nt0 : j == 2 ? nt0 + nt1 : nt0 + nt1 + nt2);
+      sg = Seg{t1, t1 + pick4(rg.tail, j), t1 / B, s_tail + j * kTT};
+    };
+    MfmaK<D> kt;
+    MfmaV<D> vt;
+    Seg sg;
+    int k, j;
+    seg_of(w, sg, k, j);
+    load_k(kt, sg, k);
+    load_v(vt, sg, k);
+    for (int g = w; g < ntail; g += kNW) {
+      Seg ns;
+      int nk, nj;
+      seg_of(min(g + kNW, ntail - 1), ns, nk, nj);
+      const bool col_ok = r16 >= j * a.G && r16 < (j + 1) * a.G;
+      step(kt, vt, sg, k, col_ok, ns, nk, g + kNW < ntail);
+      sg = ns;
+      k = nk;
+      j = nj;
+    }
   }
 
   // Wave 0 is done with its tiles: claim the next item now (thread 0), so the atomic's latency
@@ -593,6 +670,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   // s_o doubles as each wave's K staging slot, read and written in 16-byte vectors: keep it
   // (and the rest) 16-byte aligned whatever the table slice's size
   __shared__ __attribute__((aligned(16))) int s_tbl[kMaxPT / B + 1];
+  __shared__ int s_tail[kGroupMembers * kTailTbl<B>];  // fused tails' table entries
   __shared__ int s_bad, s_next;
   __shared__ __attribute__((aligned(16))) float s_ml[kNW][16][2];
   __shared__ __attribute__((aligned(16))) float s_o[kNW][16][D];
@@ -601,12 +679,16 @@ void decode_mfma_kernel(DecodeArgs a) {
   // the same kv-head on one XCD, and a non-temporal load marks it to leave first.  Shared-
   // prefix batches: 0.1975 -> 0.183 ms (B = 16), 0.205 -> 0.190 ms (B = 32); on a batch with
   // no sharing the hint is worth 11% (Llama-3-70B-shaped batch 0.296 vs 0.33 ms without it).
+  // With share groups the re-read blocks are the groups' ranges: only share-group items keep
+  // their lines; a sequence's own tokens are read once and stay non-temporal (shared-prefix
+  // batch with groups: 0.1656 -> 0.1423 ms against keeping every item's lines).
   const bool keep = a.queue[1] != 0;
+  const bool grouped = a.gmem > 0 && a.ngroups > 0;
   for_each_item(a, &s_next, [&](const int4 e0, const int4 e1, int kvh, auto&& claim) {
-    if (keep)
-      mfma_item<D, B, true>(a, e0, e1, kvh, s_tbl, &s_bad, s_ml, s_o, claim);
+    if (keep && (!grouped || e0.x < 0))
+      mfma_item<D, B, true>(a, e0, e1, kvh, s_tbl, &s_bad, s_tail, s_ml, s_o, claim);
     else
-      mfma_item<D, B, false>(a, e0, e1, kvh, s_tbl, &s_bad, s_ml, s_o, claim);
+      mfma_item<D, B, false>(a, e0, e1, kvh, s_tbl, &s_bad, s_tail, s_ml, s_o, claim);
   });
 }
 
@@ -655,7 +737,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int4 e0, co
       }
   }
 
-  const ItemRange rg = begin_item<B>(a, e0, e1, s_tbl, s_bad);
+  const ItemRange rg = begin_item<B>(a, e0, e1, s_tbl, s_bad, nullptr);
   const int t0 = rg.t0, t1 = rg.t1, b0 = rg.b0;
 
   float m_run[G], l_run[G], acc[G][DV];
@@ -799,6 +881,26 @@ __global__ __launch_bounds__(kNW * kWave) void decode_valu_kernel(DecodeArgs a) 
 // so the order inside a bucket can change from call to call; results do not depend on it
 // (each item's output has a fixed place).
 // ---------------------------------------------------------------------------------------
+// A range of R tokens in partitions: `full` of PT tokens, then a last one of `last` tokens (0:
+// none).  A last partition of at most PT / 4 tokens joins the one before it (a partition of up
+// to 1.25 PT tokens, within kMaxPT), so no item is a sliver that costs an item start-up, a
+// partial result and a merge for a few tokens.
+struct Split {
+  int full, last;
+};
+__device__ __forceinline__ Split split_range(int R, int PT) {
+  Split sp{R / PT, R % PT};
+  if (sp.last > 0 && sp.full > 0 && 4 * sp.last <= PT && PT + sp.last <= kMaxPT) {
+    sp.full -= 1;
+    sp.last += PT;
+  }
+  return sp;
+}
+__device__ __forceinline__ int parts_of(int R, int PT) {
+  const Split sp = split_range(R, PT);
+  return sp.full + (sp.last > 0);
+}
+
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
@@ -818,8 +920,10 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 // claim); a group keeps L' = min(L, its members' lengths) rounded down to a multiple of 32, and
 // is dropped (its members then plan alone) with fewer than two members or L' < 32.  Each
 // accepted group's range is split into partitions of PT tokens, and each partition into items
-// of a.gmem members; a member's own items cover [L', n) in partitions of PT from L'.  Its
-// partial results are the group's partitions first (slots 0 .. ceil(L'/PT) - 1), then its own.
+// of a.gmem members; a member's own items cover [L', n) in partitions of PT from L', unless
+// 0 < n - L' <= kFuseTail: then the group's item that ends at L' also reads those tokens of the
+// member (its "fused tail": the member's slot in the entry carries the tail length in its upper
+// 16 bits).  A member's partial results are the group's partitions first, then its own.
 __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src,
                           int32_t* lens_out, bool sys) {
   constexpr int kPlanWaves = kPlanThreads / kWave;
@@ -946,9 +1050,18 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   }
   __syncthreads();
   const int PT = s_pt;
-  const int nbk = PT / 32;  // a partial partition has 0 .. PT-1 tokens: buckets 0 .. nbk
+  // a last partition has 0 .. 1.25 PT tokens (see split_range): buckets 0 .. nbk
+  const int nbk = (min(kMaxPT, PT + PT / 4) + 31) / 32;
   for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
   __syncthreads();
+  // A group member's slot in the entry of the group's last item: its index, and in the upper 16
+  // bits the number of its own tokens that item reads after the range (0 when it has none, or
+  // more than kFuseTail, which get items of their own).
+  auto fused_member = [&](int m, int Lg) {
+    bool bad;
+    const int tail = eff_len(s_len[m], a.len_cap, bad) - Lg;
+    return m | ((tail > 0 && tail <= kFuseTail ? tail : 0) << 16);
+  };
   // Pass 1: full partitions get consecutive entries from a block-wide prefix sum; partial ones
   // are counted per bucket.  Round r: thread t takes sequence r * kPlanThreads + t and group
   // r * kPlanThreads + t.
@@ -961,11 +1074,12 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
       n = eff_len(raw, a.len_cap, bad);
       base = groups_on ? s_grp[s] : 0;
-      npre = (base + PT - 1) / PT;
-      if (!bad) full_s = (n - base) / PT;
-      const int rem = bad ? 0 : n - base - full_s * PT;
-      a.nparts[s] = bad ? 1 : npre + full_s + (rem > 0);
-      if (bad || rem > 0) atomicAdd(&s_cnt[(rem + 31) / 32], 1);
+      npre = parts_of(base, PT);
+      const bool fused = base > 0 && n - base <= kFuseTail;
+      const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
+      full_s = sp.full;
+      a.nparts[s] = bad ? 1 : npre + sp.full + (sp.last > 0);  // fused: the group's alone
+      if (bad || sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], 1);
     }
     const int* v = nullptr;
     if (g < ngroups) {
@@ -974,9 +1088,9 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       nm = v[1 + kGroupMembers];
       if (Lg > 0) {
         chunks = (nm + a.gmem - 1) / a.gmem;
-        full_g = Lg / PT;
-        const int rem = Lg - full_g * PT;
-        if (rem > 0) atomicAdd(&s_cnt[(rem + 31) / 32], chunks);
+        const Split sp = split_range(Lg, PT);
+        full_g = sp.full;
+        if (sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], chunks);
       }
     }
     const int mine = full_s + chunks * full_g;
@@ -990,16 +1104,21 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       a.items[2 * e] = make_int4(s, npre + q, base + q * PT, base + (q + 1) * PT);
       a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
     }
+    const bool ends_full = chunks > 0 && full_g * PT == Lg;  // the last full entry ends at Lg
     for (int c = 0; c < chunks; ++c) {
-      int mm[kGroupMembers];
+      int mm[kGroupMembers], mt[kGroupMembers];
 #pragma unroll
       for (int k = 0; k < kGroupMembers; ++k) {
         const int j = c * a.gmem + k;
         mm[k] = k < a.gmem && j < nm ? v[1 + j] : -1;
+        mt[k] = mm[k] >= 0 ? fused_member(mm[k], Lg) : mm[k];
       }
       for (int p = 0; p < full_g; ++p, ++e) {
         a.items[2 * e] = make_int4(-1 - g, p, p * PT, (p + 1) * PT);
-        a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
+        if (ends_full && p == full_g - 1)
+          a.items[2 * e + 1] = make_int4(mt[0], mt[1], mt[2], mt[3]);
+        else
+          a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
       }
     }
     __syncthreads();
@@ -1029,11 +1148,12 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
     const int n = eff_len(raw, a.len_cap, bad);
     const int base = groups_on ? s_grp[s] : 0;
-    const int full = bad ? 0 : (n - base) / PT, rem = bad ? 0 : n - base - full * PT;
-    if (bad || rem > 0) {
-      const int e = atomicAdd(&s_base[(rem + 31) / 32], 1);
-      const int t0 = bad ? 0 : base + full * PT;
-      a.items[2 * e] = make_int4(s, bad ? 0 : (base + PT - 1) / PT + full, t0, bad ? 0 : n);
+    const bool fused = base > 0 && n - base <= kFuseTail;
+    const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
+    if (bad || sp.last > 0) {
+      const int e = atomicAdd(&s_base[(sp.last + 31) / 32], 1);
+      const int t0 = bad ? 0 : base + sp.full * PT;
+      a.items[2 * e] = make_int4(s, bad ? 0 : parts_of(base, PT) + sp.full, t0, bad ? 0 : n);
       a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
     }
   }
@@ -1041,17 +1161,18 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int* v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
     const int Lg = v[0], nm = v[1 + kGroupMembers];
     if (Lg <= 0) continue;
-    const int full = Lg / PT, rem = Lg - full * PT;
-    if (rem == 0) continue;
+    const Split sp = split_range(Lg, PT);
+    if (sp.last == 0) continue;
+    const int full = sp.full;
     const int chunks = (nm + a.gmem - 1) / a.gmem;
     for (int c = 0; c < chunks; ++c) {
       int mm[kGroupMembers];
 #pragma unroll
       for (int k = 0; k < kGroupMembers; ++k) {
         const int j = c * a.gmem + k;
-        mm[k] = k < a.gmem && j < nm ? v[1 + j] : -1;
+        mm[k] = k < a.gmem && j < nm ? fused_member(v[1 + j], Lg) : -1;
       }
-      const int e = atomicAdd(&s_base[(rem + 31) / 32], 1);
+      const int e = atomicAdd(&s_base[(sp.last + 31) / 32], 1);
       a.items[2 * e] = make_int4(-1 - g, full, full * PT, Lg);
       a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
     }

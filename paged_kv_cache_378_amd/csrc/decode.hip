@@ -1025,7 +1025,10 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int chunks = (v[1 + kGroupMembers] + a.gmem - 1) / a.gmem;
     my_total += static_cast<unsigned long long>(v[0]) * static_cast<unsigned long long>(chunks);
   }
-  if (my_total) atomicAdd(&s_total, my_total);
+  // one LDS atomic per wave: 256 64-bit atomics on one word serialised (~2.5 us of the plan)
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) my_total += __shfl_xor(my_total, off, kWave);
+  if (lane == 0 && my_total) atomicAdd(&s_total, my_total);
   __syncthreads();
   // Partition length: the caller's, or the longest power of two in [kMinAutoPT, kMaxAutoPT]
   // that is at most 3/4 of one workgroup's share of the work (token-heads / grid).  Longer
@@ -1125,13 +1128,26 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     if (threadIdx.x == kPlanThreads - 1) s_full = before + incl;
     __syncthreads();
   }
-  // Buckets in decreasing order after the full partitions: base[b] = full + sum_{b' > b} cnt[b'].
-  for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) {
-    int above = 0;
-    for (int c = b + 1; c <= nbk; ++c) above += s_cnt[c];
-    s_base[b] = s_full + above;
-    if (b == 0) {
-      a.queue[0] = (s_full + above + s_cnt[0]) * a.Hkv;
+  // Buckets in decreasing order after the full partitions: base[b] = full + sum_{b' > b} cnt[b'],
+  // by a block-wide scan with thread t on bucket nbk - t (a serial sum per thread took ~6 us at
+  // 160 buckets).  nbk <= kPlanThreads: only bucket 0 can be left over, when nbk == kPlanThreads.
+  {
+    const int b = nbk - static_cast<int>(threadIdx.x);
+    const int c = b >= 0 ? s_cnt[b] : 0;
+    const int incl = wave_inclusive_sum(c);  // sum of cnt over buckets b .. b + lane
+    if (lane == kWave - 1) s_wave[w] = incl;
+    __syncthreads();
+    int above = 0;  // buckets above this wave's
+    for (int u = 0; u < w; ++u) above += s_wave[u];
+    if (b >= 0) s_base[b] = s_full + above + incl - c;
+    if (threadIdx.x == 0) {
+      int all = 0;
+      for (int u = 0; u < kPlanWaves; ++u) all += s_wave[u];
+      if (nbk >= kPlanThreads) {  // bucket 0 had no thread
+        s_base[0] = s_full + all;
+        all += s_cnt[0];
+      }
+      a.queue[0] = (s_full + all) * a.Hkv;
       // per-XCD queues (kv-head affinity) when at least 1/8 of the sequences share their
       // first block and the kv-heads split evenly over the XCDs; else one global cursor
       a.queue[1] = (a.Hkv % kXcd == 0 && 8 * s_dups >= a.S) ? 1 : 0;

@@ -127,35 +127,49 @@ template <typename T, int D, int HMAX>
 __device__ void finish_partition(const DecodeArgs& a, const int (&mem)[kGroupMembers],
                                  const int (&np)[kGroupMembers], int ncols, int kvh, int slot,
                                  bool bad, float (*s_ml)[HMAX][2], float (*s_o)[HMAX][D]) {
+  // A thread finishes four consecutive dims of one column: the column's wave weights are
+  // computed once for the four, the LDS reads and the store are 16-byte ones.  (One dim per
+  // thread recomputed the weights per output and, with the member selected per output, took
+  // 1.3-2.4 us per item beside the other workgroup's tiles.)
+  constexpr int C4 = D / 4;
   const int G = a.G;
-  for (int idx = threadIdx.x; idx < ncols * D; idx += kNW * kWave) {
-    const int c = idx / D, d = idx - c * D;
-    const int j = c / G, h = c - j * G;
-    const int s = pick4(mem, j), nparts = pick4(np, j);
+  for (int idx = threadIdx.x; idx < ncols * C4; idx += kNW * kWave) {
+    const int c = idx / C4, d4 = idx - c * C4;
+    const int j = (c >= G) + (c >= 2 * G) + (c >= 3 * G);  // member (at most four)
+    const int h = c - j * G;
+    const int s = j == 0 ? mem[0] : j == 1 ? mem[1] : j == 2 ? mem[2] : mem[3];
+    const int nparts = j == 0 ? np[0] : j == 1 ? np[1] : j == 2 ? np[2] : np[3];
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_ml[w][c][0]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f;
+    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kNW; ++w) {
       const float sc = exp2f(s_ml[w][c][0] - M);
       L += s_ml[w][c][1] * sc;
-      O += s_o[w][c][d] * sc;
+      O += *reinterpret_cast<const f32x4*>(&s_o[w][c][4 * d4]) * sc;
     }
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = bad ? NAN : O[i] / L;
     const int hq = kvh * G + h;
-    const float r = bad ? NAN : O / L;
     if (nparts == 1) {
-      static_cast<T*>(a.out)[(static_cast<size_t>(s) * a.Hq + hq) * D + d] = Elem<T>::from_f32(r);
+      T* op = static_cast<T*>(a.out) + (static_cast<size_t>(s) * a.Hq + hq) * D + 4 * d4;
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t lo = Elem<T>::from_f32(r[0]) | (uint32_t(Elem<T>::from_f32(r[1])) << 16);
+        const uint32_t hi = Elem<T>::from_f32(r[2]) | (uint32_t(Elem<T>::from_f32(r[3])) << 16);
+        *reinterpret_cast<uint2*>(op) = make_uint2(lo, hi);
+      } else {
+        *reinterpret_cast<f32x4*>(op) = r;
+      }
     } else {
       // partials are written through to memory (agent scope): the workgroup that merges them
       // may run on another XCD, behind another L2
       const size_t row = (static_cast<size_t>(s) * a.Hq + hq) * a.Pmax + slot;
-      st_agent(a.part_o + row * D + d, r);
-      if (d == 0) {
-        float* ml = reinterpret_cast<float*>(a.part_ml + row);
-        st_agent(ml, bad ? 0.f : M);
-        st_agent(ml + 1, bad ? NAN : L);
-      }
+      st_agent2(a.part_o + row * D + 4 * d4, r[0], r[1]);
+      st_agent2(a.part_o + row * D + 4 * d4 + 2, r[2], r[3]);
+      if (d4 == 0) st_agent2(reinterpret_cast<float*>(a.part_ml + row), bad ? 0.f : M, bad ? NAN : L);
     }
   }
 }
@@ -171,14 +185,7 @@ __device__ void finish_partition(const DecodeArgs& a, const int (&mem)[kGroupMem
 // partitions in index order (the result does not depend on which workgroup merges).
 // ---------------------------------------------------------------------------------------
 template <typename T, int D>
-__device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
-  __shared__ int s_last;
-  if (nparts <= 1) return;
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(a.done + s * a.Hkv + kvh, 1) == nparts - 1;
-  __syncthreads();
-  if (!s_last) return;
+__device__ void merge_partials(const DecodeArgs& a, int s, int kvh, int nparts) {
   bool bad;
   (void)eff_len(a.ctx_lens[s], a.len_cap, bad);
   constexpr int C4 = D / 4;  // float4 chunks per head
@@ -201,8 +208,11 @@ __device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
       // groups of kGrp partitions: every load of a group is issued before any is used; the
       // indices of a short last group are clamped to the last partition and skipped
       constexpr int kGrp = 8;
+      // up to kGrp partitions form one group: the max comes from the group's own loads below
+      // (a separate pass of loads for the max cost one more round trip to memory per merge)
+      const bool one_group = nparts <= kGrp;
       float M = -INFINITY;
-      for (int p0 = 0; p0 < nparts; p0 += kGrp) {
+      for (int p0 = 0; !one_group && p0 < nparts; p0 += kGrp) {
         float mv[kGrp];
 #pragma unroll
         for (int k = 0; k < kGrp; ++k)
@@ -221,6 +231,10 @@ __device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
           const int r = hr + min(p0 + k, nparts - 1);
           mlv[k] = __builtin_amdgcn_raw_buffer_load_b64(rm, r * 8, 0, kSc1);
           ov[k] = __builtin_amdgcn_raw_buffer_load_b128(ro, (r * D + 4 * d4) * 4, 0, kSc1);
+        }
+        if (one_group) {
+#pragma unroll
+          for (int k = 0; k < kGrp; ++k) M = fmaxf(M, __uint_as_float(mlv[k][0]));
         }
 #pragma unroll
         for (int k = 0; k < kGrp; ++k) {  // partitions in index order
@@ -273,6 +287,17 @@ __device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
   }
 }
 
+template <typename T, int D>
+__device__ void merge_if_last(const DecodeArgs& a, int s, int kvh, int nparts) {
+  __shared__ int s_last;
+  if (nparts <= 1) return;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(a.done + s * a.Hkv + kvh, 1) == nparts - 1;
+  __syncthreads();
+  if (s_last) merge_partials<T, D>(a, s, kvh, nparts);
+}
+
 // Start of a work item: its token range [t0, t1), partial slot and members come with the
 // entry; read each member's number of partial results, the context length (for the bad-length
 // check of a sequence's own item) and stage the slice of the block table the range needs in
@@ -291,12 +316,25 @@ struct ItemRange {
 template <int B>
 constexpr int kTailTbl = kFuseTail / B + 1;
 
+// The item's loads (all independent of each other, in flight together), kept in registers
+// until begin_stage writes them to LDS.
 template <int B>
-__device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, const int4 e0, const int4 e1,
-                                                int* s_tbl, int* s_bad, int* s_tail) {
-  constexpr int kTbl = kMaxPT / B + 1;  // a range may start inside a block
-  constexpr int kPer = (kTbl + kNW * kWave - 1) / (kNW * kWave);
+struct ItemLoad {
+  static constexpr int kTbl = kMaxPT / B + 1;  // a range may start inside a block
+  static constexpr int kPer = (kTbl + kNW * kWave - 1) / (kNW * kWave);
   ItemRange it;
+  int nb;         // table entries of the range
+  int ent[kPer];  // thread's entries i = threadIdx.x + r * threads
+  int tent;       // fused-tail entry (thread (tj, ti)); -1 past the table row: block 0, NaN out
+  bool tneed, bad_len;
+};
+
+template <int B>
+__device__ __forceinline__ ItemLoad<B> begin_load(const DecodeArgs& a, const int4 e0,
+                                                  const int4 e1, bool tails) {
+  using L = ItemLoad<B>;
+  L ld;
+  ItemRange& it = ld.it;
   it.t0 = e0.z;
   it.t1 = e0.w;
   it.slot = e0.y;
@@ -308,43 +346,50 @@ __device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, const int4 
     it.tail[k] = c4[k] < 0 ? 0 : (c4[k] >> 16);
   }
   it.nmem = 1 + (e1.y >= 0) + (e1.z >= 0) + (e1.w >= 0);
+  it.bad = false;
   const int s = it.mem[0];
   const bool own = e0.x >= 0;
   const int raw_n = own ? a.ctx_lens[s] : 1;
   it.b0 = it.t0 / B;
   int nb = it.t1 > it.t0 ? (it.t1 - 1) / B - it.b0 + 1 : 0;
-  nb = min(nb, a.max_blocks - it.b0);
+  ld.nb = min(nb, a.max_blocks - it.b0);
   const int32_t* row = a.tables + static_cast<size_t>(s) * a.max_blocks + it.b0;
-  int ent[kPer];
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
+  for (int r = 0; r < L::kPer; ++r) {
     const int i = threadIdx.x + r * kNW * kWave;
-    ent[r] = i < nb ? row[i] : 0;
+    ld.ent[r] = i < ld.nb ? row[i] : 0;
   }
 #pragma unroll
   for (int k = 0; k < kGroupMembers; ++k) it.np[k] = it.mem[k] >= 0 ? a.nparts[it.mem[k]] : 0;
   // fused tails: thread (j, i) loads entry i of member j's blocks from t1 on
   constexpr int kTT = kTailTbl<B>;
   const int tj = static_cast<int>(threadIdx.x) / kTT, ti = static_cast<int>(threadIdx.x) - tj * kTT;
-  int tent = -1;  // an entry the tail needs past the table row stays -1: block 0, output NaN
-  bool tneed = false;
-  if (s_tail && tj < kGroupMembers) {
+  ld.tent = -1;
+  ld.tneed = false;
+  if (tails && tj < kGroupMembers) {
     const int tl = pick4(it.tail, tj);
     const int cnt = tl > 0 ? (it.t1 + tl - 1) / B - it.t1 / B + 1 : 0;
-    tneed = ti < cnt;
-    if (tneed && it.t1 / B + ti < a.max_blocks)
-      tent = a.tables[static_cast<size_t>(pick4(it.mem, tj)) * a.max_blocks + it.t1 / B + ti];
+    ld.tneed = ti < cnt;
+    if (ld.tneed && it.t1 / B + ti < a.max_blocks)
+      ld.tent = a.tables[static_cast<size_t>(pick4(it.mem, tj)) * a.max_blocks + it.t1 / B + ti];
   }
-  bool bad_len = false;
-  if (own) (void)eff_len(raw_n, a.len_cap, bad_len);
-  if (threadIdx.x == 0) *s_bad = 0;
-  __syncthreads();
+  ld.bad_len = false;
+  if (own) (void)eff_len(raw_n, a.len_cap, ld.bad_len);
+  return ld;
+}
+
+// Write the loaded entries to LDS.  *s_bad must have been cleared before a barrier that
+// precedes this call; after the next barrier it is 1 when an entry lay outside the pool.
+template <int B>
+__device__ __forceinline__ void begin_stage(const DecodeArgs& a, const ItemLoad<B>& ld,
+                                            int* s_tbl, int* s_bad, int* s_tail) {
+  using L = ItemLoad<B>;
   bool bad_ent = false;
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
+  for (int r = 0; r < L::kPer; ++r) {
     const int i = threadIdx.x + r * kNW * kWave;
-    if (i < nb) {
-      int p = ent[r];
+    if (i < ld.nb) {
+      int p = ld.ent[r];
       if (p < 0 || p >= a.num_blocks) {
         bad_ent = true;
         p = 0;
@@ -352,7 +397,10 @@ __device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, const int4 
       s_tbl[i] = p;
     }
   }
-  if (tneed) {
+  if (ld.tneed) {
+    constexpr int kTT = kTailTbl<B>;
+    const int tj = static_cast<int>(threadIdx.x) / kTT, ti = static_cast<int>(threadIdx.x) - tj * kTT;
+    int tent = ld.tent;
     if (tent < 0 || tent >= a.num_blocks) {
       bad_ent = true;
       tent = 0;
@@ -360,8 +408,18 @@ __device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, const int4 
     s_tail[tj * kTT + ti] = tent;
   }
   if (bad_ent) *s_bad = 1;
+}
+
+template <int B>
+__device__ __forceinline__ ItemRange begin_item(const DecodeArgs& a, const int4 e0, const int4 e1,
+                                                int* s_tbl, int* s_bad, int* s_tail) {
+  const ItemLoad<B> ld = begin_load<B>(a, e0, e1, s_tail != nullptr);
+  if (threadIdx.x == 0) *s_bad = 0;
   __syncthreads();
-  it.bad = bad_len || *s_bad;
+  begin_stage<B>(a, ld, s_tbl, s_bad, s_tail);
+  __syncthreads();
+  ItemRange it = ld.it;
+  it.bad = ld.bad_len || *s_bad;
   return it;
 }
 
@@ -430,46 +488,128 @@ struct MfmaV {
   bf16x8 v[D / 16];     // V^T rows (16 dims per tile) x 8 tokens of this lane group
 };
 
+// A segment of tokens [t0, t1) read through table entries tbl[] of logical blocks from b0 on:
+// an item's range, or one member's fused tail.
+struct Seg {
+  int t0, t1, b0;
+  const int* tbl;
+};
+
 // KEEP: K/V loaded without the non-temporal hint (the plan saw blocks shared by several
 // sequences; their lines are read again by other items).
-template <int D, int B, bool KEEP, typename Claim>
-__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, const int4 e1,
-                                          int kvh, int* s_tbl, int* s_bad, int* s_tail,
-                                          float (*s_ml)[16][2], float (*s_o)[16][D],
-                                          Claim&& claim) {
+//
+// K is loaded in whole rows (instruction i covers tokens TPI*i .. TPI*i + TPI-1 of the tile,
+// 1 KB contiguous; the matrix-core layout would read 16 rows x 64 B per instruction, measured
+// 5% slower) and re-laid out through the wave's LDS slot.  Tokens past the end repeat the
+// last live token; their scores are masked.
+template <int D, int B, bool KEEP>
+__device__ __forceinline__ void load_k_tile(const DecodeArgs& a, MfmaK<D>& kt, const Seg& sg,
+                                            int tile, int kvh) {
+  using KT = MfmaK<D>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
+  const size_t head_stride = static_cast<size_t>(B) * D;  // elements per (block, kv-head)
+  const int tt = sg.t0 + 32 * tile;
+#pragma unroll
+  for (int i = 0; i < KT::NI; ++i) {
+    const int tok = min(tt + KT::TPI * i + lane / KT::CH, sg.t1 - 1);
+    const int p = sg.tbl[tok / B - sg.b0];
+    const uint16_t* kp = kc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride +
+                         static_cast<size_t>(tok % B) * D;
+    kt.raw[i] = KEEP ? ld_kv16_keep(kp + 8 * (lane % KT::CH)) : ld_kv16(kp + 8 * (lane % KT::CH));
+  }
+}
+
+// V^T rows: lane (gp, r16) reads dim 16*ni + r16 at tokens 8*gp .. 8*gp+7 of the tile
+// (16 contiguous bytes of the transposed block).
+template <int D, int B, bool KEEP>
+__device__ __forceinline__ void load_v_tile(const DecodeArgs& a, MfmaV<D>& vt, const Seg& sg,
+                                            int tile, int kvh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r16 = lane & 15, gp = lane >> 4;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
+  const size_t head_stride = static_cast<size_t>(B) * D;
+  const int tv = min(sg.t0 + 32 * tile + 8 * gp, (sg.t1 - 1) & ~7);
+  const int p = sg.tbl[tv / B - sg.b0];
+  const uint16_t* vp = vc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride + (tv % B);
+  // At B = 64 a V^T row is 128 bytes and a 32-token tile reads half of it; the other half is
+  // another wave's tile, read at about the same time.  A non-temporal load lets the line go
+  // before that second read (HBM reads were 27% above the algorithmic bytes), so these loads
+  // are ordinary ones: 0.378 -> 0.325 ms on the Llama-3-70B-shaped batch at B = 64.  At
+  // B <= 32 each line is used whole by one load instruction and non-temporal stays faster.
+#pragma unroll
+  for (int ni = 0; ni < D / 16; ++ni)
+    vt.v[ni] = (KEEP || B == 64) ? ld_kv16_keep(vp + (16 * ni + r16) * B)
+                                 : ld_kv16(vp + (16 * ni + r16) * B);
+}
+
+// Q^T operand: column r16 = head r16 % G of member r16 / G (zero past the item's members),
+// k = 8 dims per step.  A sequence's own item has one member; a share-group item up to 16 / G.
+template <int D>
+__device__ __forceinline__ void load_qop(const DecodeArgs& a, const int4 e1, int kvh,
+                                         bf16x8 (&qop)[D / 32]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r16 = lane & 15, gp = lane >> 4;
+  const int j = r16 / a.G, h = r16 - j * a.G;
+  const int cj = j == 0 ? e1.x : j == 1 ? e1.y : j == 2 ? e1.z : j == 3 ? e1.w : -1;
+  const bool live = cj >= 0;
+  const int mj = live ? (cj & 0xFFFF) : (e1.x & 0xFFFF);  // low 16 bits: the sequence
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                       (static_cast<size_t>(mj) * a.Hq + kvh * a.G + (live ? h : 0)) * D;
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st) {
+    uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (4 * st + gp));
+    if (!live) u = make_uint4(0, 0, 0, 0);
+    qop[st] = __builtin_bit_cast(bf16x8, u);
+  }
+}
+
+constexpr bool kPrefetchTile = false;
+
+// A workgroup's current item and what was loaded for it before its tiles start: the entry, the
+// range (table slice staged in LDS), the Q^T operand and, when `pre`, this wave's first tile.
+template <int D>
+struct MfmaCur {
+  int4 e0, e1;
+  int kvh;
+  ItemRange rg;
+  bf16x8 qop[D / 32];
+  MfmaK<D> kt;
+  MfmaV<D> vt;
+  bool pre;
+};
+
+// Shared state of the persistent loop.
+template <int D>
+struct MfmaShared {
+  int* tbl;
+  int* tail;
+  int* bad;
+  int* next;
+  int* last;
+  float (*ml)[16][2];
+  float (*o)[16][D];
+};
+
+// One item: its tiles, then an epilogue that overlaps the item's completion with the next
+// item's start.  Item start-up (entry, table slice, first tile: three dependent round trips to
+// memory) and completion (partial stores, done counter, merge loads: three more) cost 8-9 us
+// per item when run one after the other; a workgroup spent about a fifth of a Mistral-7B-shaped
+// decode there.  The epilogue therefore issues the next item's entry load before the wave
+// states are merged, the next item's table, context length and Q loads together with the
+// partial stores, its table staging together with the done counters, and this wave's first
+// tile of the next item before the merge, so the waits overlap.  Returns the next item index.
+template <int D, int B, bool KEEP>
+__device__ __forceinline__ int mfma_item(const DecodeArgs& a, MfmaCur<D>& c,
+                                         const MfmaShared<D>& sh, int count, bool per_xcd,
+                                         bool keep, bool grouped) {
   constexpr int NST = D / 32, NNT = D / 16;
   const int lane = threadIdx.x & (kWave - 1), w = wave_id();
   const int r16 = lane & 15, gp = lane >> 4;
-  const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
-  const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
-
-  // Q^T operand: column r16 = head r16 % G of member r16 / G (zero past the item's members),
-  // k = 8 dims per step.  A sequence's own item has one member; a share-group item up to 16 / G.
-  bf16x8 qop[NST];
-  {
-    const int j = r16 / a.G, h = r16 - j * a.G;
-    const int cj = j == 0 ? e1.x : j == 1 ? e1.y : j == 2 ? e1.z : j == 3 ? e1.w : -1;
-    const bool live = cj >= 0;
-    const int mj = live ? (cj & 0xFFFF) : (e1.x & 0xFFFF);  // low 16 bits: the sequence
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<size_t>(mj) * a.Hq + kvh * a.G + (live ? h : 0)) * D;
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (4 * st + gp));
-      if (!live) u = make_uint4(0, 0, 0, 0);
-      qop[st] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
-
-  const ItemRange rg = begin_item<B>(a, e0, e1, s_tbl, s_bad, s_tail);
+  const ItemRange rg = c.rg;
+  const int kvh = c.kvh;
   const int t0 = rg.t0, t1 = rg.t1, b0 = rg.b0;
-  // A segment of tokens [t0, t1) read through table entries tbl[] of logical blocks from b0 on:
-  // the item's range, or one member's fused tail.
-  struct Seg {
-    int t0, t1, b0;
-    const int* tbl;
-  };
-  const Seg main_seg{t0, t1, b0, s_tbl};
+  const Seg main_seg{t0, t1, b0, sh.tbl};
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[NNT];
@@ -477,26 +617,10 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
   for (int i = 0; i < NNT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ntiles = t1 > t0 ? (t1 - t0 + 31) / 32 : 0;
-  const size_t head_stride = static_cast<size_t>(B) * D;  // elements per (block, kv-head)
 
-  // K is loaded in whole rows (instruction i covers tokens TPI*i .. TPI*i + TPI-1 of the tile,
-  // 1 KB contiguous; the matrix-core layout would read 16 rows x 64 B per instruction, measured
-  // 5% slower) and re-laid out through this wave's LDS slot.  Tokens past the end repeat the
-  // last live token; their scores are masked.
   using KT = MfmaK<D>;
-  unsigned char* kstage = reinterpret_cast<unsigned char*>(&s_o[w][0][0]);
-  static_assert(sizeof(s_o[0]) >= 32 * D * 2, "the wave's output slot holds a K tile");
-  auto load_k = [&](KT& kt, const Seg& sg, int tile) {
-    const int tt = sg.t0 + 32 * tile;
-#pragma unroll
-    for (int i = 0; i < KT::NI; ++i) {
-      const int tok = min(tt + KT::TPI * i + lane / KT::CH, sg.t1 - 1);
-      const int p = sg.tbl[tok / B - sg.b0];
-      const uint16_t* kp = kc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride +
-                           static_cast<size_t>(tok % B) * D;
-      kt.raw[i] = KEEP ? ld_kv16_keep(kp + 8 * (lane % KT::CH)) : ld_kv16(kp + 8 * (lane % KT::CH));
-    }
-  };
+  unsigned char* kstage = reinterpret_cast<unsigned char*>(&sh.o[w][0][0]);
+  static_assert(sizeof(sh.o[0]) >= 32 * D * 2, "the wave's output slot holds a K tile");
   // Stage the tile (row = token of the tile, chunks permuted by kswz) and read back the QK^T
   // operand: row r16 of row group m holds token 8*(r16/4) + 4*m + r16%4 of the tile, so that
   // after QK^T lane group gp owns tokens 8*gp .. 8*gp+7 (the PV operand layout).  The wave
@@ -515,22 +639,6 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
       kop[st] = *reinterpret_cast<const bf16x8*>(
           kstage + row * (D * 2) + (((4 * st + gp) ^ kswz<D>(row)) << 4));
   };
-  // V^T rows: lane (gp, r16) reads dim 16*ni + r16 at tokens 8*gp .. 8*gp+7 of the tile
-  // (16 contiguous bytes of the transposed block).
-  auto load_v = [&](MfmaV<D>& vt, const Seg& sg, int tile) {
-    const int tv = min(sg.t0 + 32 * tile + 8 * gp, (sg.t1 - 1) & ~7);
-    const int p = sg.tbl[tv / B - sg.b0];
-    const uint16_t* vp = vc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride + (tv % B);
-    // At B = 64 a V^T row is 128 bytes and a 32-token tile reads half of it; the other half is
-    // another wave's tile, read at about the same time.  A non-temporal load lets the line go
-    // before that second read (HBM reads were 27% above the algorithmic bytes), so these loads
-    // are ordinary ones: 0.378 -> 0.325 ms on the Llama-3-70B-shaped batch at B = 64.  At
-    // B <= 32 each line is used whole by one load instruction and non-temporal stays faster.
-#pragma unroll
-    for (int ni = 0; ni < NNT; ++ni)
-      vt.v[ni] = (KEEP || B == 64) ? ld_kv16_keep(vp + (16 * ni + r16) * B)
-                                   : ld_kv16(vp + (16 * ni + r16) * B);
-  };
 
   // One tile of segment sg: QK^T on kt, refill kt with tile `pf` of segment nsg (when `more`),
   // softmax, PV on vt, refill vt.  col_ok: this lane's column takes part (false for the other
@@ -539,7 +647,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
                   const Seg& nsg, int pf, bool more) {
     const int tt = sg.t0 + 32 * tile;
     stage_k(kt);
-    if (more) load_k(kt, nsg, pf);  // the raw registers are free once staged
+    if (more) load_k_tile<D, B, KEEP>(a, kt, nsg, pf, kvh);  // the raw registers are free once staged
     f32x4 sacc[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -548,7 +656,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
       sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < NST; ++st)
-        sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], qop[st], sacc[m], 0, 0, 0);
+        sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], c.qop[st], sacc[m], 0, 0, 0);
     }
 
     // lane (gp, r16): scores of head r16 for tokens tt + 8*gp + j, j = 4*m + i
@@ -595,18 +703,18 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
       o[ni] *= alpha;
       o[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt.v[ni], pop, o[ni], 0, 0, 0);
     }
-    if (more) load_v(vt, nsg, pf);
+    if (more) load_v_tile<D, B, KEEP>(a, vt, nsg, pf, kvh);
   };
 
   // The wave's tiles are w, w + NW, ...  (A second register set, two tiles in flight at two
   // waves per SIMD, measured no faster than one set at three waves per SIMD.)
   if (w < ntiles) {
-    MfmaK<D> kt;
-    MfmaV<D> vt;
-    load_k(kt, main_seg, w);
-    load_v(vt, main_seg, w);
+    if (!c.pre) {
+      load_k_tile<D, B, KEEP>(a, c.kt, main_seg, w, kvh);
+      load_v_tile<D, B, KEEP>(a, c.vt, main_seg, w, kvh);
+    }
     for (int tile = w; tile < ntiles; tile += kNW)
-      step(kt, vt, main_seg, tile, true, main_seg, tile + kNW, tile + kNW < ntiles);
+      step(c.kt, c.vt, main_seg, tile, true, main_seg, tile + kNW, tile + kNW < ntiles);
   }
 
   // Fused tails (a share-group item that ends its range): member j's own tokens [t1, t1 +
@@ -620,21 +728,20 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
     auto seg_of = [&](int g, Seg& sg, int& k, int& j) {
       j = g < nt0 ? 0 : g < nt0 + nt1 ? 1 : g < nt0 + nt1 + nt2 ? 2 : 3;
       k = g - (j == 0 ? 0 : j == 1 ? nt0 : j == 2 ? nt0 + nt1 : nt0 + nt1 + nt2);
-      sg = Seg{t1, t1 + pick4(rg.tail, j), t1 / B, s_tail + j * kTT};
+      sg = Seg{t1, t1 + pick4(rg.tail, j), t1 / B, sh.tail + j * kTT};
     };
-    MfmaK<D> kt;
-    MfmaV<D> vt;
+    // (the main range's tile registers are free again)
     Seg sg;
     int k, j;
     seg_of(w, sg, k, j);
-    load_k(kt, sg, k);
-    load_v(vt, sg, k);
+    load_k_tile<D, B, KEEP>(a, c.kt, sg, k, kvh);
+    load_v_tile<D, B, KEEP>(a, c.vt, sg, k, kvh);
     for (int g = w; g < ntail; g += kNW) {
       Seg ns;
       int nk, nj;
       seg_of(min(g + kNW, ntail - 1), ns, nk, nj);
       const bool col_ok = r16 >= j * a.G && r16 < (j + 1) * a.G;
-      step(kt, vt, sg, k, col_ok, ns, nk, g + kNW < ntail);
+      step(c.kt, c.vt, sg, k, col_ok, ns, nk, g + kNW < ntail);
       sg = ns;
       k = nk;
       j = nj;
@@ -642,24 +749,85 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int4 e0, co
   }
 
   // Wave 0 is done with its tiles: claim the next item now (thread 0), so the atomic's latency
-  // hides behind the epilogue.  (Claiming one or two tiles earlier measured the same or up to
-  // 1% slower on long contexts; at the start of the item, 1-5% slower.)
-  claim();
+  // hides behind the wave-state merge.  A claim taken a whole item ahead commits the workgroup
+  // to work that an idle one could run, and with items of up to 2048 tokens that shows as a
+  // ragged end (claiming at the start of the item measured 1-5% slower; one or two tiles early,
+  // the same or up to 1% slower on long contexts).
+  int nxt = 0;
+  if (threadIdx.x == 0) {
+    const int x = static_cast<int>(blockIdx.x % kXcd);
+    nxt = per_xcd ? atomicAdd(&a.queue[2 + x], 1) * kXcd + x : atomicAdd(&a.queue[2 + kXcd], 1);
+  }
   // Wave state -> LDS.  l_run is per lane (its 8 tokens); sum the four lane groups.
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
   if (gp == 0) {
-    s_ml[w][r16][0] = m_run;
-    s_ml[w][r16][1] = l_run;
+    sh.ml[w][r16][0] = m_run;
+    sh.ml[w][r16][1] = l_run;
   }
 #pragma unroll
   for (int ni = 0; ni < NNT; ++ni)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[w][r16][16 * ni + 4 * gp + i] = o[ni][i];
+    for (int i = 0; i < 4; ++i) sh.o[w][r16][16 * ni + 4 * gp + i] = o[ni][i];
+  if (threadIdx.x == 0) *sh.next = nxt;
   __syncthreads();
-  finish_partition<uint16_t, D, 16>(a, rg.mem, rg.np, rg.nmem * a.G, kvh, rg.slot, rg.bad, s_ml, s_o);
-  for (int k = 0; k < rg.nmem; ++k)
-    merge_if_last<uint16_t, D>(a, pick4(rg.mem, k), kvh, pick4(rg.np, k));
+  const int ni = __builtin_amdgcn_readfirstlane(*sh.next);
+  const bool more = ni < count;
+  int4 ne0 = make_int4(0, 0, 0, 0), ne1 = make_int4(0, 0, 0, 0);
+  if (more) {
+    const int e = ni / a.Hkv;
+    ne0 = a.items[2 * e];
+    ne1 = a.items[2 * e + 1];
+  }
+  finish_partition<uint16_t, D, 16>(a, rg.mem, rg.np, rg.nmem * a.G, kvh, rg.slot, rg.bad, sh.ml, sh.o);
+  // members with partial results count them once this thread's stores have completed
+  bool split = false;
+#pragma unroll
+  for (int k = 0; k < kGroupMembers; ++k) split = split || (rg.mem[k] >= 0 && rg.np[k] > 1);
+  const int nkvh = more ? ni % a.Hkv : 0;
+  ItemLoad<B> nl;
+  bf16x8 nq[NST];
+  if (more) {
+    nl = begin_load<B>(a, ne0, ne1, true);
+    load_qop<D>(a, ne1, nkvh, nq);
+  }
+  if (split) __builtin_amdgcn_s_waitcnt(0);
+  if (threadIdx.x == 0) *sh.bad = 0;
+  __syncthreads();  // partial stores complete; the wave states and the table slice are free
+  int last = 0;
+  if (split && threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < kGroupMembers; ++k) {
+      const int s = pick4(rg.mem, k), np = pick4(rg.np, k);
+      if (s >= 0 && np > 1 && atomicAdd(a.done + s * a.Hkv + kvh, 1) == np - 1) last |= 1 << k;
+    }
+  }
+  if (more) begin_stage<B>(a, nl, sh.tbl, sh.bad, sh.tail);
+  if (threadIdx.x == 0) *sh.last = last;
+  __syncthreads();
+  last = __builtin_amdgcn_readfirstlane(*sh.last);
+  if (more) {
+    c.e0 = ne0;
+    c.e1 = ne1;
+    c.kvh = nkvh;
+    c.rg = nl.it;
+    c.rg.bad = nl.bad_len || *sh.bad;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) c.qop[st] = nq[st];
+    // this wave's first tile of the next item, when that item uses the same load kind
+    const bool nkeep = keep && (!grouped || ne0.x < 0);
+    const int nt = c.rg.t1 > c.rg.t0 ? (c.rg.t1 - c.rg.t0 + 31) / 32 : 0;
+    c.pre = kPrefetchTile && nkeep == KEEP && w < nt;
+    if (c.pre) {
+      const Seg ns{c.rg.t0, c.rg.t1, c.rg.b0, sh.tbl};
+      load_k_tile<D, B, KEEP>(a, c.kt, ns, w, nkvh);
+      load_v_tile<D, B, KEEP>(a, c.vt, ns, w, nkvh);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kGroupMembers; ++k)
+    if ((last >> k) & 1) merge_partials<uint16_t, D>(a, pick4(rg.mem, k), kvh, pick4(rg.np, k));
+  return ni;
 }
 
 template <int D, int B>
@@ -671,7 +839,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   // (and the rest) 16-byte aligned whatever the table slice's size
   __shared__ __attribute__((aligned(16))) int s_tbl[kMaxPT / B + 1];
   __shared__ int s_tail[kGroupMembers * kTailTbl<B>];  // fused tails' table entries
-  __shared__ int s_bad, s_next;
+  __shared__ int s_bad, s_next, s_last;
   __shared__ __attribute__((aligned(16))) float s_ml[kNW][16][2];
   __shared__ __attribute__((aligned(16))) float s_o[kNW][16][D];
   // A batch whose sequences share prefix blocks (the plan's sharing test, which also picks
@@ -684,12 +852,29 @@ void decode_mfma_kernel(DecodeArgs a) {
   // batch with groups: 0.1656 -> 0.1423 ms against keeping every item's lines).
   const bool keep = a.queue[1] != 0;
   const bool grouped = a.gmem > 0 && a.ngroups > 0;
-  for_each_item(a, &s_next, [&](const int4 e0, const int4 e1, int kvh, auto&& claim) {
-    if (keep && (!grouped || e0.x < 0))
-      mfma_item<D, B, true>(a, e0, e1, kvh, s_tbl, &s_bad, s_tail, s_ml, s_o, claim);
+  const int count = a.queue[0];
+  // Persistent loop: workgroup g starts with item g and claims the next one near the end of
+  // each item (see for_each_item for the two ways to claim); every workgroup leaves once the
+  // claims pass the item count.
+  int i = blockIdx.x;
+  if (i >= count) return;
+  const MfmaShared<D> sh{s_tbl, s_tail, &s_bad, &s_next, &s_last, s_ml, s_o};
+  MfmaCur<D> c;
+  {
+    const int e = i / a.Hkv;
+    c.e0 = a.items[2 * e];
+    c.e1 = a.items[2 * e + 1];
+    c.kvh = i % a.Hkv;
+    load_qop<D>(a, c.e1, c.kvh, c.qop);
+    c.rg = begin_item<B>(a, c.e0, c.e1, s_tbl, &s_bad, s_tail);
+    c.pre = false;
+  }
+  do {
+    if (keep && (!grouped || c.e0.x < 0))
+      i = mfma_item<D, B, true>(a, c, sh, count, keep, keep, grouped);
     else
-      mfma_item<D, B, false>(a, e0, e1, kvh, s_tbl, &s_bad, s_tail, s_ml, s_o, claim);
-  });
+      i = mfma_item<D, B, false>(a, c, sh, count, keep, keep, grouped);
+  } while (i < count);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -45,6 +45,8 @@
 // values past the end (even NaN) cannot reach the output.
 
 #include <climits>
+#include <cstddef>
+#include <cstring>
 #include <cmath>
 #include <map>
 #include <mutex>
@@ -1389,17 +1391,39 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int gr
 // others scatter the new tokens.
 static_assert(kPlanThreads == kWriteThreads, "one block size for both halves of the prologue");
 
+// A step's slots and lengths carried in the prologue's kernel arguments: when the caller keeps
+// them in page-locked host memory and the batch is small enough, the host copies them at the
+// call, so the kernel reads them from device memory instead of across the bus (a bus round
+// trip is ~1.4 us of the step's first kernel).
+constexpr int kMetaMax = 384;  // entries of each array (3 KiB; kernel arguments stay < 4 KiB)
+struct StepMeta {
+  int32_t has_slots, has_lens;  // 0: read through the pointers in the write's arguments
+  int32_t slots[kMetaMax];
+  int32_t lens[kMetaMax];
+};
+static_assert(sizeof(CacheWriteArgs) + sizeof(DecodeArgs) + sizeof(StepMeta) + 16 <= 3584,
+              "the prologue's kernel arguments (with the runtime's hidden ones) fit in 4 KiB");
+static_assert(offsetof(StepMeta, has_slots) == 0 && offsetof(StepMeta, has_lens) == 4,
+              "the kernel reads the flags as the segment's first two words");
+
 // The plan reads the step's lengths from w.tp.ctx_lens (where the write's table patch reads
 // them too) and, when lens_out is set, stores them for the decode kernel.
+// m is the first argument, so it starts the kernel-argument segment; the kernel reads it there
+// through the segment pointer (taking its address would copy 3 KiB into scratch memory).
 template <typename T>
-__global__ __launch_bounds__(kPlanThreads) void step_prologue_kernel(CacheWriteArgs w,
+__global__ __launch_bounds__(kPlanThreads) void step_prologue_kernel(StepMeta m, CacheWriteArgs w,
                                                                      DecodeArgs a, int grid,
                                                                      int32_t* lens_out) {
+  const int32_t* km = (const int32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  // w.sys covers what is still read through host pointers
+  CacheWriteArgs wl = w;
+  if (km[0]) wl.slots = km + offsetof(StepMeta, slots) / 4;
+  if (km[1]) wl.tp.ctx_lens = km + offsetof(StepMeta, lens) / 4;
   if (blockIdx.x == 0) {  // dispatched first: the plan is the longer chain
-    plan_body(a, grid, w.tp.ctx_lens, lens_out, w.sys);
+    plan_body(a, grid, wl.tp.ctx_lens, lens_out, wl.sys);
     return;
   }
-  cache_write_wg<T>(w, blockIdx.x - 1);
+  cache_write_wg<T>(wl, blockIdx.x - 1);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1486,7 +1510,8 @@ static KernelFn pick_valu(int32_t dtype, int G) {
 template <int D, int B>
 static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void* workspace,
                         size_t workspace_bytes_in, hipStream_t stream,
-                        const CacheWriteArgs* wr = nullptr, int32_t* lens_out = nullptr) {
+                        const CacheWriteArgs* wr = nullptr, int32_t* lens_out = nullptr,
+                        const StepMeta* meta = nullptr) {
   KernelFn k = nullptr;
   if (dtype == PA_DTYPE_BF16 && a.G >= 3 && a.G <= 16)
     k = decode_mfma_kernel<D, B>;
@@ -1523,10 +1548,12 @@ static pa_status launch(DecodeArgs a, int32_t dtype, int partition_tokens, void*
   const int grid = static_cast<int>(max_items < cap ? max_items : cap);
   if (wr) {
     const unsigned nw = static_cast<unsigned>(cache_write_wgs(*wr));
+    static const StepMeta none{};  // nothing carried: read through the pointers
+    const StepMeta& m = meta ? *meta : none;
     if (dtype == PA_DTYPE_F32)
-      hipLaunchKernelGGL(step_prologue_kernel<float>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, *wr, a, grid, lens_out);
+      hipLaunchKernelGGL(step_prologue_kernel<float>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, m, *wr, a, grid, lens_out);
     else
-      hipLaunchKernelGGL(step_prologue_kernel<uint16_t>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, *wr, a, grid, lens_out);
+      hipLaunchKernelGGL(step_prologue_kernel<uint16_t>, dim3(nw + 1), dim3(kPlanThreads), 0, stream, m, *wr, a, grid, lens_out);
     if (pa_status st = launch_status("pa_decode_step (cache write + plan)")) return st;
   } else {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, grid);
@@ -1621,15 +1648,16 @@ static pa_status decode_setup(const char* who, void* out, const void* q, const v
 }
 
 static pa_status dispatch(DecodeArgs a, int D, int B, int32_t dtype, int pt, void* w, size_t wb,
-                          void* stream, const CacheWriteArgs* wr, int32_t* lens_out = nullptr) {
+                          void* stream, const CacheWriteArgs* wr, int32_t* lens_out = nullptr,
+                          const StepMeta* meta = nullptr) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 64)
-    return B == 16 ? launch<64, 16>(a, dtype, pt, w, wb, st, wr, lens_out)
-         : B == 32 ? launch<64, 32>(a, dtype, pt, w, wb, st, wr, lens_out)
-                   : launch<64, 64>(a, dtype, pt, w, wb, st, wr, lens_out);
-  return B == 16 ? launch<128, 16>(a, dtype, pt, w, wb, st, wr, lens_out)
-       : B == 32 ? launch<128, 32>(a, dtype, pt, w, wb, st, wr, lens_out)
-                 : launch<128, 64>(a, dtype, pt, w, wb, st, wr, lens_out);
+    return B == 16 ? launch<64, 16>(a, dtype, pt, w, wb, st, wr, lens_out, meta)
+         : B == 32 ? launch<64, 32>(a, dtype, pt, w, wb, st, wr, lens_out, meta)
+                   : launch<64, 64>(a, dtype, pt, w, wb, st, wr, lens_out, meta);
+  return B == 16 ? launch<128, 16>(a, dtype, pt, w, wb, st, wr, lens_out, meta)
+       : B == 32 ? launch<128, 32>(a, dtype, pt, w, wb, st, wr, lens_out, meta)
+                 : launch<128, 64>(a, dtype, pt, w, wb, st, wr, lens_out, meta);
 }
 
 // Checks the share groups of pa_decode_shared / pa_decode_step_shared visible on the host and
@@ -1693,9 +1721,16 @@ static pa_status step_call(const char* who, void* out, const void* q, const void
   CacheWriteArgs wr = make_cache_write_args(
       key, value, k_cache, v_cache, slot_mapping, S, Hkv, D, B, num_blocks, dtype,
       TablePatch{block_tables, new_ctx_lens ? new_ctx_lens : ctx_lens, 1, max_blocks});
-  wr.sys = host_slots || host_lens;
+  // Host-memory slots and lengths of a batch of at most kMetaMax sequences travel in the
+  // first kernel's arguments (copied here, at the call); the rest is read across the bus.
+  StepMeta meta;
+  meta.has_slots = host_slots && S <= kMetaMax;
+  meta.has_lens = host_lens && S <= kMetaMax;
+  if (meta.has_slots) std::memcpy(meta.slots, slot_mapping, sizeof(int32_t) * S);
+  if (meta.has_lens) std::memcpy(meta.lens, new_ctx_lens, sizeof(int32_t) * S);
+  wr.sys = (host_slots && !meta.has_slots) || (host_lens && !meta.has_lens);
   return dispatch(a, D, B, dtype, partition_tokens, workspace, workspace_bytes_in, stream, &wr,
-                  new_ctx_lens ? ctx_lens : nullptr);
+                  new_ctx_lens ? ctx_lens : nullptr, &meta);
 }
 
 extern "C" pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -127,6 +127,10 @@ STEP_CASES = {
         "stepmany", 49, [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 512, 513, 1023, 1024,
                          1025, 1500, 2047, 2048, 2049] * 6 + [700] * 34, 64, 8, 128, 16, "bf16",
         extra_blocks=40),
+    # more sequences than the step's kernel arguments carry (384): slots and lengths in pinned
+    # memory are then read across the bus by the kernel
+    "bf16_wide": lambda: wl.custom_decode("stepwide", 50, [1, 17, 33, 200, 513] * 80, 32, 8, 128,
+                                          16, "bf16", extra_blocks=60),
 }
 
 
@@ -136,7 +140,8 @@ def test_fused_step_equals_append_then_decode(gpu, name, meta):
     """pa_decode_step (cache write + plan in one launch, then decode) gives bit-identical
     outputs, pools and tables to pa_cache_append followed by pa_decode, step after step.
     meta="pinned": the step's slots and new lengths come from the same two pinned host buffers
-    every step (read by the kernel directly, so a stale cached copy would show)."""
+    every step: up to 384 sequences the call copies them into the first kernel's arguments,
+    beyond that the kernel reads them directly (so a stale cached copy would show)."""
     from paged_kv_cache_378_amd import _lib
     from paged_kv_cache_378_amd.runner import PagedState
     w = STEP_CASES[name]()

@@ -399,9 +399,10 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
  * new_ctx_lens: int32 [S], the lengths AFTER the step (including the new token), or NULL when
  * ctx_lens already holds them; when given, the step copies them into ctx_lens.
  * slot_mapping and new_ctx_lens may each be device memory or page-locked host memory
- * (hipHostMalloc, a pinned torch tensor): the step's first kernel reads host memory directly,
- * so a serving loop needs no separate upload of its per-step metadata.  Such a host buffer
- * must not be rewritten before the step has completed on the stream.
+ * (hipHostMalloc, a pinned torch tensor), so a serving loop needs no separate upload of its
+ * per-step metadata: for S <= 384 the call copies page-locked buffers into the first kernel's
+ * arguments; for larger batches that kernel reads host memory directly, and such a buffer must
+ * then not be rewritten before the step has completed on the stream.
  * q, out, the pools, max_ctx_len, scale, partition_tokens and the workspace are as in
  * pa_decode (the size query is the same).  Errors as in pa_cache_append and pa_decode, and
  * PA_ERR_INVALID_ARG when slot_mapping or new_ctx_lens is pageable host memory; nothing is

@@ -1,5 +1,10 @@
-"""GPU parity at the full workload sizes, in the launch configuration bench.py times (automatic
-partition length, persistent schedule), on outputs the fp64 oracle computes one by one:
+"""GPU parity at the full workload sizes through pa_cache_write followed by pa_decode: the
+decode kernels, the plan, the automatic partition length and the persistent schedule that
+bench.py's pa_decode_step runs (its first kernel adds the cache write and the table patch to
+the plan's launch; tests/test_gpu_append.py checks that fused form bit for bit against this
+two-call path, tests/test_gpu_step_full.py runs it at the Llama-3-70B size and
+tests/test_gpu_share_groups.py with share groups at the shared-prefix size), on outputs the
+fp64 oracle computes one by one:
 
 * Llama-3-70B-shaped decode batch (256 sequences, churned pool): every sequence;
 * Mistral-7B-shaped batch (64): every sequence;

@@ -1128,7 +1128,9 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   const bool groups_on = a.gmem > 0 && a.ngroups > 0 && a.S <= kPlanKeep;
   const int ngroups = groups_on ? a.ngroups : 0;
   for (int i = threadIdx.x; i < kShareSlots; i += kPlanThreads) s_first[i] = -1;
-  for (int i = threadIdx.x; i < kPlanKeep; i += kPlanThreads) s_grp[i] = -1;
+  if (groups_on)
+    for (int i = threadIdx.x; i < kPlanKeep; i += kPlanThreads) s_grp[i] = -1;
+  for (int b = threadIdx.x; b < kMaxBuckets; b += kPlanThreads) s_cnt[b] = 0;
   if (threadIdx.x == 0) {
     s_full = 0;
     s_dups = 0;
@@ -1137,8 +1139,9 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   for (int i = threadIdx.x; i < a.S * a.Hkv; i += kPlanThreads) a.done[i] = 0;
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   __syncthreads();
-  // Pass 0, one sequence per thread per round: lengths (kept in LDS, copied to lens_out) and
-  // the sharing test.
+  // Pass 0, one sequence per thread per round: lengths (kept in LDS, copied to lens_out), the
+  // sharing test, and without share groups the total of tokens the items read.
+  unsigned long long my_total = 0;
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
     // The table entry is requested first: it then travels with the length, which may have to
     // come over the bus.
@@ -1146,6 +1149,11 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int raw = ld_step(lens_src + s, sys);
     if (lens_out) lens_out[s] = raw;
     if (s < kPlanKeep) s_len[s] = raw;
+    if (!groups_on) {
+      bool bad;
+      const int n = eff_len(raw, a.len_cap, bad);
+      my_total += static_cast<unsigned long long>(bad ? 0 : n);
+    }
     // Prefix sharing shows as one physical first block in several tables.  A set in LDS
     // (bounded probing, so a full set only undercounts) counts the repeats.
     if (blk >= 0) {
@@ -1161,6 +1169,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       }
     }
   }
+  if (groups_on) {
   __syncthreads();
   // Share groups: claim members, then record each group as accepted (L' = 0: dropped).
   for (int g = threadIdx.x; g < ngroups; g += kPlanThreads) {
@@ -1195,7 +1204,6 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   __syncthreads();
   // Each claimed sequence's range base: its group's L' (0 for a dropped group); the total of
   // tokens the items read (a group's range once per item of gmem members).
-  unsigned long long my_total = 0;
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
     bool bad;
     const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
@@ -1212,6 +1220,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int* v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
     const int chunks = (v[1 + kGroupMembers] + a.gmem - 1) / a.gmem;
     my_total += static_cast<unsigned long long>(v[0]) * static_cast<unsigned long long>(chunks);
+  }
   }
   // one LDS atomic per wave: 256 64-bit atomics on one word serialised (~2.5 us of the plan)
 #pragma unroll
@@ -1239,9 +1248,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   __syncthreads();
   const int PT = s_pt;
   // a last partition has 0 .. 1.25 PT tokens (see split_range): buckets 0 .. nbk
-  const int nbk = (min(kMaxPT, PT + PT / 4) + 31) / 32;
-  for (int b = threadIdx.x; b <= nbk; b += kPlanThreads) s_cnt[b] = 0;
-  __syncthreads();
+  const int nbk = (min(kMaxPT, PT + PT / 4) + 31) / 32;  // s_cnt was zeroed at the start
   // A group member's slot in the entry of the group's last item: its index, and in the upper 16
   // bits the number of its own tokens that item reads after the range (0 when it has none, or
   // more than kFuseTail, which get items of their own).
@@ -1250,49 +1257,37 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int tail = eff_len(s_len[m], a.len_cap, bad) - Lg;
     return m | ((tail > 0 && tail <= kFuseTail ? tail : 0) << 16);
   };
-  // Pass 1: full partitions get consecutive entries from a block-wide prefix sum; partial ones
-  // are counted per bucket.  Round r: thread t takes sequence r * kPlanThreads + t and group
-  // r * kPlanThreads + t.
-  const int rounds = (max(a.S, ngroups) + kPlanThreads - 1) / kPlanThreads;
-  for (int r = 0; r < rounds; ++r) {
-    const int s = r * kPlanThreads + threadIdx.x, g = s;
-    int full_s = 0, full_g = 0, chunks = 0, n = 0, base = 0, npre = 0, nm = 0, Lg = 0;
-    bool bad = false;
-    if (s < a.S) {
-      const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
-      n = eff_len(raw, a.len_cap, bad);
-      base = groups_on ? s_grp[s] : 0;
-      npre = parts_of(base, PT);
-      const bool fused = base > 0 && n - base <= kFuseTail;
-      const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
-      full_s = sp.full;
-      a.nparts[s] = bad ? 1 : npre + sp.full + (sp.last > 0);  // fused: the group's alone
-      if (bad || sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], 1);
-    }
-    const int* v = nullptr;
-    if (g < ngroups) {
-      v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
-      Lg = v[0];
-      nm = v[1 + kGroupMembers];
-      if (Lg > 0) {
-        chunks = (nm + a.gmem - 1) / a.gmem;
-        const Split sp = split_range(Lg, PT);
-        full_g = sp.full;
-        if (sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], chunks);
+  // Pass 1: full partitions take their entries through an LDS cursor (they all have PT tokens,
+  // so their order in the list does not matter); partial ones are counted per bucket.  (A
+  // block-wide prefix sum that kept them in sequence order cost three barriers per round.)
+  for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
+    bool bad;
+    const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
+    const int n = eff_len(raw, a.len_cap, bad);
+    const int base = groups_on ? s_grp[s] : 0;
+    const int npre = parts_of(base, PT);
+    const bool fused = base > 0 && n - base <= kFuseTail;
+    const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
+    a.nparts[s] = bad ? 1 : npre + sp.full + (sp.last > 0);  // fused: the group's alone
+    if (bad || sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], 1);
+    if (sp.full > 0) {
+      int e = atomicAdd(&s_full, sp.full);
+      for (int q = 0; q < sp.full; ++q, ++e) {
+        a.items[2 * e] = make_int4(s, npre + q, base + q * PT, base + (q + 1) * PT);
+        a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
       }
     }
-    const int mine = full_s + chunks * full_g;
-    const int incl = wave_inclusive_sum(mine);
-    if (lane == kWave - 1) s_wave[w] = incl;
-    __syncthreads();
-    int before = s_full;
-    for (int u = 0; u < w; ++u) before += s_wave[u];
-    int e = before + incl - mine;
-    for (int q = 0; q < full_s; ++q, ++e) {
-      a.items[2 * e] = make_int4(s, npre + q, base + q * PT, base + (q + 1) * PT);
-      a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
-    }
-    const bool ends_full = chunks > 0 && full_g * PT == Lg;  // the last full entry ends at Lg
+  }
+  for (int g = threadIdx.x; g < ngroups; g += kPlanThreads) {
+    const int* v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
+    const int Lg = v[0], nm = v[1 + kGroupMembers];
+    if (Lg <= 0) continue;
+    const int chunks = (nm + a.gmem - 1) / a.gmem;
+    const Split sp = split_range(Lg, PT);
+    if (sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], chunks);
+    if (sp.full == 0) continue;
+    int e = atomicAdd(&s_full, chunks * sp.full);
+    const bool ends_full = sp.last == 0;  // the last full entry ends at Lg
     for (int c = 0; c < chunks; ++c) {
       int mm[kGroupMembers], mt[kGroupMembers];
 #pragma unroll
@@ -1301,18 +1296,16 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
         mm[k] = k < a.gmem && j < nm ? v[1 + j] : -1;
         mt[k] = mm[k] >= 0 ? fused_member(mm[k], Lg) : mm[k];
       }
-      for (int p = 0; p < full_g; ++p, ++e) {
+      for (int p = 0; p < sp.full; ++p, ++e) {
         a.items[2 * e] = make_int4(-1 - g, p, p * PT, (p + 1) * PT);
-        if (ends_full && p == full_g - 1)
+        if (ends_full && p == sp.full - 1)
           a.items[2 * e + 1] = make_int4(mt[0], mt[1], mt[2], mt[3]);
         else
           a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
       }
     }
-    __syncthreads();
-    if (threadIdx.x == kPlanThreads - 1) s_full = before + incl;
-    __syncthreads();
   }
+  __syncthreads();
   // Buckets in decreasing order after the full partitions: base[b] = full + sum_{b' > b} cnt[b'],
   // by a block-wide scan with thread t on bucket nbk - t (a serial sum per thread took ~6 us at
   // 160 buckets).  nbk <= kPlanThreads: only bucket 0 can be left over, when nbk == kPlanThreads.

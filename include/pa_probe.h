@@ -1,5 +1,5 @@
 /*
- * pa_probe.h -- HBM read-bandwidth probes for MI355X (libpa_probe.so).
+ * pa_probe.h -- HBM read-bandwidth and matrix-core throughput probes for MI355X (libpa_probe.so).
  *
  * Measurement aids, not part of the paged-attention method: they give the achievable read
  * rates that the decode kernel's bandwidth is compared with (the 8 TB/s figure is the vendor's
@@ -9,8 +9,10 @@
  *     decode over a pool whose blocks are scattered ([TT] "How the Architecture Works": logical
  *     blocks map to physical blocks anywhere in the pool; at B = 16, D = 128, bf16 a
  *     (block, kv-head) K or V tile is 4 KiB).
- * Both only enqueue one kernel on `stream` (a hipStream_t, NULL = null stream); the caller owns
- * every buffer and times the launch.  Loads are 16-byte non-temporal loads; each thread folds
+ * A third probe gives the matrix cores' sustained rate for the bf16 instruction shapes the
+ * kernels use (the 2.5 PFLOP/s dense bf16 figure is the vendor's peak at the nominal clock).
+ * Each probe only enqueues one kernel on `stream` (a hipStream_t, NULL = null stream); the caller
+ * owns every buffer and times the launch.  Loads are 16-byte non-temporal loads; each thread folds
  * what it read into one word of `sink` so no load can be removed.  Return: 0, or -1 for an
  * argument outside what the kernels support, -7 for a launch error (as pa.h's codes).
  */
@@ -37,6 +39,14 @@ int32_t pa_probe_read_stream(const void* buf, size_t nbytes, int32_t workgroups,
  * four 1 KiB contiguous loads.  workgroups of 256 threads; sink as above. */
 int32_t pa_probe_read_gather(const void* buf, const int32_t* order, int32_t nchunks,
                              int32_t per_wave, int32_t workgroups, uint32_t* sink, void* stream);
+
+/* Back-to-back independent bf16 matrix-core instructions with register operands:
+ * shape 16 = v_mfma_f32_16x16x32_bf16 (8 accumulators per wave), 32 = v_mfma_f32_32x32x16_bf16
+ * (4 accumulators); each wave issues iters rounds.  workgroups in [1, 65536] of waves_per_wg in
+ * {1, 2, 4, 8} waves; *flops receives the launch's flop count (2 per multiply-add).
+ * sink: device, workgroups * 64 * waves_per_wg floats. */
+int32_t pa_probe_mfma(int32_t shape, int32_t workgroups, int32_t waves_per_wg, int32_t iters,
+                      float* sink, double* flops, void* stream);
 
 #ifdef __cplusplus
 }

@@ -11,20 +11,23 @@
 // Decomposition (CDNA4-specific):
 //   * a workgroup = (sequence, kv-head, block of TQ chunk tokens); its rows are the
 //     (token, query head) pairs of that kv-head's group, so every K/V tile loaded is used by
-//     all g heads (GQA) -- 256 rows per workgroup, 32 per wave (8 waves), in 2 column tiles
-//     of 16 (the accumulators of 32 rows fit in VGPRs; 64 rows per wave spilled them to AGPRs
-//     and the loop moved them back and forth);
+//     all g heads (GQA) -- 256 rows per workgroup, 32 per wave (8 waves): the accumulators of
+//     32 rows fit in VGPRs (64 rows per wave spilled them to AGPRs and the loop moved them
+//     back and forth);
 //   * the query blocks of one (sequence, kv-head) run on one XCD, so they share its L2;
 //   * K/V tiles of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4, no
 //     register staging), two stages: tile t+1 is requested before tile t is multiplied.  The
 //     16-byte chunks of K rows and of V^T rows are XOR-swizzled by row (the lane-to-address
 //     choice of the loads does it) so the 16-lane operand reads hit distinct banks;
-//   * S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 32 keys x 16 rows per tile pair) puts keys on the
-//     MFMA rows so a query row's scores sit in one lane column: the row max needs only two
-//     cross-lane steps; O^T = V^T P^T contracts over the 32 keys with P taken straight from
-//     the score registers (V is stored transposed per block in the pool);
+//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 rows per step):
+//     keys on the MFMA rows put a query row's scores in one lane column, split over the two
+//     lane halves, so the row max needs one cross-lane swap.  The K rows enter the QK^T
+//     product in a permuted order that leaves the scores exactly where the PV product wants its
+//     P^T operand, so the weights go from the score registers straight into the next product
+//     (V is stored transposed per block in the pool);
 //   * online softmax in the log2 domain, fp32 accumulation, P rounded to bf16 for the MFMA
-//     and the row sum accumulated from the same rounded values.
+//     and the row sum accumulated from the same rounded values (v_dot2c_f32_bf16 against
+//     ones, each lane half summing its 16 keys; the halves are added once at the end).
 
 #include <climits>
 #include <cmath>
@@ -37,7 +40,6 @@ namespace chunk {
 
 constexpr int kWaves = 8;
 constexpr int kRowsPerWave = 32;
-constexpr int kNC = kRowsPerWave / 16;  // 16-row column tiles per wave
 constexpr int kRows = kWaves * kRowsPerWave;
 constexpr int kKT = 64;                 // keys per LDS tile (one barrier per tile)
 constexpr int kSub = 32;                // keys per compute step (two steps per tile)
@@ -45,6 +47,26 @@ constexpr int kTblWin = 512;            // block-table entries staged in LDS at 
 constexpr float kLazy = 8.f;            // lazy-rescale threshold (log2 units: weights < 256)
 constexpr int kXcd = 8;                 // XCDs of an MI355X
 constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+
+// Chunk permutation of the K tile in LDS: 16-byte chunk c of key row `key` sits at position
+// c ^ kswz_chunk(key).  A matrix-core operand read has 16 lanes fetch the same chunk of 16
+// consecutive keys (in kperm order); a K row of D = 128 fills the 64 banks once, one of
+// D = 64 fills half of them, so the permutation takes key bits 0-3 (D = 128) or 1-3 (D = 64,
+// where bit 0 already picks the bank half) and the 16 reads hit distinct banks.
+template <int D>
+__device__ __forceinline__ int kswz_chunk(int key) {
+  return D == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+
+// Sum over lane pairs (i, i ^ 32) with gfx950's 32-lane row swap.
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct Args {
   uint16_t* out;
@@ -68,8 +90,8 @@ struct Smem {
 
 template <int D, int B>
 __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
-  constexpr int NST = D / 32;  // QK k-steps
-  constexpr int NNT = D / 16;  // PV dim tiles
+  constexpr int NST = D / 16;  // QK contraction steps (16 dims each)
+  constexpr int NDT = D / 32;  // PV tiles of 32 dims
   using SM = Smem<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem0[SM::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char smem1[SM::STAGE];
@@ -83,7 +105,6 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   if (grp >= a.S * a.Hkv) return;  // padding of the last round of groups
   const int qb = j % a.NQB, kvh = grp % a.Hkv, s = grp / a.Hkv;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = wave_id();
-  const int r16 = lane & 15, gp = lane >> 4;
   const int G = a.G, C = a.C;
 
   const int n_raw = a.ctx_lens[s];
@@ -97,24 +118,23 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   const int kend = bad ? 0 : base + i1;
   const int ntiles = (kend + kKT - 1) / kKT;
 
-  // ---- query operand: row rho = 64 w + 16 c + r16 -> (token i0 + rho / G, head rho % G)
-  int row_tok[kNC];   // chunk token of this lane's row in column tile c (-1: padding)
-  int row_head[kNC];
-  bf16x8 qop[kNC][NST];
-#pragma unroll
-  for (int c = 0; c < kNC; ++c) {
-    const int rho = kRowsPerWave * w + 16 * c + r16;
-    const int tok = i0 + rho / G;
-    const bool valid = rho < a.TQ * G && tok < i1;
-    row_tok[c] = valid ? tok : -1;
-    row_head[c] = rho % G;
-    const uint16_t* qp = a.q + ((static_cast<size_t>(s) * C + (valid ? tok : 0)) * a.Hq +
-                                kvh * G + (valid ? row_head[c] : 0)) * D;
+  // ---- query operand: row rho = 32 w + lane % 32 -> (token i0 + rho / G, head rho % G).
+  // The B operand of v_mfma_f32_32x32x16_bf16 has lane l hold B[8 (l / 32) + j][l % 32], so
+  // lane half hf holds dims 16 st + 8 hf .. + 7 of the row for contraction step st.
+  const int r32 = lane & 31, hf = lane >> 5;
+  const int rho = kRowsPerWave * w + r32;
+  const bool valid = rho < a.TQ * G && i0 + rho / G < i1;
+  const int row_tok = valid ? i0 + rho / G : -1;  // chunk token of this lane's row (-1: padding)
+  const int row_head = rho % G;
+  bf16x8 qop[NST];
+  {
+    const uint16_t* qp = a.q + ((static_cast<size_t>(s) * C + (valid ? row_tok : 0)) * a.Hq +
+                                kvh * G + (valid ? row_head : 0)) * D;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      uint4 u = *reinterpret_cast<const uint4*>(qp + 8 * (4 * st + gp));
+      uint4 u = *reinterpret_cast<const uint4*>(qp + 16 * st + 8 * hf);
       if (!valid) u = make_uint4(0, 0, 0, 0);
-      qop[c][st] = __builtin_bit_cast(bf16x8, u);
+      qop[st] = __builtin_bit_cast(bf16x8, u);
     }
   }
 
@@ -166,7 +186,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       const int u = w + kWaves * p;                    // this wave's 1 KiB piece of the tile
       const int e = u * kWave + lane;
       const int key = e / KV_PER_ROW, pos = e % KV_PER_ROW;
-      const int piece = pos ^ pa::kswz<D>(key);
+      const int piece = pos ^ kswz_chunk<D>(key);
       const int j = min(k0 + key, kend - 1);   // clamp: never past the last needed key
       const int blk = s_tbl[j / B - win0];
       const uint16_t* src = a.kc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride +
@@ -204,110 +224,109 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     }
   };
 
-  float m_run[kNC];
-  f32x4 lsum[kNC];  // row sums: every element of lane (gp, r16) holds row r16's sum
-  bf16x8 ones;
+  float m_run = -INFINITY;  // the row's reference max (log2 units)
+  float lpart = 0.f;        // this lane's half of the row sum (its 16 keys of every step)
+  f32x16 o[NDT];            // O^T tiles: 32 dims x 32 rows
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ones[j] = static_cast<__bf16>(1.f);
-  f32x4 o[kNC][NNT];
+  for (int i = 0; i < NDT; ++i)
 #pragma unroll
-  for (int c = 0; c < kNC; ++c) {
-    m_run[c] = -INFINITY;
-    lsum[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < NNT; ++i) o[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
 
-  // One 32-key step on the staged tile (keys k0 .. k0 + 31 = rows kSub*hs .. of the tile), in
-  // two halves: qk issues the S^T = K Q^T matrix-core work; softmax_pv turns the scores into
-  // weights and accumulates O^T += V^T P^T.  A tile's two steps are issued as qk, qk,
-  // softmax_pv, softmax_pv, so the second step's QK^T runs on the matrix cores while the first
-  // step's softmax runs on the VALU.
-  using SAcc = f32x4[2][kNC];
-  auto qk = [&](const unsigned char* kb, int hs, SAcc& sacc) {
-    // row r16 of key group m is key 8*(r16/4) + 4*m + r16%4 of the 32-key step
+  // A tile is two 32-key steps (keys kSub*hs .. kSub*hs + 31 of the tile).  Per step: qk
+  // issues S^T = K Q^T on the matrix cores; softmax turns the scores into bf16 weights; pv
+  // accumulates O^T += V^T P^T.  A tile is issued as qk, qk, softmax, pv, softmax, pv, so the
+  // second step's QK^T runs on the matrix cores while the first step's softmax runs on the VALU.
+  //
+  // The K rows are fed to the A operand in the order kperm, chosen so that the S^T result
+  // lands where the P^T operand of the PV product needs it: the 32x32 result gives lane l
+  // element e at row 8 (e / 4) + 4 (l / 32) + e % 4, and kperm of that row is key
+  // 16 (e / 8) + 8 (l / 32) + e % 8, i.e. lane half hf holds keys 8 hf .. 8 hf + 7 of each
+  // 16-key slice -- the B-operand layout of the product over that slice.
+  auto kperm = [](int r) { return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3); };
+  using KOps = bf16x8[NST];
+  using VOps = bf16x8[2 * NDT];
+  auto read_k = [&](const unsigned char* kb, int hs, KOps& kop) {
+    const int key = kSub * hs + kperm(r32);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int key = kSub * hs + 8 * (r16 >> 2) + 4 * m + (r16 & 3);
-      bf16x8 kop[NST];
+    for (int st = 0; st < NST; ++st)
+      kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+          kb + key * SM::KROW + (((2 * st + hf) ^ kswz_chunk<D>(key)) << 4)));
+  };
+  auto read_v = [&](const unsigned char* vb, int hs, VOps& vop) {
 #pragma unroll
-      for (int st = 0; st < NST; ++st)
-        kop[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-            kb + key * SM::KROW + (((4 * st + gp) ^ pa::kswz<D>(key)) << 4)));
+    for (int i = 0; i < NDT; ++i) {
+      const int dim = 32 * i + r32;
 #pragma unroll
-      for (int c = 0; c < kNC; ++c) {
-        sacc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < NST; ++st)
-          sacc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], qop[c][st], sacc[m][c], 0, 0, 0);
-      }
+      for (int ks = 0; ks < 2; ++ks)
+        vop[2 * i + ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+            vb + dim * SM::VROW + (((4 * hs + 2 * ks + hf) ^ vswz(dim)) * 16)));
     }
   };
+  auto qk = [&](const KOps& kop, f32x16& sacc) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[st], qop[st], sacc, 0, 0, 0);
+  };
 
-  auto softmax_pv = [&](const unsigned char* vb, int k0, int hs, const SAcc& sacc) {
-      // Online softmax per column tile; lane (gp, r16) owns keys k0 + 8 gp + j of row r16.
-      // Masking is needed only on tiles that reach past the causal limit of the workgroup's first
-      // row (which also covers every key at or past kend); padding rows are never masked, their
-      // outputs are dropped.
-      const bool need_mask = k0 + kSub - 1 > base + i0;  // uniform
-      bf16x8 pop[kNC];
-      float alpha[kNC];
-      bool any_rescale = false;
-  #pragma unroll
-      for (int c = 0; c < kNC; ++c) {
-        // raw scores; the scale (> 0, checked on the host) is applied inside the exponent
-        float x[8];
-  #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = sacc[j >> 2][c][j & 3];
-        if (need_mask) {
-          const int limit = row_tok[c] < 0 ? INT32_MAX : base + row_tok[c];  // last visible key
-  #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (k0 + 8 * gp + j > limit) x[j] = -INFINITY;
-        }
-        float mx = vmax(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], vmax3(x[5], x[6], x[7])));
-        mx = max_xor32(max_xor16(mx));
-        mx *= a.scale_log2;  // row max in log2 units (the scale is positive)
-        // Lazy rescaling: the row's reference max m_run moves only when a score exceeds it by
-        // more than kLazy (log2 units).  Weights exp2(x - m_run) then stay below 2^kLazy, and
-        // the rescale of the row's accumulators is rare.  After the final division by the
-        // row sum the result is the same softmax.
-        alpha[c] = 1.f;
-        if (mx > m_run[c] + kLazy) {
-          alpha[c] = fast_exp2(m_run[c] - mx);  // 0 on the first visible key (m_run = -inf)
-          m_run[c] = mx;
-          any_rescale = true;
-        }
-        const float m_use = m_run[c] == -INFINITY ? 0.f : m_run[c];
-  #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          pop[c][j] = static_cast<__bf16>(fast_exp2(fmaf(x[j], a.scale_log2, -m_use)));
-      }
+  auto softmax = [&](int k0, const f32x16& sacc, bf16x8 (&pop)[2]) {
+    // Online softmax; lane (hf, r32) owns keys k0 + 16 (e / 8) + 8 hf + e % 8 of row r32.
+    // Masking is needed only on steps that reach past the causal limit of the workgroup's first
+    // row (which also covers every key at or past kend); padding rows are never masked, their
+    // outputs are dropped.
+    const bool need_mask = k0 + kSub - 1 > base + i0;  // uniform
+    // raw scores; the scale (> 0, checked on the host) is applied inside the exponent
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = sacc[e];
+    if (need_mask) {
+      const int limit = row_tok < 0 ? INT32_MAX : base + row_tok;  // last visible key
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (k0 + 16 * (e >> 3) + 8 * hf + (e & 7) > limit) x[e] = -INFINITY;
+    }
+    float mx = vmax(vmax3(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], x[5]), vmax3(x[6], x[7], x[8])),
+                    vmax3(vmax3(x[9], x[10], x[11]), vmax3(x[12], x[13], x[14]), x[15]));
+    mx = max_xor32(mx);
+    mx *= a.scale_log2;  // row max in log2 units (the scale is positive)
+    // Lazy rescaling: the row's reference max m_run moves only when a score exceeds it by
+    // more than kLazy (log2 units).  Weights exp2(x - m_run) then stay below 2^kLazy, and
+    // the rescale of the row's accumulators is rare.  After the final division by the
+    // row sum the result is the same softmax.
+    float alpha = 1.f;
+    bool rescale = false;
+    if (mx > m_run + kLazy) {
+      alpha = fast_exp2(m_run - mx);  // 0 on the first visible key (m_run = -inf)
+      m_run = mx;
+      rescale = true;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      pop[e >> 3][e & 7] = static_cast<__bf16>(fast_exp2(fmaf(x[e], a.scale_log2, -m_use)));
 
-      // O^T += V^T P^T over the 32 keys (V of keys past kend was zeroed when staged), and the
-      // row sums by the same instruction against a tile of ones, so they are summed from the
-      // same bf16 weights the numerator uses.
-      if (__builtin_amdgcn_ballot_w64(any_rescale)) {  // uniform: some row of the wave rescales
-  #pragma unroll
-        for (int c = 0; c < kNC; ++c) {
-          lsum[c] *= alpha[c];
-  #pragma unroll
-          for (int ni = 0; ni < NNT; ++ni) o[c][ni] *= alpha[c];
-        }
+    // O^T += V^T P^T over the 32 keys (V of keys past kend was zeroed when staged); the row
+    // sum is taken from the same bf16 weights the numerator uses.
+    if (__builtin_amdgcn_ballot_w64(rescale)) {  // uniform: some row of the wave rescales
+      lpart *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) o[i] *= alpha;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 pr = {pop[ks][2 * i], pop[ks][2 * i + 1]};
+        lpart = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, lpart, false);
       }
-  #pragma unroll
-      for (int c = 0; c < kNC; ++c)
-        lsum[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[c], lsum[c], 0, 0, 0);
-  #pragma unroll
-      for (int ni = 0; ni < NNT; ++ni) {
-        const bf16x8 vop = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(vb + (16 * ni + r16) * SM::VROW +
-                                                  (((4 * hs + gp) ^ vswz(16 * ni + r16)) * 16)));
-  #pragma unroll
-        for (int c = 0; c < kNC; ++c)
-          o[c][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[c], o[c][ni], 0, 0, 0);
-      }
-
+  };
+  auto pv = [&](const VOps& vop, const bf16x8 (&pop)[2]) {
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[2 * i + ks], pop[ks], o[i], 0, 0, 0);
   };
 
   // Iteration t: request tile t+1 into the other stage (free: tile t-1 used it and the last
@@ -327,12 +346,24 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     const unsigned char* vb = kb + SM::KBYTES;
     static_assert(kKT == 2 * kSub, "two steps per tile");
     const int k0 = t * kKT;
-    const bool second = k0 + kSub < kend;  // uniform
-    SAcc s0, s1;
-    qk(kb, 0, s0);
-    if (second) qk(kb, 1, s1);
-    softmax_pv(vb, k0, 0, s0);
-    if (second) softmax_pv(vb, k0 + kSub, 1, s1);
+    // Both steps run unconditionally: on a last tile that ends in its first half, the second
+    // step's keys are all past kend, masked to weight 0, and their V^T rows were zeroed.
+    // The operand reads of a product are issued together, ahead of its matrix-core
+    // instructions, so the wave waits for LDS once per group instead of once per product.
+    f32x16 s0, s1;
+    KOps ka, kc;
+    read_k(kb, 0, ka);
+    read_k(kb, 1, kc);
+    qk(ka, s0);
+    qk(kc, s1);
+    bf16x8 p0[2], p1[2];
+    VOps va, vc;
+    read_v(vb, 0, va);
+    softmax(k0, s0, p0);
+    pv(va, p0);
+    read_v(vb, 1, vc);
+    softmax(k0 + kSub, s1, p1);
+    pv(vc, p1);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's requests for tile t+1 have landed
     __syncthreads();
     if (t + 1 < ntiles && (t + 2) * kKT > kend) {  // uniform: tile t+1 is the last
@@ -358,22 +389,23 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   // bad table entries anywhere in the workgroup poison its outputs
   const int any_bad = __syncthreads_or(bad_entry);
 
-  // ---- normalise and store: lane holds row r16 of tile c, dims 16 ni + 4 gp + i
-#pragma unroll
-  for (int c = 0; c < kNC; ++c) {
-    const float l = lsum[c][0];
-    if (row_tok[c] < 0) continue;
+  // ---- normalise and store: the two lane halves hold the row's two halves of the sum; lane
+  // (hf, r32) holds row r32's dims 32 i + 8 g + 4 hf + 0..3 in o[i][4 g .. 4 g + 3].
+  const float l = add_xor32(lpart);
+  if (row_tok >= 0) {
     const float inv = (bad || any_bad) ? NAN : 1.f / l;
-    uint16_t* op = a.out + ((static_cast<size_t>(s) * C + row_tok[c]) * a.Hq + kvh * G + row_head[c]) * D;
+    uint16_t* op = a.out + ((static_cast<size_t>(s) * C + row_tok) * a.Hq + kvh * G + row_head) * D;
 #pragma unroll
-    for (int ni = 0; ni < NNT; ++ni) {
-      uint2 pk2;
-      pk2.x = static_cast<uint32_t>(f32_to_bf16(o[c][ni][0] * inv)) |
-              (static_cast<uint32_t>(f32_to_bf16(o[c][ni][1] * inv)) << 16);
-      pk2.y = static_cast<uint32_t>(f32_to_bf16(o[c][ni][2] * inv)) |
-              (static_cast<uint32_t>(f32_to_bf16(o[c][ni][3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(op + 16 * ni + 4 * gp) = pk2;
-    }
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 pk2;
+        pk2.x = static_cast<uint32_t>(f32_to_bf16(o[i][4 * g] * inv)) |
+                (static_cast<uint32_t>(f32_to_bf16(o[i][4 * g + 1] * inv)) << 16);
+        pk2.y = static_cast<uint32_t>(f32_to_bf16(o[i][4 * g + 2] * inv)) |
+                (static_cast<uint32_t>(f32_to_bf16(o[i][4 * g + 3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(op + 32 * i + 8 * g + 4 * hf) = pk2;
+      }
   }
 }
 

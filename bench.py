@@ -95,7 +95,8 @@ WORKLOADS = {
             "256) swapped out to pinned host memory and back in",
     "ceilings": "HBM read ceilings: a streaming read of 4 GiB and a gather of 4 GiB as 4 KiB chunks "
                 "in shuffled and in sequential order, swept over launch shapes; and the matrix "
-                "cores' sustained bf16 rate (independent back-to-back instructions)",
+                "cores' sustained bf16 rate (independent back-to-back instructions, fixed and "
+                "random operands) with the shader clock they ran at",
     "paging_cost": "paging cost at small batch: the long-context decode step (32,768 tokens, "
                    "64/8 heads, D=128, B=32) over a scattered pool vs physically consecutive "
                    "blocks, alternating",
@@ -513,8 +514,8 @@ def run_ceilings(args, dev):
                                          C.POINTER(C.c_size_t), C.c_void_p]
     lib.pa_probe_read_gather.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                          C.c_void_p, C.c_void_p]
-    lib.pa_probe_mfma.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
-                                  C.POINTER(C.c_double), C.c_void_p]
+    lib.pa_probe_mfma.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                  C.c_void_p, C.c_void_p, C.POINTER(C.c_double), C.c_void_p]
     nbytes = 4 << 30
     nchunks = nbytes // 4096
     buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
@@ -557,22 +558,30 @@ def run_ceilings(args, dev):
                                                             sink.data_ptr(), s_ptr))
                 gather_rows.append({"order": name, "workgroups": wg, "chunks_per_wave": per_wave,
                                     "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
-    # matrix cores: back-to-back independent bf16 instructions, register operands
+    # matrix cores: back-to-back independent bf16 instructions, register operands, with a fixed
+    # sparse operand pattern and with random operands (the clock drops under the heavier draw)
     mfma_rows = []
     msink = torch.empty(2048 * 512, dtype=torch.float32, device=dev)
-    for shape in (16, 32):
-        for wg, waves in ((256, 4), (512, 4), (1024, 4), (512, 8), (1024, 8), (2048, 8)):
-            fl = C.c_double()
-            st = lib.pa_probe_mfma(shape, wg, waves, 20000, msink.data_ptr(), C.byref(fl), s_ptr)
-            if st:
-                return {"error": f"pa_probe_mfma({shape}, {wg}, {waves}) returned {st}"}
-            ms = timed(lambda: lib.pa_probe_mfma(shape, wg, waves, 20000, msink.data_ptr(),
-                                                 C.byref(fl), s_ptr), reps=5)
-            mfma_rows.append({"shape": f"{shape}x{shape}x{512 // shape}", "workgroups": wg,
-                              "waves_per_workgroup": waves,
-                              "TFLOPs": round(fl.value / (ms * 1e-3) / 1e12, 1)})
-    best_mfma = {r0: max((r for r in mfma_rows if r["shape"] == r0), key=lambda r: r["TFLOPs"])
-                 for r0 in ("16x16x32", "32x32x16")}
+    clocks = torch.zeros(2 * 2048, dtype=torch.int64, device=dev)
+    for operands, kind in ((0, "fixed"), (1, "random")):
+        for shape in (16, 32):
+            for wg, waves in ((256, 4), (512, 4), (1024, 4), (512, 8), (1024, 8), (2048, 8)):
+                fl = C.c_double()
+                st = lib.pa_probe_mfma(shape, operands, wg, waves, 20000, msink.data_ptr(),
+                                       clocks.data_ptr(), C.byref(fl), s_ptr)
+                if st:
+                    return {"error": f"pa_probe_mfma({shape}, {operands}, {wg}, {waves}) returned {st}"}
+                ms = timed(lambda: lib.pa_probe_mfma(shape, operands, wg, waves, 20000,
+                                                     msink.data_ptr(), clocks.data_ptr(),
+                                                     C.byref(fl), s_ptr), reps=5)
+                ck = clocks[:2 * wg].view(wg, 2).double().sum(0).tolist()
+                mfma_rows.append({"shape": f"{shape}x{shape}x{512 // shape}", "operands": kind,
+                                  "workgroups": wg, "waves_per_workgroup": waves,
+                                  "TFLOPs": round(fl.value / (ms * 1e-3) / 1e12, 1),
+                                  "clock_MHz": round(100.0 * ck[0] / ck[1]) if ck[1] else None})
+    best_mfma = {f"{r0} {kind}": max((r for r in mfma_rows if r["shape"] == r0 and r["operands"] == kind),
+                                     key=lambda r: r["TFLOPs"])
+                 for kind in ("fixed", "random") for r0 in ("16x16x32", "32x32x16")}
     best_stream = max(stream_rows, key=lambda r: r["GBps"])
     best = {n: max((r for r in gather_rows if r["order"] == n), key=lambda r: r["GBps"])
             for n in orders}

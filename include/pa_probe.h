@@ -42,11 +42,18 @@ int32_t pa_probe_read_gather(const void* buf, const int32_t* order, int32_t nchu
 
 /* Back-to-back independent bf16 matrix-core instructions with register operands:
  * shape 16 = v_mfma_f32_16x16x32_bf16 (8 accumulators per wave), 32 = v_mfma_f32_32x32x16_bf16
- * (4 accumulators); each wave issues iters rounds.  workgroups in [1, 65536] of waves_per_wg in
- * {1, 2, 4, 8} waves; *flops receives the launch's flop count (2 per multiply-add).
- * sink: device, workgroups * 64 * waves_per_wg floats. */
-int32_t pa_probe_mfma(int32_t shape, int32_t workgroups, int32_t waves_per_wg, int32_t iters,
-                      float* sink, double* flops, void* stream);
+ * (4 accumulators); each wave issues iters rounds.  operands 0: a fixed sparse pattern (few
+ * bits switch between instructions); 1: random bf16 words of magnitude 0.5 .. 2 with random
+ * signs, a different set per accumulator, so consecutive instructions see unrelated bits, as in
+ * attention on real data (the chip's power draw, and so its clock, depends on this).
+ * workgroups in [1, 65536] of waves_per_wg in {1, 2, 4, 8} waves; *flops receives the launch's
+ * flop count (2 per multiply-add).  sink: device, workgroups * 64 * waves_per_wg floats.
+ * clocks: NULL, or device, 2 * workgroups uint64: per workgroup, the shader-clock ticks
+ * (s_memtime) and the 100 MHz reference ticks (s_memrealtime) its first wave spent in the
+ * loop, so their ratio x 100 MHz is the clock it ran at.  Returns 0, -1 on a bad argument, -7 on
+ * a launch error. */
+int32_t pa_probe_mfma(int32_t shape, int32_t operands, int32_t workgroups, int32_t waves_per_wg,
+                      int32_t iters, float* sink, uint64_t* clocks, double* flops, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1089,6 +1089,8 @@ __device__ __forceinline__ int parts_of(int R, int PT) {
   return sp.full + (sp.last > 0);
 }
 
+template <bool V> struct Flag { static constexpr bool value = V; };
+
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
@@ -1124,9 +1126,16 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   __shared__ int s_first[kShareSlots];  // open-addressing set of first blocks seen
   __shared__ int s_dups;                // sequences whose first block another one also has
   __shared__ unsigned long long s_total;  // tokens the items will read
-  __shared__ int s_pt, s_pmax;
   const bool groups_on = a.gmem > 0 && a.ngroups > 0 && a.S <= kPlanKeep;
   const int ngroups = groups_on ? a.ngroups : 0;
+  // The first round's table entries and lengths are requested before the LDS set-up, so their
+  // latency (device memory; the bus for page-locked lengths) overlaps it.  The table entry goes
+  // first: it then travels with the length.
+  int pre_blk = -1, pre_raw = 0;
+  if (threadIdx.x < a.S) {
+    pre_blk = a.tables[static_cast<size_t>(threadIdx.x) * a.max_blocks];
+    pre_raw = ld_step(lens_src + threadIdx.x, sys);
+  }
   for (int i = threadIdx.x; i < kShareSlots; i += kPlanThreads) s_first[i] = -1;
   if (groups_on)
     for (int i = threadIdx.x; i < kPlanKeep; i += kPlanThreads) s_grp[i] = -1;
@@ -1136,17 +1145,15 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     s_dups = 0;
     s_total = 0;
   }
-  for (int i = threadIdx.x; i < a.S * a.Hkv; i += kPlanThreads) a.done[i] = 0;
   const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  __syncthreads();
+  lds_barrier();
   // Pass 0, one sequence per thread per round: lengths (kept in LDS, copied to lens_out), the
   // sharing test, and without share groups the total of tokens the items read.
   unsigned long long my_total = 0;
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
-    // The table entry is requested first: it then travels with the length, which may have to
-    // come over the bus.
-    const int blk = a.tables[static_cast<size_t>(s) * a.max_blocks];
-    const int raw = ld_step(lens_src + s, sys);
+    const bool first = s < kPlanThreads;
+    const int blk = first ? pre_blk : a.tables[static_cast<size_t>(s) * a.max_blocks];
+    const int raw = first ? pre_raw : ld_step(lens_src + s, sys);
     if (lens_out) lens_out[s] = raw;
     if (s < kPlanKeep) s_len[s] = raw;
     if (!groups_on) {
@@ -1170,7 +1177,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     }
   }
   if (groups_on) {
-  __syncthreads();
+  lds_barrier();
   // Share groups: claim members, then record each group as accepted (L' = 0: dropped).
   for (int g = threadIdx.x; g < ngroups; g += kPlanThreads) {
     const int32_t* rec = a.groups + static_cast<size_t>(g) * kGroupRec;
@@ -1201,7 +1208,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     v[4] = m3;
     v[1 + kGroupMembers] = nm;
   }
-  __syncthreads();
+  __syncthreads();  // vgroups: global memory read by other threads
   // Each claimed sequence's range base: its group's L' (0 for a dropped group); the total of
   // tokens the items read (a group's range once per item of gmem members).
   for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
@@ -1226,27 +1233,23 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) my_total += __shfl_xor(my_total, off, kWave);
   if (lane == 0 && my_total) atomicAdd(&s_total, my_total);
-  __syncthreads();
+  lds_barrier();
   // Partition length: the caller's, or the longest multiple of kAutoPTStep in [kMinAutoPT,
   // kMaxAutoPT] that is at most 3/4 of one workgroup's share of the work (token-heads / grid).
   // Longer partitions mean fewer partial results and item start-ups; the bound keeps the
   // longest items short enough for the tail to even out.  (Powers of two only gave the
-  // Mistral-7B-shaped batch 1,024 where 1,280-1,536 measured 1.4% faster.)
-  if (threadIdx.x == 0) {
-    int pt = a.PT;
-    if (pt == 0) {
-      const unsigned long long share = s_total * static_cast<unsigned long long>(a.Hkv) /
-                                       static_cast<unsigned long long>(grid > 0 ? grid : 1);
-      const unsigned long long lim = 3ull * share / 4ull / kAutoPTStep * kAutoPTStep;
-      pt = static_cast<int>(lim < kMinAutoPT ? kMinAutoPT : lim > kMaxAutoPT ? kMaxAutoPT : lim);
-    }
-    s_pt = pt;
-    // a member's group partitions and own partitions together are at most one more than an
-    // unsplit range's
-    s_pmax = (a.len_cap + pt - 1) / pt + (groups_on ? 1 : 0);
+  // Mistral-7B-shaped batch 1,024 where 1,280-1,536 measured 1.4% faster.)  Every thread
+  // derives it from the total itself (no barrier to publish it).
+  int PT = a.PT;
+  if (PT == 0) {
+    const unsigned long long share = s_total * static_cast<unsigned long long>(a.Hkv) /
+                                     static_cast<unsigned long long>(grid > 0 ? grid : 1);
+    const unsigned long long lim = 3ull * share / 4ull / kAutoPTStep * kAutoPTStep;
+    PT = static_cast<int>(lim < kMinAutoPT ? kMinAutoPT : lim > kMaxAutoPT ? kMaxAutoPT : lim);
   }
-  __syncthreads();
-  const int PT = s_pt;
+  // a member's group partitions and own partitions together are at most one more than an
+  // unsplit range's
+  const int pmax = (a.len_cap + PT - 1) / PT + (groups_on ? 1 : 0);
   // a last partition has 0 .. 1.25 PT tokens (see split_range): buckets 0 .. nbk
   const int nbk = (min(kMaxPT, PT + PT / 4) + 31) / 32;  // s_cnt was zeroed at the start
   // A group member's slot in the entry of the group's last item: its index, and in the upper 16
@@ -1260,24 +1263,43 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   // Pass 1: full partitions take their entries through an LDS cursor (they all have PT tokens,
   // so their order in the list does not matter); partial ones are counted per bucket.  (A
   // block-wide prefix sum that kept them in sequence order cost three barriers per round.)
-  for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
-    bool bad;
-    const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
-    const int n = eff_len(raw, a.len_cap, bad);
-    const int base = groups_on ? s_grp[s] : 0;
-    const int npre = parts_of(base, PT);
-    const bool fused = base > 0 && n - base <= kFuseTail;
-    const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
-    a.nparts[s] = bad ? 1 : npre + sp.full + (sp.last > 0);  // fused: the group's alone
-    if (bad || sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], 1);
-    if (sp.full > 0) {
-      int e = atomicAdd(&s_full, sp.full);
-      for (int q = 0; q < sp.full; ++q, ++e) {
+  // A sequence's length in passes 1 and 2: from LDS when pass 0 kept them all.  The loops then
+  // hold no global load, so the wave never waits on the stores it issued before (on this ISA
+  // the counter a load is waited on with also counts stores, and stores take ~1 us to retire).
+  auto seq_len = [&](int s, auto all_kept) {
+    if constexpr (decltype(all_kept)::value) return s_len[s];
+    else return s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
+  };
+  auto pass1 = [&](auto all_kept) {
+    for (int s0 = threadIdx.x - lane; s0 < a.S; s0 += kPlanThreads) {  // wave-uniform rounds
+      const int s = s0 + lane;
+      int full = 0, npre = 0, base = 0;
+      if (s < a.S) {
+        bool bad;
+        const int n = eff_len(seq_len(s, all_kept), a.len_cap, bad);
+        base = groups_on ? s_grp[s] : 0;
+        npre = parts_of(base, PT);
+        const bool fused = base > 0 && n - base <= kFuseTail;
+        const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
+        a.nparts[s] = bad ? 1 : npre + sp.full + (sp.last > 0);  // fused: the group's alone
+        if (bad || sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], 1);
+        full = sp.full;
+      }
+      // The wave's full partitions take one cursor claim, placed by a wave prefix sum (per-lane
+      // claims of differing sizes were serialised over the lanes: ~1 us per round).
+      const int incl = wave_inclusive_sum(full);
+      const int wsum = __shfl(incl, kWave - 1, kWave);
+      int wbase = 0;
+      if (lane == kWave - 1 && wsum > 0) wbase = atomicAdd(&s_full, wsum);
+      int e = __shfl(wbase, kWave - 1, kWave) + incl - full;
+      for (int q = 0; q < full; ++q, ++e) {
         a.items[2 * e] = make_int4(s, npre + q, base + q * PT, base + (q + 1) * PT);
         a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
       }
     }
-  }
+  };
+  if (a.S <= kPlanKeep) pass1(Flag<true>{});
+  else pass1(Flag<false>{});
   for (int g = threadIdx.x; g < ngroups; g += kPlanThreads) {
     const int* v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
     const int Lg = v[0], nm = v[1 + kGroupMembers];
@@ -1305,7 +1327,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // Buckets in decreasing order after the full partitions: base[b] = full + sum_{b' > b} cnt[b'],
   // by a block-wide scan with thread t on bucket nbk - t (a serial sum per thread took ~6 us at
   // 160 buckets).  nbk <= kPlanThreads: only bucket 0 can be left over, when nbk == kPlanThreads.
@@ -1314,7 +1336,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int c = b >= 0 ? s_cnt[b] : 0;
     const int incl = wave_inclusive_sum(c);  // sum of cnt over buckets b .. b + lane
     if (lane == kWave - 1) s_wave[w] = incl;
-    __syncthreads();
+    lds_barrier();
     int above = 0;  // buckets above this wave's
     for (int u = 0; u < w; ++u) above += s_wave[u];
     if (b >= 0) s_base[b] = s_full + above + incl - c;
@@ -1332,25 +1354,28 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       for (int x = 0; x < kXcd; ++x) a.queue[2 + x] = (grid - x + kXcd - 1) / kXcd;
       a.queue[2 + kXcd] = grid;
       a.queue[kPtSlot] = PT;
-      a.queue[kPmaxSlot] = s_pmax;
+      a.queue[kPmaxSlot] = pmax;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // Pass 2: the partial partitions (each thread revisits the sequences and groups of pass 1).
-  for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
-    bool bad;
-    const int raw = s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
-    const int n = eff_len(raw, a.len_cap, bad);
-    const int base = groups_on ? s_grp[s] : 0;
-    const bool fused = base > 0 && n - base <= kFuseTail;
-    const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
-    if (bad || sp.last > 0) {
-      const int e = atomicAdd(&s_base[(sp.last + 31) / 32], 1);
-      const int t0 = bad ? 0 : base + sp.full * PT;
-      a.items[2 * e] = make_int4(s, bad ? 0 : parts_of(base, PT) + sp.full, t0, bad ? 0 : n);
-      a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
+  auto pass2 = [&](auto all_kept) {
+    for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
+      bool bad;
+      const int n = eff_len(seq_len(s, all_kept), a.len_cap, bad);
+      const int base = groups_on ? s_grp[s] : 0;
+      const bool fused = base > 0 && n - base <= kFuseTail;
+      const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
+      if (bad || sp.last > 0) {
+        const int e = atomicAdd(&s_base[(sp.last + 31) / 32], 1);
+        const int t0 = bad ? 0 : base + sp.full * PT;
+        a.items[2 * e] = make_int4(s, bad ? 0 : parts_of(base, PT) + sp.full, t0, bad ? 0 : n);
+        a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
+      }
     }
-  }
+  };
+  if (a.S <= kPlanKeep) pass2(Flag<true>{});
+  else pass2(Flag<false>{});
   for (int g = threadIdx.x; g < ngroups; g += kPlanThreads) {
     const int* v = a.vgroups + static_cast<size_t>(g) * kVGroupRec;
     const int Lg = v[0], nm = v[1 + kGroupMembers];
@@ -1371,6 +1396,9 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
       a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
     }
   }
+  // The decode kernel's per-(sequence, kv-head) done counters, zeroed last: nothing here waits
+  // for these stores.
+  for (int i = threadIdx.x; i < a.S * a.Hkv; i += kPlanThreads) a.done[i] = 0;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int grid) {

@@ -110,6 +110,17 @@ __device__ __forceinline__ void load16_to_lds(const void* src, void* lds) {
 #endif
 }
 
+// Workgroup barrier for data exchanged through LDS only: the wave's LDS operations complete
+// before it, its global stores may still be in flight.  (__syncthreads also waits for those:
+// ~1 us at each barrier that follows a pass of stores.)
+__device__ __forceinline__ void lds_barrier() {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#endif
+}
+
 // Index of this wave in its workgroup, as a wave-uniform (scalar) value.  Without the
 // readfirstlane the compiler treats threadIdx.x / 64 as divergent, so every loop bounded by
 // it becomes exec-masked vector control flow instead of a scalar loop.

@@ -1120,7 +1120,8 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   __shared__ int s_cnt[kMaxBuckets];   // partial partitions per bucket
   __shared__ int s_base[kMaxBuckets];  // first entry of each bucket (then a cursor)
   __shared__ int s_wave[kPlanWaves];
-  __shared__ int s_full;               // full partitions counted so far
+  __shared__ int s_full;               // full partitions (pass 1's count)
+  __shared__ int s_fcur;               // next list position of a full partition (pass 2)
   __shared__ int s_len[kPlanKeep];     // pass 0's lengths of the first kPlanKeep sequences
   __shared__ int s_grp[kPlanKeep];     // group that took the sequence (claims), then its L'
   __shared__ int s_first[kShareSlots];  // open-addressing set of first blocks seen
@@ -1142,6 +1143,7 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
   for (int b = threadIdx.x; b < kMaxBuckets; b += kPlanThreads) s_cnt[b] = 0;
   if (threadIdx.x == 0) {
     s_full = 0;
+    s_fcur = 0;  // set by the scan (PT is a multiple of 32 in [32, kMaxPT]: bucket PT / 32 exists)
     s_dups = 0;
     s_total = 0;
   }
@@ -1260,9 +1262,6 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int tail = eff_len(s_len[m], a.len_cap, bad) - Lg;
     return m | ((tail > 0 && tail <= kFuseTail ? tail : 0) << 16);
   };
-  // Pass 1: full partitions take their entries through an LDS cursor (they all have PT tokens,
-  // so their order in the list does not matter); partial ones are counted per bucket.  (A
-  // block-wide prefix sum that kept them in sequence order cost three barriers per round.)
   // A sequence's length in passes 1 and 2: from LDS when pass 0 kept them all.  The loops then
   // hold no global load, so the wave never waits on the stores it issued before (on this ISA
   // the counter a load is waited on with also counts stores, and stores take ~1 us to retire).
@@ -1270,32 +1269,22 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     if constexpr (decltype(all_kept)::value) return s_len[s];
     else return s < kPlanKeep ? s_len[s] : lens_out ? lens_out[s] : ld_step(lens_src + s, sys);
   };
+  // The list, longest first: partial partitions longer than PT (a last partition that took in
+  // a sliver), the full partitions (PT tokens each, in any order), then the shorter partial
+  // ones, each group of partials by 32-token buckets in decreasing order.  Pass 1 counts, the
+  // scan turns the counts into list positions, pass 2 writes the entries.
+  // Pass 1: partial partitions per bucket, full partitions in total.
+  int my_full = 0;
   auto pass1 = [&](auto all_kept) {
-    for (int s0 = threadIdx.x - lane; s0 < a.S; s0 += kPlanThreads) {  // wave-uniform rounds
-      const int s = s0 + lane;
-      int full = 0, npre = 0, base = 0;
-      if (s < a.S) {
-        bool bad;
-        const int n = eff_len(seq_len(s, all_kept), a.len_cap, bad);
-        base = groups_on ? s_grp[s] : 0;
-        npre = parts_of(base, PT);
-        const bool fused = base > 0 && n - base <= kFuseTail;
-        const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
-        a.nparts[s] = bad ? 1 : npre + sp.full + (sp.last > 0);  // fused: the group's alone
-        if (bad || sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], 1);
-        full = sp.full;
-      }
-      // The wave's full partitions take one cursor claim, placed by a wave prefix sum (per-lane
-      // claims of differing sizes were serialised over the lanes: ~1 us per round).
-      const int incl = wave_inclusive_sum(full);
-      const int wsum = __shfl(incl, kWave - 1, kWave);
-      int wbase = 0;
-      if (lane == kWave - 1 && wsum > 0) wbase = atomicAdd(&s_full, wsum);
-      int e = __shfl(wbase, kWave - 1, kWave) + incl - full;
-      for (int q = 0; q < full; ++q, ++e) {
-        a.items[2 * e] = make_int4(s, npre + q, base + q * PT, base + (q + 1) * PT);
-        a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
-      }
+    for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
+      bool bad;
+      const int n = eff_len(seq_len(s, all_kept), a.len_cap, bad);
+      const int base = groups_on ? s_grp[s] : 0;
+      const bool fused = base > 0 && n - base <= kFuseTail;
+      const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
+      a.nparts[s] = bad ? 1 : parts_of(base, PT) + sp.full + (sp.last > 0);  // fused: the group's alone
+      if (bad || sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], 1);
+      my_full += sp.full;
     }
   };
   if (a.S <= kPlanKeep) pass1(Flag<true>{});
@@ -1307,31 +1296,21 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int chunks = (nm + a.gmem - 1) / a.gmem;
     const Split sp = split_range(Lg, PT);
     if (sp.last > 0) atomicAdd(&s_cnt[(sp.last + 31) / 32], chunks);
-    if (sp.full == 0) continue;
-    int e = atomicAdd(&s_full, chunks * sp.full);
-    const bool ends_full = sp.last == 0;  // the last full entry ends at Lg
-    for (int c = 0; c < chunks; ++c) {
-      int mm[kGroupMembers], mt[kGroupMembers];
-#pragma unroll
-      for (int k = 0; k < kGroupMembers; ++k) {
-        const int j = c * a.gmem + k;
-        mm[k] = k < a.gmem && j < nm ? v[1 + j] : -1;
-        mt[k] = mm[k] >= 0 ? fused_member(mm[k], Lg) : mm[k];
-      }
-      for (int p = 0; p < sp.full; ++p, ++e) {
-        a.items[2 * e] = make_int4(-1 - g, p, p * PT, (p + 1) * PT);
-        if (ends_full && p == sp.full - 1)
-          a.items[2 * e + 1] = make_int4(mt[0], mt[1], mt[2], mt[3]);
-        else
-          a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
-      }
-    }
+    my_full += chunks * sp.full;
+  }
+  // one LDS atomic per wave (per-lane atomics of differing amounts are serialised over the lanes)
+  {
+    const int wsum = __shfl(wave_inclusive_sum(my_full), kWave - 1, kWave);
+    if (lane == 0 && wsum > 0) atomicAdd(&s_full, wsum);
   }
   lds_barrier();
-  // Buckets in decreasing order after the full partitions: base[b] = full + sum_{b' > b} cnt[b'],
-  // by a block-wide scan with thread t on bucket nbk - t (a serial sum per thread took ~6 us at
-  // 160 buckets).  nbk <= kPlanThreads: only bucket 0 can be left over, when nbk == kPlanThreads.
+  // List positions by a block-wide scan over the buckets in decreasing order, thread t on bucket
+  // nbk - t (a serial sum per thread took ~6 us at 160 buckets): base[b] = sum_{b' > b} cnt[b'],
+  // plus the full partitions' count for buckets of at most PT tokens (b <= PT / 32); the full
+  // partitions start after the longer buckets.  nbk <= kPlanThreads: only bucket 0 can be left
+  // over, when nbk == kPlanThreads.
   {
+    const int bb = PT / 32;
     const int b = nbk - static_cast<int>(threadIdx.x);
     const int c = b >= 0 ? s_cnt[b] : 0;
     const int incl = wave_inclusive_sum(c);  // sum of cnt over buckets b .. b + lane
@@ -1339,12 +1318,15 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     lds_barrier();
     int above = 0;  // buckets above this wave's
     for (int u = 0; u < w; ++u) above += s_wave[u];
-    if (b >= 0) s_base[b] = s_full + above + incl - c;
+    const int excl = above + incl - c;
+    if (b >= 0) s_base[b] = excl + (b <= bb ? s_full : 0);
+    if (b == bb) s_fcur = excl;
     if (threadIdx.x == 0) {
       int all = 0;
       for (int u = 0; u < kPlanWaves; ++u) all += s_wave[u];
       if (nbk >= kPlanThreads) {  // bucket 0 had no thread
         s_base[0] = s_full + all;
+        if (bb == 0) s_fcur = all;
         all += s_cnt[0];
       }
       a.queue[0] = (s_full + all) * a.Hkv;
@@ -1358,18 +1340,34 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     }
   }
   lds_barrier();
-  // Pass 2: the partial partitions (each thread revisits the sequences and groups of pass 1).
+  // Pass 2: the entries (each thread revisits the sequences and groups of pass 1).  A wave's
+  // full partitions take one claim on the full cursor, placed by a wave prefix sum.
   auto pass2 = [&](auto all_kept) {
-    for (int s = threadIdx.x; s < a.S; s += kPlanThreads) {
-      bool bad;
-      const int n = eff_len(seq_len(s, all_kept), a.len_cap, bad);
-      const int base = groups_on ? s_grp[s] : 0;
-      const bool fused = base > 0 && n - base <= kFuseTail;
-      const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
-      if (bad || sp.last > 0) {
-        const int e = atomicAdd(&s_base[(sp.last + 31) / 32], 1);
-        const int t0 = bad ? 0 : base + sp.full * PT;
-        a.items[2 * e] = make_int4(s, bad ? 0 : parts_of(base, PT) + sp.full, t0, bad ? 0 : n);
+    for (int s0 = threadIdx.x - lane; s0 < a.S; s0 += kPlanThreads) {  // wave-uniform rounds
+      const int s = s0 + lane;
+      int full = 0, npre = 0, base = 0;
+      if (s < a.S) {
+        bool bad;
+        const int n = eff_len(seq_len(s, all_kept), a.len_cap, bad);
+        base = groups_on ? s_grp[s] : 0;
+        npre = parts_of(base, PT);
+        const bool fused = base > 0 && n - base <= kFuseTail;
+        const Split sp = bad || fused ? Split{0, 0} : split_range(n - base, PT);
+        if (bad || sp.last > 0) {
+          const int e = atomicAdd(&s_base[(sp.last + 31) / 32], 1);
+          const int t0 = bad ? 0 : base + sp.full * PT;
+          a.items[2 * e] = make_int4(s, bad ? 0 : npre + sp.full, t0, bad ? 0 : n);
+          a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
+        }
+        full = sp.full;
+      }
+      const int incl = wave_inclusive_sum(full);
+      const int wsum = __shfl(incl, kWave - 1, kWave);
+      int wbase = 0;
+      if (lane == kWave - 1 && wsum > 0) wbase = atomicAdd(&s_fcur, wsum);
+      int e = __shfl(wbase, kWave - 1, kWave) + incl - full;
+      for (int q = 0; q < full; ++q, ++e) {
+        a.items[2 * e] = make_int4(s, npre + q, base + q * PT, base + (q + 1) * PT);
         a.items[2 * e + 1] = make_int4(s, -1, -1, -1);
       }
     }
@@ -1381,19 +1379,31 @@ __device__ void plan_body(const DecodeArgs& a, int grid, const int32_t* lens_src
     const int Lg = v[0], nm = v[1 + kGroupMembers];
     if (Lg <= 0) continue;
     const Split sp = split_range(Lg, PT);
-    if (sp.last == 0) continue;
     const int full = sp.full;
     const int chunks = (nm + a.gmem - 1) / a.gmem;
+    const bool ends_full = sp.last == 0;  // the last full entry ends at Lg
+    int e = full > 0 ? atomicAdd(&s_fcur, chunks * full) : 0;
     for (int c = 0; c < chunks; ++c) {
-      int mm[kGroupMembers];
+      int mm[kGroupMembers], mt[kGroupMembers];
 #pragma unroll
       for (int k = 0; k < kGroupMembers; ++k) {
         const int j = c * a.gmem + k;
-        mm[k] = k < a.gmem && j < nm ? fused_member(v[1 + j], Lg) : -1;
+        mm[k] = k < a.gmem && j < nm ? v[1 + j] : -1;
+        mt[k] = mm[k] >= 0 ? fused_member(mm[k], Lg) : mm[k];
       }
-      const int e = atomicAdd(&s_base[(sp.last + 31) / 32], 1);
-      a.items[2 * e] = make_int4(-1 - g, full, full * PT, Lg);
-      a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
+      // a member's slot in the group's last item carries its fused tail (see fused_member)
+      for (int p = 0; p < full; ++p, ++e) {
+        a.items[2 * e] = make_int4(-1 - g, p, p * PT, (p + 1) * PT);
+        if (ends_full && p == full - 1)
+          a.items[2 * e + 1] = make_int4(mt[0], mt[1], mt[2], mt[3]);
+        else
+          a.items[2 * e + 1] = make_int4(mm[0], mm[1], mm[2], mm[3]);
+      }
+      if (sp.last > 0) {
+        const int el = atomicAdd(&s_base[(sp.last + 31) / 32], 1);
+        a.items[2 * el] = make_int4(-1 - g, full, full * PT, Lg);
+        a.items[2 * el + 1] = make_int4(mt[0], mt[1], mt[2], mt[3]);
+      }
     }
   }
   // The decode kernel's per-(sequence, kv-head) done counters, zeroed last: nothing here waits

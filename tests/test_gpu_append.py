@@ -131,6 +131,10 @@ STEP_CASES = {
     # memory are then read across the bus by the kernel
     "bf16_wide": lambda: wl.custom_decode("stepwide", 50, [1, 17, 33, 200, 513] * 80, 32, 8, 128,
                                           16, "bf16", extra_blocks=60),
+    # more sequences than the planner keeps in LDS (2,048): the lengths of the rest come from
+    # the device copy the step writes
+    "bf16_over_plan_keep": lambda: wl.custom_decode("stepkeep", 52, [1, 9, 33, 64, 100] * 421, 8,
+                                                    2, 64, 16, "bf16", extra_blocks=450),
 }
 
 

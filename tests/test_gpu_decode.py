@@ -52,6 +52,10 @@ def small_cases():
                                                     8, 8, 128, 16, "f32"),
         "bf16_g2_d128_multiround": wl.custom_decode("bf16_g2_mr", 30, [1, 15, 16, 17, 300, 1500],
                                                     8, 4, 128, 16, "bf16"),
+        # more sequences than the planner keeps in LDS (2,048): its later passes then read the
+        # lengths of the rest from memory, and every pass runs nine rounds of 256 sequences
+        "bf16_g4_over_plan_keep": wl.custom_decode("keep", 37, [1, 5, 17, 33, 70] * 421, 8, 2, 64,
+                                                   16, "bf16"),
     }
 
 

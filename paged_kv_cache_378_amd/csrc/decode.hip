@@ -567,10 +567,10 @@ __device__ __forceinline__ void load_qop(const DecodeArgs& a, const int4 e1, int
   }
 }
 
-constexpr bool kPrefetchTile = false;
-
 // A workgroup's current item and what was loaded for it before its tiles start: the entry, the
-// range (table slice staged in LDS), the Q^T operand and, when `pre`, this wave's first tile.
+// range (table slice staged in LDS) and the Q^T operand; kt / vt are the wave's tile registers.
+// (Loading this wave's first tile of the next item during the epilogue as well kept the tile
+// registers live through the merge: 48-56 bytes of scratch per lane.)
 template <int D>
 struct MfmaCur {
   int4 e0, e1;
@@ -579,7 +579,6 @@ struct MfmaCur {
   bf16x8 qop[D / 32];
   MfmaK<D> kt;
   MfmaV<D> vt;
-  bool pre;
 };
 
 // Shared state of the persistent loop.
@@ -600,12 +599,11 @@ struct MfmaShared {
 // per item when run one after the other; a workgroup spent about a fifth of a Mistral-7B-shaped
 // decode there.  The epilogue therefore issues the next item's entry load before the wave
 // states are merged, the next item's table, context length and Q loads together with the
-// partial stores, its table staging together with the done counters, and this wave's first
-// tile of the next item before the merge, so the waits overlap.  Returns the next item index.
+// partial stores, and its table staging together with the done counters, so the waits overlap.
+// Returns the next item index.
 template <int D, int B, bool KEEP>
 __device__ __forceinline__ int mfma_item(const DecodeArgs& a, MfmaCur<D>& c,
-                                         const MfmaShared<D>& sh, int count, bool per_xcd,
-                                         bool keep, bool grouped) {
+                                         const MfmaShared<D>& sh, int count, bool per_xcd) {
   constexpr int NST = D / 32, NNT = D / 16;
   const int lane = threadIdx.x & (kWave - 1), w = wave_id();
   const int r16 = lane & 15, gp = lane >> 4;
@@ -712,10 +710,8 @@ __device__ __forceinline__ int mfma_item(const DecodeArgs& a, MfmaCur<D>& c,
   // The wave's tiles are w, w + NW, ...  (A second register set, two tiles in flight at two
   // waves per SIMD, measured no faster than one set at three waves per SIMD.)
   if (w < ntiles) {
-    if (!c.pre) {
-      load_k_tile<D, B, KEEP>(a, c.kt, main_seg, w, kvh);
-      load_v_tile<D, B, KEEP>(a, c.vt, main_seg, w, kvh);
-    }
+    load_k_tile<D, B, KEEP>(a, c.kt, main_seg, w, kvh);
+    load_v_tile<D, B, KEEP>(a, c.vt, main_seg, w, kvh);
     for (int tile = w; tile < ntiles; tile += kNW)
       step(c.kt, c.vt, main_seg, tile, true, main_seg, tile + kNW, tile + kNW < ntiles);
   }
@@ -817,15 +813,6 @@ __device__ __forceinline__ int mfma_item(const DecodeArgs& a, MfmaCur<D>& c,
     c.rg.bad = nl.bad_len || *sh.bad;
 #pragma unroll
     for (int st = 0; st < NST; ++st) c.qop[st] = nq[st];
-    // this wave's first tile of the next item, when that item uses the same load kind
-    const bool nkeep = keep && (!grouped || ne0.x < 0);
-    const int nt = c.rg.t1 > c.rg.t0 ? (c.rg.t1 - c.rg.t0 + 31) / 32 : 0;
-    c.pre = kPrefetchTile && nkeep == KEEP && w < nt;
-    if (c.pre) {
-      const Seg ns{c.rg.t0, c.rg.t1, c.rg.b0, sh.tbl};
-      load_k_tile<D, B, KEEP>(a, c.kt, ns, w, nkvh);
-      load_v_tile<D, B, KEEP>(a, c.vt, ns, w, nkvh);
-    }
   }
 #pragma unroll
   for (int k = 0; k < kGroupMembers; ++k)
@@ -870,13 +857,12 @@ void decode_mfma_kernel(DecodeArgs a) {
     c.kvh = i % a.Hkv;
     load_qop<D>(a, c.e1, c.kvh, c.qop);
     c.rg = begin_item<B>(a, c.e0, c.e1, s_tbl, &s_bad, s_tail);
-    c.pre = false;
   }
   do {
     if (keep && (!grouped || c.e0.x < 0))
-      i = mfma_item<D, B, true>(a, c, sh, count, keep, keep, grouped);
+      i = mfma_item<D, B, true>(a, c, sh, count, keep);
     else
-      i = mfma_item<D, B, false>(a, c, sh, count, keep, keep, grouped);
+      i = mfma_item<D, B, false>(a, c, sh, count, keep);
   } while (i < count);
 }
 

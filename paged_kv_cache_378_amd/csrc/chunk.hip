@@ -138,12 +138,12 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
     }
   }
 
-  // ---- cooperative tile loads: 256 threads x 16 B per pass
-  // K tile: 32 keys x D dims (row-major)  -> KTILE_VECS 16-byte pieces
-  // V tile: D dims x 32 keys (transposed) -> VTILE_VECS 16-byte pieces
+  // ---- cooperative tile loads: the workgroup's 512 threads x 16 B per pass
+  // K tile: kKT keys x D dims (row-major)  -> KTILE_VECS 16-byte pieces
+  // V tile: D dims x kKT keys (transposed) -> VTILE_VECS 16-byte pieces
   constexpr int KV_PER_ROW = D * 2 / 16;           // 16-byte pieces per key row
   constexpr int KTILE_VECS = kKT * KV_PER_ROW;
-  constexpr int VP_PER_ROW = kKT * 2 / 16;         // 16-byte pieces per dim row (4)
+  constexpr int VP_PER_ROW = kKT * 2 / 16;         // 16-byte pieces per dim row (8)
   constexpr int VTILE_VECS = D * VP_PER_ROW;
   constexpr int PASSES_K = KTILE_VECS / (kWaves * kWave);
   constexpr int PASSES_V = VTILE_VECS / (kWaves * kWave);

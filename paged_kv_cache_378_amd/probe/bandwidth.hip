@@ -65,7 +65,8 @@ int32_t launched() { return hipGetLastError() == hipSuccess ? 0 : -7; }
 extern "C" int32_t pa_probe_read_stream(const void* buf, size_t nbytes, int32_t workgroups,
                                         int32_t loads, uint32_t* sink, size_t* read_bytes,
                                         void* stream) {
-  if (!buf || !sink || !read_bytes || !aligned16(buf) || workgroups < 1 || workgroups > 65536)
+  if (!buf || !sink || !read_bytes || !aligned16(buf) || workgroups < 1 || workgroups > 65536 ||
+      (loads != 1 && loads != 2 && loads != 4 && loads != 8))
     return -1;
   const size_t step = static_cast<size_t>(workgroups) * kThreads * static_cast<size_t>(loads);
   const size_t n = nbytes / 16 / step * step;

@@ -95,7 +95,9 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   using SM = Smem<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem0[SM::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char smem1[SM::STAGE];
-  __shared__ int s_tbl[kTblWin];  // physical blocks of logical blocks win0 .. win0 + kTblWin - 1
+  // element offset of (physical block, kv-head) in the pools, for logical blocks win0 ..
+  // win0 + kTblWin - 1 (K and V blocks share the stride B * D per head)
+  __shared__ long long s_tbl[kTblWin];
 
   // XCD-aware order: the dispatcher deals workgroups round-robin to the kXcd XCDs, so
   // workgroup L runs on XCD L % kXcd.  Every query block of one (sequence, kv-head) group is
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
         bad_entry = 1;
         blk = 0;
       }
-      s_tbl[i] = blk;
+      s_tbl[i] = (static_cast<long long>(blk) * a.Hkv + kvh) * static_cast<long long>(head_stride);
     }
   };
   load_window(0);
@@ -188,9 +190,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       const int key = e / KV_PER_ROW, pos = e % KV_PER_ROW;
       const int piece = pos ^ kswz_chunk<D>(key);
       const int j = min(k0 + key, kend - 1);   // clamp: never past the last needed key
-      const int blk = s_tbl[j / B - win0];
-      const uint16_t* src = a.kc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride +
-                            static_cast<size_t>(j % B) * D + piece * 8;
+      const uint16_t* src = a.kc + s_tbl[j / B - win0] + ((j % B) * D + piece * 8);
       pa::load16_to_lds(src, kb + u * (kWave * 16));
     }
 #pragma unroll
@@ -200,9 +200,7 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
       const int dim = e / VP_PER_ROW, pos = e % VP_PER_ROW;
       const int piece = pos ^ vswz(dim);               // 8 keys
       const int j = min(k0 + 8 * piece, (kend - 1) & ~7);
-      const int blk = s_tbl[j / B - win0];
-      const uint16_t* src = a.vc + (static_cast<size_t>(blk) * a.Hkv + kvh) * head_stride +
-                            static_cast<size_t>(dim) * B + (j % B);
+      const uint16_t* src = a.vc + s_tbl[j / B - win0] + (dim * B + (j % B));
       pa::load16_to_lds(src, vb + u * (kWave * 16));
     }
   };

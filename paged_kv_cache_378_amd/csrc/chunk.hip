@@ -31,6 +31,8 @@
 
 #include <climits>
 #include <cmath>
+#include <map>
+#include <mutex>
 
 #include "device_common.h"
 
@@ -76,6 +78,7 @@ struct Args {
   const int32_t* tables;
   const int32_t* ctx_lens;
   int S, C, Hq, Hkv, G, TQ, NQB, max_blocks, num_blocks;
+  int units;  // XCD-ordered query blocks: groups (padded to a multiple of kXcd) x NQB
   float scale_log2;
 };
 
@@ -88,21 +91,19 @@ struct Smem {
   static constexpr int STAGE = KBYTES + VBYTES;
 };
 
+// One unit of work: the query block `L` of the XCD-ordered list (see chunk_kernel), with the
+// workgroup's two LDS stages and its table window.
 template <int D, int B>
-__global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
+__device__ __forceinline__ void chunk_unit(const Args& a, int L, unsigned char* smem0,
+                                           unsigned char* smem1, long long* s_tbl) {
   constexpr int NST = D / 16;  // QK contraction steps (16 dims each)
   constexpr int NDT = D / 32;  // PV tiles of 32 dims
   using SM = Smem<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem0[SM::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char smem1[SM::STAGE];
-  // element offset of (physical block, kv-head) in the pools, for logical blocks win0 ..
-  // win0 + kTblWin - 1 (K and V blocks share the stride B * D per head)
-  __shared__ long long s_tbl[kTblWin];
 
-  // XCD-aware order: the dispatcher deals workgroups round-robin to the kXcd XCDs, so
-  // workgroup L runs on XCD L % kXcd.  Every query block of one (sequence, kv-head) group is
-  // placed on the same XCD, where they stream the same K/V through one L2.
-  const int L = blockIdx.x, xcd = L % kXcd, j = L / kXcd;
+  // XCD-aware order: unit L runs on XCD L % kXcd (see chunk_kernel).  Every query block of one
+  // (sequence, kv-head) group is placed on the same XCD, where they stream the same K/V
+  // through one L2.
+  const int xcd = L % kXcd, j = L / kXcd;
   const int grp = (j / a.NQB) * kXcd + xcd;
   if (grp >= a.S * a.Hkv) return;  // padding of the last round of groups
   const int qb = j % a.NQB, kvh = grp % a.Hkv, s = grp / a.Hkv;
@@ -407,10 +408,61 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   }
 }
 
+// Persistent: a grid of as many workgroups as fit on the device at once (a multiple of kXcd),
+// each running units blockIdx.x, blockIdx.x + gridDim.x, ...  The dispatcher deals workgroups
+// round-robin to the kXcd XCDs, so workgroup g runs on XCD g % kXcd, and so does every unit it
+// takes.  A workgroup per unit instead left each CU idle between one workgroup's end and the
+// next one's first tile (dispatch, Q and table loads, the first tile's round trip) four times
+// per kernel.
+template <int D, int B>
+__global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
+  using SM = Smem<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem0[SM::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem1[SM::STAGE];
+  // element offset of (physical block, kv-head) in the pools, for logical blocks win0 ..
+  // win0 + kTblWin - 1 (K and V blocks share the stride B * D per head)
+  __shared__ long long s_tbl[kTblWin];
+  for (int L = blockIdx.x; L < a.units; L += gridDim.x) chunk_unit<D, B>(a, L, smem0, smem1, s_tbl);
+}
+
 }  // namespace chunk
 }  // namespace pa
 
 using namespace pa;
+
+namespace {
+
+// Workgroups of chunk_kernel<D, B> resident on the current device at once, rounded down to a
+// multiple of kXcd (the persistent grid); cached per (kernel, device).
+template <int D, int B>
+int chunk_grid_cap() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk::chunk_kernel<D, B>,
+                                                   chunk::kWaves * kWave, 0) != hipSuccess)
+    return 0;
+  const int cap = cus * (per_cu > 0 ? per_cu : 1) / chunk::kXcd * chunk::kXcd;
+  cache[dev] = cap < chunk::kXcd ? chunk::kXcd : cap;
+  return cache[dev];
+}
+
+template <int D, int B>
+pa_status launch_chunk(const chunk::Args& a, hipStream_t st) {
+  const int cap = chunk_grid_cap<D, B>();
+  if (cap <= 0) return fail(PA_ERR_HIP, "pa_chunk_attend: cannot query the device");
+  const unsigned grid = static_cast<unsigned>(a.units < cap ? a.units : cap);
+  hipLaunchKernelGGL((chunk::chunk_kernel<D, B>), dim3(grid), dim3(chunk::kWaves * kWave), 0, st, a);
+  return launch_status("pa_chunk_attend");
+}
+
+}  // namespace
 
 extern "C" pa_status pa_chunk_attend(void* out, const void* q, const void* k_cache,
                                      const void* v_cache, const int32_t* block_tables,
@@ -456,16 +508,14 @@ extern "C" pa_status pa_chunk_attend(void* out, const void* q, const void* k_cac
   a.scale_log2 = scale * chunk::kLog2e;
   const int64_t groups = (static_cast<int64_t>(S) * Hkv + chunk::kXcd - 1) / chunk::kXcd * chunk::kXcd;
   if (groups * a.NQB > INT_MAX) return fail(PA_ERR_INVALID_ARG, "pa_chunk_attend: grid too large");
-  const dim3 grid(static_cast<unsigned>(groups * a.NQB));
+  a.units = static_cast<int>(groups * a.NQB);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 64) {
-    if (B == 64) hipLaunchKernelGGL((chunk::chunk_kernel<64, 64>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
-    else if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<64, 16>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
-    else hipLaunchKernelGGL((chunk::chunk_kernel<64, 32>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
-  } else {
-    if (B == 64) hipLaunchKernelGGL((chunk::chunk_kernel<128, 64>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
-    else if (B == 16) hipLaunchKernelGGL((chunk::chunk_kernel<128, 16>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
-    else hipLaunchKernelGGL((chunk::chunk_kernel<128, 32>), grid, dim3(chunk::kWaves * kWave), 0, st, a);
+    if (B == 64) return launch_chunk<64, 64>(a, st);
+    if (B == 16) return launch_chunk<64, 16>(a, st);
+    return launch_chunk<64, 32>(a, st);
   }
-  return launch_status("pa_chunk_attend");
+  if (B == 64) return launch_chunk<128, 64>(a, st);
+  if (B == 16) return launch_chunk<128, 16>(a, st);
+  return launch_chunk<128, 32>(a, st);
 }

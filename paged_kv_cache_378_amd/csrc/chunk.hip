@@ -409,11 +409,16 @@ __device__ __forceinline__ void chunk_unit(const Args& a, int L, unsigned char* 
 }
 
 // Persistent: a grid of as many workgroups as fit on the device at once (a multiple of kXcd),
-// each running units blockIdx.x, blockIdx.x + gridDim.x, ...  The dispatcher deals workgroups
+// each running one unit per round of gridDim.x units.  The dispatcher deals workgroups
 // round-robin to the kXcd XCDs, so workgroup g runs on XCD g % kXcd, and so does every unit it
 // takes.  A workgroup per unit instead left each CU idle between one workgroup's end and the
 // next one's first tile (dispatch, Q and table loads, the first tile's round trip) four times
 // per kernel.
+//
+// In odd rounds a workgroup takes the unit mirrored within its XCD (g = 8 m + x -> 8 (M-1-m)
+// + x for M = gridDim.x / 8).  Later query blocks of a group see more keys (the causal limit),
+// and without the mirror a workgroup took the same block position in every round, so those
+// holding the last blocks set the kernel's end; mirrored rounds pair long units with short.
 template <int D, int B>
 __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   using SM = Smem<D>;
@@ -422,7 +427,13 @@ __global__ __launch_bounds__(kWaves * kWave) void chunk_kernel(Args a) {
   // element offset of (physical block, kv-head) in the pools, for logical blocks win0 ..
   // win0 + kTblWin - 1 (K and V blocks share the stride B * D per head)
   __shared__ long long s_tbl[kTblWin];
-  for (int L = blockIdx.x; L < a.units; L += gridDim.x) chunk_unit<D, B>(a, L, smem0, smem1, s_tbl);
+  const int g = blockIdx.x, G = gridDim.x;
+  const int mirrored = G - kXcd - g + 2 * (g % kXcd);
+  for (int r = 0;; ++r) {
+    const int L = ((r & 1) ? mirrored : g) + r * G;
+    if (L >= a.units) break;
+    chunk_unit<D, B>(a, L, smem0, smem1, s_tbl);
+  }
 }
 
 }  // namespace chunk

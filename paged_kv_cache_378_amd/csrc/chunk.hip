@@ -190,8 +190,9 @@ __device__ __forceinline__ void chunk_unit(const Args& a, int L, unsigned char* 
       const int e = u * kWave + lane;
       const int key = e / KV_PER_ROW, pos = e % KV_PER_ROW;
       const int piece = pos ^ kswz_chunk<D>(key);
-      const int j = min(k0 + key, kend - 1);   // clamp: never past the last needed key
-      const uint16_t* src = a.kc + s_tbl[j / B - win0] + ((j % B) * D + piece * 8);
+      // clamp: never past the last needed key (kend >= 1 here, so j >= 0)
+      const unsigned j = static_cast<unsigned>(min(k0 + key, kend - 1));
+      const uint16_t* src = a.kc + s_tbl[static_cast<int>(j / B) - win0] + ((j % B) * D + piece * 8);
       pa::load16_to_lds(src, kb + u * (kWave * 16));
     }
 #pragma unroll
@@ -200,8 +201,8 @@ __device__ __forceinline__ void chunk_unit(const Args& a, int L, unsigned char* 
       const int e = u * kWave + lane;
       const int dim = e / VP_PER_ROW, pos = e % VP_PER_ROW;
       const int piece = pos ^ vswz(dim);               // 8 keys
-      const int j = min(k0 + 8 * piece, (kend - 1) & ~7);
-      const uint16_t* src = a.vc + s_tbl[j / B - win0] + (dim * B + (j % B));
+      const unsigned j = static_cast<unsigned>(min(k0 + 8 * piece, (kend - 1) & ~7));
+      const uint16_t* src = a.vc + s_tbl[static_cast<int>(j / B) - win0] + (dim * B + (j % B));
       pa::load16_to_lds(src, vb + u * (kWave * 16));
     }
   };

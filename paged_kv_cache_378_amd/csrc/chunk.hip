@@ -51,8 +51,6 @@ constexpr int kXcd = 8;                 // XCDs of an MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-constexpr bf16x2 kOnes2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
 // Chunk permutation of the K tile in LDS: 16-byte chunk c of key row `key` sits at position
 // c ^ kswz_chunk(key).  A matrix-core operand read has 16 lanes fetch the same chunk of 16

@@ -15,6 +15,9 @@ constexpr int kWave = 64;  // CDNA wavefront width
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// (1, 1): the second operand of a dot2 that sums a pair of bf16 values into an fp32 total
+constexpr bf16x2 kOnes2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
 // 16-byte load of K/V pool data.  Each byte is read once per call, so the load is marked
 // non-temporal (measured ~2% faster on the Llama-3-70B-shaped decode batch).

@@ -352,9 +352,9 @@ pa_status pa_decode_workspace_size(int32_t S, int32_t Hq, int32_t D, int32_t max
  * q, out: device [S, Hq, D] of dtype (out is rounded to nearest-even for BF16).
  * block_tables: device int32 [S, max_blocks]; ctx_lens: device int32 [S], each in
  * [1, max_blocks * B] and <= max_ctx_len.  Positions >= ctx_len of a sequence never influence
- * its output (NaN or Inf there is harmless).  Computation: fp32 accumulation; split-K over
- * partitions of partition_tokens tokens (0 = library's choice, else a multiple of 32 and of B in
- * [32, 8192]) followed by a merge.  workspace: device buffer of at least
+ * its output (NaN or Inf there is harmless).  scale: positive and finite.  Computation: fp32
+ * accumulation; split-K over partitions of partition_tokens tokens (0 = library's choice, else
+ * a multiple of 32 and of B in [32, 8192]) followed by a merge.  workspace: device buffer of at least
  * pa_decode_workspace_size(S, Hq, D, max_ctx_len, partition_tokens) bytes (may be NULL if
  * that size is 0).  Deterministic: results depend on logical positions only, not on which
  * physical blocks hold them. */
@@ -471,8 +471,8 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host, const int32_t
  * sequences has ctx_lens[s] tokens in the pool INCLUDING its C new ones (already written by
  * pa_cache_write); query row i (0 <= i < C) sits at position ctx_lens[s] - C + i and attends
  * to positions 0 .. ctx_lens[s] - C + i (causal inside the chunk).
- * q, out: device [S, C, Hq, D] (BF16).  ctx_lens[s] in [C, max_blocks * B].  fp32
- * accumulation on the matrix cores.  No workspace. */
+ * q, out: device [S, C, Hq, D] (BF16).  ctx_lens[s] in [C, max_blocks * B].  scale: positive
+ * and finite.  fp32 accumulation on the matrix cores.  No workspace. */
 pa_status pa_chunk_attend(void* out, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* ctx_lens, int32_t S,
                           int32_t C, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,

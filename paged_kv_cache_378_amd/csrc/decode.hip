@@ -516,6 +516,25 @@ __device__ __forceinline__ void load_k_tile(const DecodeArgs& a, MfmaK<D>& kt, c
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
   const size_t head_stride = static_cast<size_t>(B) * D;  // elements per (block, kv-head)
   const int tt = sg.t0 + 32 * tile;
+  if ((tt & 31) == 0 && tt + 32 <= sg.t1) {  // uniform: a whole aligned tile, nothing to clamp
+    // The tile's 32 tokens lie in NB consecutive blocks (B = 16: two; B >= 32: one), so one
+    // table entry and one address per block serve its loads, which differ by constant offsets.
+    constexpr int NB = B >= 32 ? 1 : 32 / B;
+    constexpr int PER = KT::NI / NB;  // loads per block
+    const size_t lane_off = static_cast<size_t>(lane / KT::CH) * D + 8 * (lane % KT::CH);
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+      const int p = sg.tbl[tt / B + bi - sg.b0];
+      const uint16_t* bp = kc + (static_cast<size_t>(p) * a.Hkv + kvh) * head_stride +
+                           static_cast<size_t>(tt % B) * D + lane_off;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const uint16_t* kp = bp + static_cast<size_t>(KT::TPI * i) * D;
+        kt.raw[bi * PER + i] = KEEP ? ld_kv16_keep(kp) : ld_kv16(kp);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < KT::NI; ++i) {
     const unsigned tok = static_cast<unsigned>(min(tt + KT::TPI * i + lane / KT::CH, sg.t1 - 1));
@@ -666,17 +685,17 @@ __device__ __forceinline__ int mfma_item(const DecodeArgs& a, MfmaCur<D>& c,
 
     // lane (gp, r16): scores of head r16 for tokens tt + 8*gp + j, j = 4*m + i
     const int valid = sg.t1 - (tt + 8 * gp);  // tokens of this lane's group that exist
+    // raw scores; the scale (> 0, checked on the host) is applied inside the exponent
     float x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = sacc[j >> 2][j & 3] * a.scale_log2;
-      x[j] = j < valid && col_ok ? v : -INFINITY;
-    }
-    float mx = x[0];
+    for (int j = 0; j < 8; ++j) x[j] = col_ok ? sacc[j >> 2][j & 3] : -INFINITY;
+    if (sg.t1 - tt < 32) {  // uniform: the segment's last tile holds tokens past its end
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+      for (int j = 0; j < 8; ++j) x[j] = j < valid ? x[j] : -INFINITY;
+    }
+    // column max over the 32 tokens: this lane's 8, then its xor-16 and xor-32 partners
+    float mx = vmax(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], vmax3(x[5], x[6], x[7])));
+    mx = max_xor32(max_xor16(mx)) * a.scale_log2;
     // Lazy rescaling: a column's reference max m_run moves only when a score exceeds it by
     // more than kLazyRescale (log2 units), so its weights stay below 2^kLazyRescale and the
     // accumulators are rescaled on few tiles; the final division by the sum makes the result
@@ -693,7 +712,8 @@ __device__ __forceinline__ int mfma_item(const DecodeArgs& a, MfmaCur<D>& c,
     }
     bf16x8 pop;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pop[j] = static_cast<__bf16>(fast_exp2(x[j] - m_use));
+    for (int j = 0; j < 8; ++j)
+      pop[j] = static_cast<__bf16>(fast_exp2(fmaf(x[j], a.scale_log2, -m_use)));
     // the sum takes the same bf16 weights the numerator uses
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1636,7 +1656,9 @@ static pa_status decode_setup(const char* who, void* out, const void* q, const v
   if (partition_tokens % B)  // a partition is made of whole blocks
     return fail(PA_ERR_INVALID_ARG, "%s: partition_tokens %d is not a multiple of the block size %d",
                 who, partition_tokens, B);
-  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is NaN", who);
+  // the kernels take the row max of the raw scores and scale it afterwards
+  if (!(scale > 0.f) || scale == INFINITY)
+    return fail(PA_ERR_INVALID_ARG, "%s: scale must be positive and finite", who);
   if (S == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens)
     return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", who);

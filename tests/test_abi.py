@@ -72,6 +72,10 @@ def test_device_calls_reject_bad_arguments_before_launch(libpa):
     st = lib.pa_decode(fake, fake, fake, fake, fake, fake, 4, 4, 4, 64, 16, 10, 10, 100, 0.1,
                        7, 0, None, 0, None)
     assert st == libpa.PA_ERR_UNSUPPORTED
+    for bad_scale in (0.0, -0.1, float("inf"), float("nan")):
+        st = lib.pa_decode(fake, fake, fake, fake, fake, fake, 4, 4, 4, 64, 16, 10, 10, 100,
+                           bad_scale, libpa.PA_DTYPE_F32, 0, None, 0, None)
+        assert st == libpa.PA_ERR_INVALID_ARG and b"scale" in lib.pa_last_error()
     st = lib.pa_cache_write(fake, fake, fake, fake, fake, 3, 4, 64, 16, 10, 9, None)
     assert st == libpa.PA_ERR_UNSUPPORTED
     st = lib.pa_cache_write(C.c_void_p(0x1004), fake, fake, fake, fake, 3, 4, 64, 16, 10,

@@ -14,7 +14,8 @@
 // Work decomposition (chosen for CDNA4, not taken from the pages):
 //   * a work item is one partition of PT tokens of one (sequence, kv-head); NW = 4 waves split
 //     the partition's 32-token tiles round-robin and each keeps its own online-softmax state
-//     (running max m, running sum l, unnormalised output o), scores in the log2 domain;
+//     (reference max m, sum l, unnormalised output o relative to m), scores in the log2
+//     domain; the matrix-core kernel moves m only when a score passes it by 2^8;
 //   * one workgroup plans: it turns the context lengths into a work list, longest first --
 //     every full partition, then the partial last partitions by decreasing length.  It runs as
 //     a one-workgroup kernel (pa_decode) or as workgroup 0 of the step's first kernel beside

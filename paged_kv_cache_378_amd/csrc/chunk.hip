@@ -9,11 +9,12 @@
 // table ("Taming the Tail", "Under the Hood: The CUDA Kernel Engineering").
 //
 // Decomposition (CDNA4-specific):
-//   * a workgroup = (sequence, kv-head, block of TQ chunk tokens); its rows are the
+//   * a unit of work = (sequence, kv-head, block of TQ chunk tokens); its rows are the
 //     (token, query head) pairs of that kv-head's group, so every K/V tile loaded is used by
-//     all g heads (GQA) -- 256 rows per workgroup, 32 per wave (8 waves): the accumulators of
+//     all g heads (GQA) -- 256 rows per unit, 32 per wave (8 waves): the accumulators of
 //     32 rows fit in VGPRs (64 rows per wave spilled them to AGPRs and the loop moved them
-//     back and forth);
+//     back and forth).  A persistent grid of resident workgroups takes the units in rounds
+//     (chunk_kernel);
 //   * the query blocks of one (sequence, kv-head) run on one XCD, so they share its L2;
 //   * K/V tiles of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4, no
 //     register staging), two stages: tile t+1 is requested before tile t is multiplied.  The

@@ -58,6 +58,8 @@ DECODE = {
     "bf16_g8_d128": wl.custom_decode("sr_g8", 41, [1, 40, 333, 2100, 5000], 16, 2, 128, 16,
                                      "bf16"),
     "bf16_g4_d64_b32": wl.custom_decode("sr_g4", 42, [3, 97, 1500, 4100], 8, 2, 64, 32, "bf16"),
+    # B = 64: a whole 32-token tile is the first or the second half of one block
+    "bf16_g8_b64": wl.custom_decode("sr_b64", 44, [5, 64, 96, 1700, 4500], 16, 2, 128, 64, "bf16"),
     # VALU decode
     "fp32_g2_d128": wl.custom_decode("sr_f32", 43, [2, 77, 1300, 3000], 4, 2, 128, 16, "f32"),
 }
@@ -77,6 +79,7 @@ def test_decode_wide_score_range(gpu, name, kind):
 CHUNK = {
     "g8_d128_b16": wl.chunked(S=2, cached=700, C=90, B=16),
     "g8_d64_b32": wl.chunked(S=2, cached=300, C=130, B=32, D=64),
+    "g8_d128_b64": wl.chunked(S=2, cached=500, C=70, B=64),
 }
 
 
